@@ -1,0 +1,304 @@
+"""Pins of the CPU oracle to facts that do not come from the oracle itself.
+
+Each ``check_*`` function takes an ``oracle.Oracle`` and raises
+AssertionError when the oracle disagrees with:
+  - hand-worked products (tests/golden/matmul_small.txt),
+  - exact rational arithmetic (Python ``fractions``) rounded once to fp32,
+  - closed forms of C = alpha*A*B + beta*C (identity and permutation
+    operands, alpha = 0, beta = 0 with a NaN C, A = 0, K = 0, all-ones),
+  - exact integer matrix products (numpy int64),
+  - an independent fp64 library product (numpy float64 matmul),
+  - the bound's formula evaluated exactly.
+The definition being pinned is the one the Phobos blog states ("Show HN:
+Phobos", section "Matrix Multiplication": C = alpha*A*B + beta*C in 32-bit
+floats) and the naive SGEMM it quotes (section "Introducing the Phobos
+Language").  tests/test_oracle_pins.py runs every check on the oracle;
+tests/test_oracle_mutants.py runs them on deliberately broken copies of it
+and requires each copy to fail at least one.
+"""
+import os
+from fractions import Fraction
+
+import numpy as np
+
+import sgemm_workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+U24 = Fraction(1, 2 ** 24)
+
+
+def rn32(q):
+    """Round a Fraction to the nearest fp32 (ties to even); normal range only."""
+    if q == 0:
+        return np.float32(0.0)
+    sign = -1 if q < 0 else 1
+    q = abs(q)
+    e = q.numerator.bit_length() - q.denominator.bit_length() - 24
+    two = Fraction(2)
+    while q / two ** e >= 2 ** 24:
+        e += 1
+    while q / two ** e < 2 ** 23:
+        e -= 1
+    n = round(q / two ** e)          # Fraction.__round__ rounds half to even
+    return np.float32(sign * n * 2.0 ** e)
+
+
+def exact_product(M, N, K, alpha, A, B, beta, C):
+    """alpha*A*B + beta*C and sum|A||B| as Fractions (lists of lists)."""
+    F = Fraction
+    out, absum = [], []
+    for i in range(M):
+        row, arow = [], []
+        for j in range(N):
+            s = F(0)
+            sa = F(0)
+            for k in range(K):
+                p = F(float(A[i, k])) * F(float(B[k, j]))
+                s += p
+                sa += abs(p)
+            v = F(float(np.float32(alpha))) * s
+            if beta != 0:
+                v += F(float(np.float32(beta))) * F(float(C[i, j]))
+            row.append(v)
+            arow.append(sa)
+        out.append(row)
+        absum.append(arow)
+    return out, absum
+
+
+def exact_bound(K, alpha, beta, absum, c):
+    # the scalars reach the oracle as fp32 values
+    bt = 0 if beta == 0 else abs(Fraction(float(np.float32(beta))) * Fraction(float(c)))
+    a = abs(Fraction(float(np.float32(alpha))))
+    return float(2 * K * U24 * (a * absum + bt)) + 1e-30
+
+
+def ulp_diff(x, y):
+    """Distance in fp32 units in the last place between same-sign finite arrays."""
+    xi = np.asarray(x, np.float32).view(np.int32).astype(np.int64)
+    yi = np.asarray(y, np.float32).view(np.int32).astype(np.int64)
+    xi = np.where(xi < 0, -(xi & 0x7FFFFFFF), xi)
+    yi = np.where(yi < 0, -(yi & 0x7FFFFFFF), yi)
+    return np.abs(xi - yi)
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# --------------------------------------------------------------------------
+def load_golden():
+    cases, cur = [], None
+    with open(os.path.join(GOLDEN, "matmul_small.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, *vals = line.split()
+            if key == "case":
+                cur = {"name": vals[0]}
+                cases.append(cur)
+            elif key in ("M", "N", "K"):
+                cur[key] = int(vals[0])
+            elif key in ("alpha", "beta"):
+                cur[key] = float(vals[0])
+            else:
+                cur[key] = np.array([float(v) for v in vals], dtype=np.float32)
+    return cases
+
+
+def check_golden(orc):
+    for c in load_golden():
+        M, N, K = c["M"], c["N"], c["K"]
+        got, _ = orc.sgemm(M, N, K, c["alpha"], c["A"].reshape(M, K), c["B"].reshape(K, N),
+                           c["beta"], c["C"].reshape(M, N))
+        want = c["expect"].reshape(M, N)
+        assert np.array_equal(got, want), (c["name"], got, want)
+
+
+def check_exact_dyadic(orc):
+    """Inputs k/8 with |k| <= 32: fp64 sums are exact, so oracle == RN32(exact)."""
+    rng = _rng(1)
+    for M, N, K in [(1, 1, 1), (2, 3, 5), (5, 2, 3), (3, 5, 8), (8, 3, 2), (4, 7, 13)]:
+        for alpha, beta in [(1.0, 0.0), (0.75, -1.25), (-2.0, 0.5)]:
+            A = (rng.integers(-32, 33, (M, K)) / 8).astype(np.float32)
+            B = (rng.integers(-32, 33, (K, N)) / 8).astype(np.float32)
+            C = (rng.integers(-32, 33, (M, N)) / 8).astype(np.float32)
+            got, bnd = orc.sgemm(M, N, K, alpha, A, B, beta, C)
+            ex, absum = exact_product(M, N, K, alpha, A, B, beta, C)
+            want = np.array([[rn32(v) for v in r] for r in ex], dtype=np.float32)
+            assert np.array_equal(got, want), ((M, N, K, alpha, beta), got, want)
+            wb = np.array([[exact_bound(K, alpha, beta, absum[i][j], C[i, j])
+                            for j in range(N)] for i in range(M)])
+            np.testing.assert_allclose(bnd, wb, rtol=1e-13, atol=0)
+
+
+def check_exact_general(orc):
+    """Random fp32 inputs: within 1 ulp of RN32(exact), almost always equal."""
+    rng = _rng(2)
+    total = equal = 0
+    for M, N, K in [(3, 4, 5), (6, 5, 17), (2, 9, 33)]:
+        for alpha, beta in [(1.3, -0.7), (-1.0, 0.25), (0.1, 0.0)]:
+            A = rng.uniform(-1, 1, (M, K)).astype(np.float32)
+            B = rng.standard_normal((K, N)).astype(np.float32)
+            C = rng.uniform(-1, 1, (M, N)).astype(np.float32)
+            got, bnd = orc.sgemm(M, N, K, alpha, A, B, beta, C)
+            ex, absum = exact_product(M, N, K, alpha, A, B, beta, C)
+            want = np.array([[rn32(v) for v in r] for r in ex], dtype=np.float32)
+            d = ulp_diff(got, want)
+            assert d.max() <= 1, ((M, N, K), d.max())
+            total += d.size
+            equal += int((d == 0).sum())
+            wb = np.array([[exact_bound(K, alpha, beta, absum[i][j], C[i, j])
+                            for j in range(N)] for i in range(M)])
+            np.testing.assert_allclose(bnd, wb, rtol=1e-13, atol=0)
+    assert equal >= 0.97 * total, (equal, total)
+
+
+def check_bound_covers_fp32_loop(orc):
+    """A plain fp32 left-to-right loop is within the bound of the reference.
+
+    The bound 2*K*u*(...) is at least the classical worst case of a K-term fp32
+    dot product plus the epilogue, so it must cover a naive fp32 computation.
+    """
+    rng = _rng(3)
+    M, N, K = 24, 20, 300
+    alpha, beta = 1.5, 0.5
+    A = rng.uniform(-1, 1, (M, K)).astype(np.float32)
+    B = rng.uniform(-1, 1, (K, N)).astype(np.float32)
+    C = rng.uniform(-1, 1, (M, N)).astype(np.float32)
+    s = np.zeros((M, N), np.float32)
+    for k in range(K):
+        s = (s + np.outer(A[:, k], B[k, :]).astype(np.float32)).astype(np.float32)
+    c32 = (np.float32(alpha) * s + np.float32(beta) * C).astype(np.float32)
+    ref, bnd = orc.sgemm(M, N, K, alpha, A, B, beta, C)
+    err = np.abs(c32.astype(np.float64) - ref.astype(np.float64))
+    assert (err <= bnd).all(), (err / bnd).max()
+    # and it is a genuine check: the naive loop does differ from the reference
+    assert (err > 0).any()
+
+
+def check_closed_forms(orc):
+    rng = _rng(4)
+    M, K = 37, 29
+    A = rng.uniform(-1, 1, (M, K)).astype(np.float32)
+    C = rng.uniform(-1, 1, (M, K)).astype(np.float32)
+    # B = I, alpha = 2, beta = 0.5: C = RN(2a + 0.5c) (two exact scalings, one rounding)
+    got, _ = orc.sgemm(M, K, K, 2.0, A, np.eye(K, dtype=np.float32), 0.5, C)
+    want = (np.float32(2) * A + np.float32(0.5) * C).astype(np.float32)
+    assert np.array_equal(got, want)
+    # alpha = 0: C = RN(beta*c); A and B arbitrary (finite)
+    B = rng.standard_normal((K, K)).astype(np.float32)
+    got, _ = orc.sgemm(M, K, K, 0.0, A, B, -0.3, C)
+    assert np.array_equal(got, (np.float32(-0.3) * C).astype(np.float32))
+    # beta = 0 with C = NaN: no NaN, equal to the result with a finite C
+    nanC = np.full_like(C, np.nan)
+    g1, b1 = orc.sgemm(M, K, K, 1.25, A, B, 0.0, nanC)
+    g2, b2 = orc.sgemm(M, K, K, 1.25, A, B, 0.0, C)
+    assert not np.isnan(g1).any() and not np.isnan(b1).any()
+    assert np.array_equal(g1, g2) and np.array_equal(b1, b2)
+    # A = 0, beta = 1: C unchanged bit for bit
+    got, _ = orc.sgemm(M, K, K, 1.0, np.zeros_like(A), B, 1.0, C)
+    assert np.array_equal(got.view(np.int32), C.view(np.int32))
+    # K = 0: C = RN(beta*c), bound is exactly the 1e-30 floor
+    got, bnd = orc.sgemm(M, K, 0, 3.0, np.zeros((M, 1), np.float32),
+                         np.zeros((1, K), np.float32), 0.75, C, lda=1, ldb=K)
+    assert np.array_equal(got, (np.float32(0.75) * C).astype(np.float32))
+    assert np.all(bnd == 1e-30)
+    # column permutation: A @ P with P[k, perm[k]] = 1 moves column k of A to perm[k]
+    perm = rng.permutation(K)
+    P = np.zeros((K, K), np.float32)
+    P[np.arange(K), perm] = 1
+    got, _ = orc.sgemm(M, K, K, 1.0, A, P, 0.0, None)
+    want = np.empty_like(A)
+    want[:, perm] = A
+    assert np.array_equal(got, want)
+    # row permutation: Q @ B with Q[i, q[i]] = 1 takes row q[i] of B
+    N = 11
+    B2 = rng.uniform(-1, 1, (K, N)).astype(np.float32)
+    q = rng.permutation(K)
+    Q = np.zeros((K, K), np.float32)
+    Q[np.arange(K), q] = 1
+    got, _ = orc.sgemm(K, N, K, 1.0, Q, B2, 0.0, None)
+    assert np.array_equal(got, B2[q])
+    # all ones: every sum is K exactly
+    got, _ = orc.sgemm(5, 6, 7, 0.5, np.ones((5, 7), np.float32),
+                       np.ones((7, 6), np.float32), -2.0, np.ones((5, 6), np.float32))
+    assert np.all(got == np.float32(0.5 * 7 - 2.0))
+
+
+def _int_case(orc, w):
+    """Integer-valued inputs: the oracle equals exact int64 arithmetic bit for bit."""
+    x = wl.make_inputs(w)
+    M = w.M
+    A = x.logical("A")
+    B = x.logical("B")
+    C = x.logical("C")
+    got, _ = orc.sgemm(M, w.N, w.K, w.alpha, x.A, x.B, w.beta, x.C,
+                       lda=w.lda, ldb=w.ldb, ldc=w.ldc)
+    prod = A.astype(np.int64) @ B.astype(np.int64)
+    want = w.alpha * prod.astype(np.float64)
+    if w.beta != 0:
+        want = want + w.beta * C.astype(np.float64)
+    assert np.array_equal(got, want.astype(np.float32)), w.name
+
+
+def check_integer_exact(orc):
+    _int_case(orc, wl.WORKLOADS[0].integer_variant())
+    # padded leading dimensions (NaN pads) and ragged sizes, on a slab of rows
+    w5 = wl.WORKLOADS[4]
+    small5 = wl.custom(71, 301, 205, w5.alpha, w5.beta, ("I7", "I7", "I7"), seed=104,
+                       lda=208, ldb=304, ldc=305)
+    _int_case(orc, small5)
+    # tall-skinny scalars and K, on a slab of rows
+    w4 = wl.WORKLOADS[3]
+    _int_case(orc, wl.custom(16, w4.N, w4.K, w4.alpha, w4.beta, ("I7", "I7", "I7"),
+                             seed=103, lda=w4.lda, ldb=w4.ldb, ldc=w4.ldc))
+
+
+def check_numpy_fp64(orc):
+    """Against an independent fp64 product (numpy matmul): within 1 ulp."""
+    for w in (wl.WORKLOADS[0],
+              wl.custom(90, 3001, 2047, -1.0, 0.25, seed=4, lda=2048, ldb=3008, ldc=3008)):
+        x = wl.make_inputs(w)
+        A = x.logical("A").astype(np.float64)
+        B = x.logical("B").astype(np.float64)
+        C = x.logical("C").astype(np.float64)
+        got, bnd = orc.sgemm(w.M, w.N, w.K, w.alpha, x.A, x.B, w.beta, x.C,
+                             lda=w.lda, ldb=w.ldb, ldc=w.ldc)
+        ref = (w.alpha * (A @ B) + w.beta * C).astype(np.float32)
+        d = ulp_diff(got, ref)
+        assert d.max() <= 1 and (d == 0).mean() > 0.99, (w.name, d.max(), (d == 0).mean())
+        wb = 2 * w.K * 2.0 ** -24 * (abs(w.alpha) * (np.abs(A) @ np.abs(B))
+                                      + np.abs(w.beta * C)) + 1e-30
+        np.testing.assert_allclose(bnd, wb, rtol=1e-12, atol=0)
+
+
+def check_entries(orc):
+    """The per-entry routine: equal to the full one, and to numpy at K = 16384."""
+    w = wl.custom(150, 130, 333, 0.5, 2.0, seed=7, lda=340, ldb=131, ldc=133)
+    x = wl.make_inputs(w)
+    full, fb = orc.sgemm(w.M, w.N, w.K, w.alpha, x.A, x.B, w.beta, x.C,
+                         lda=w.lda, ldb=w.ldb, ldc=w.ldc)
+    r, c = wl.sample_entries(w, 500)
+    got, gb = orc.sgemm_entries(w.M, w.N, w.K, w.alpha, x.A, x.B, w.beta, x.C, r, c,
+                                lda=w.lda, ldb=w.ldb, ldc=w.ldc)
+    assert np.array_equal(got, full[r, c]) and np.array_equal(gb, fb[r, c])
+    # long K, as in the 16384^3 workload
+    wk = wl.custom(8, 64, 16384, 1.0, 1.0, seed=2)
+    xk = wl.make_inputs(wk)
+    r, c = wl.sample_entries(wk, 40)
+    got, gb = orc.sgemm_entries(wk.M, wk.N, wk.K, 1.0, xk.A, xk.B, 1.0, xk.C, r, c)
+    A = xk.logical("A").astype(np.float64)
+    B = xk.logical("B").astype(np.float64)
+    C = xk.logical("C").astype(np.float64)
+    ref = ((A @ B) + C)[r, c].astype(np.float32)
+    d = ulp_diff(got, ref)
+    assert d.max() <= 1, d.max()
+    wb = 2 * wk.K * 2.0 ** -24 * ((np.abs(A) @ np.abs(B)) + np.abs(C))[r, c] + 1e-30
+    np.testing.assert_allclose(gb, wb, rtol=1e-12, atol=0)
+
+
+ALL_CHECKS = [check_golden, check_exact_dyadic, check_exact_general,
+              check_bound_covers_fp32_loop, check_closed_forms, check_integer_exact,
+              check_numpy_fp64, check_entries]

@@ -1,0 +1,85 @@
+"""Each pin set must catch plausible mistakes planted in a copy of the oracle.
+
+Every mutant is a one-line textual change to ``oracle/sgemm_oracle.c``
+(a dropped term, a wrong sign or index, a transposed operand, a lost factor
+in the bound, ...), compiled to a temporary library.  The pins of
+tests/oracle_pins.py then run against it in a child process (a mutant may
+read out of bounds and crash; a crash also counts as caught).  A mutant that
+passes every pin would mean the pins cannot tell that mistake from the
+oracle, and the test fails.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "sgemm_oracle.c")
+
+# (name, text in the oracle, replacement)
+MUTANTS = [
+    ("drop_beta_term", "if (beta != 0.0f) t += (double)beta * (double)c;", ""),
+    ("beta_term_sign", "t += (double)beta * (double)c;", "t -= (double)beta * (double)c;"),
+    ("drop_alpha", "double t = (double)alpha * sum;", "double t = sum;"),
+    ("subtract_products", "s[j] += p;", "s[j] -= p;"),
+    ("drop_last_k", "for (int64_t k = 0; k < K; ++k) {\n                    const double a",
+     "for (int64_t k = 0; k < K - 1; ++k) {\n                    const double a"),
+    ("skip_first_k", "for (int64_t k = 0; k < K; ++k) {\n                    const double a",
+     "for (int64_t k = (K > 1); k < K; ++k) {\n                    const double a"),
+    ("transposed_B", "const double p = a * (double)brow[j];",
+     "const double p = a * (double)B[j * ldb + k];"),
+    ("A_column_for_row", "const double a = (double)A[i * lda + k];",
+     "const double a = (double)A[k * lda + i];"),
+    ("B_ignores_ld", "const float* brow = B + k * ldb;", "const float* brow = B + k * N;"),
+    ("fp32_accumulator", "const double p = a * (double)brow[j];",
+     "const double p = (double)(float)(a * (double)brow[j]);"),
+    ("bound_factor_1", "return 2.0 * (double)K * ORACLE_U", "return (double)K * ORACLE_U"),
+    ("bound_signed_sum", "sa[j] += fabs(p);", "sa[j] += p;"),
+    ("bound_drops_beta", "double beta_term = (beta == 0.0f) ? 0.0 : fabs((double)beta * (double)c);",
+     "double beta_term = 0.0;"),
+    ("C_ignores_ldc", "const float c = (beta != 0.0f) ? C[i * ldc + j] : 0.0f;\n"
+     "                    Cref", "const float c = (beta != 0.0f) ? C[i * N + j] : 0.0f;\n"
+     "                    Cref"),
+    ("A_ignores_lda", "const double a = (double)A[i * lda + k];",
+     "const double a = (double)A[i * K + k];"),
+    ("alpha_scales_by_beta", "double t = (double)alpha * sum;", "double t = (double)beta * sum;"),
+    ("entries_transposed_B", "(double)B[k * ldb + j];", "(double)B[j * ldb + k];"),
+    ("entries_drop_beta", "        out[t] = finish(alpha, beta, s, c);",
+     "        out[t] = finish(alpha, 0.0f, s, c);"),
+]
+
+RUNNER = r"""
+import sys
+sys.path.insert(0, {root!r})
+import oracle
+from tests import oracle_pins
+orc = oracle.Oracle({lib!r})
+failed = []
+for check in oracle_pins.ALL_CHECKS:
+    try:
+        check(orc)
+    except Exception as e:
+        failed.append(check.__name__)
+print("FAILED_PINS", ",".join(failed))
+"""
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, name, old, new):
+    text = open(SRC).read()
+    assert text.count(old) == 1, f"mutation site for {name} not unique or missing"
+    src = tmp_path / f"{name}.c"
+    src.write_text(text.replace(old, new))
+    lib = str(tmp_path / f"lib_{name}.so")
+    oracle.build(src=str(src), out=lib)
+    env = dict(os.environ, OMP_NUM_THREADS="2")
+    proc = subprocess.run([sys.executable, "-c", RUNNER.format(root=ROOT, lib=lib)],
+                          capture_output=True, text=True, timeout=300, env=env)
+    if proc.returncode != 0:
+        return  # crashed on a planted out-of-bounds access: caught
+    line = [l for l in proc.stdout.splitlines() if l.startswith("FAILED_PINS")][-1]
+    failed = [x for x in line.split(" ", 1)[1].split(",") if x]
+    assert failed, f"mutant {name} passed every pin"
