@@ -1,0 +1,199 @@
+"""Python binding of the gfx950 FP32 SGEMM library (libphobos_sgemm.so).
+
+Argument marshalling only: every step of C <- alpha*A*B + beta*C runs in the
+library's HIP kernels.  The functions carry the names of the C entry points
+declared in include/phobos_sgemm.h and take the same arguments; pointers may
+be given as integers or as tensors (their data_ptr()), the stream as a
+torch.cuda.Stream, an integer hipStream_t or None (torch's current stream on
+the current device).  A non-zero status raises SgemmError, except in the
+``raw`` entry points, which return it.
+
+The library is loaded from this directory.  There is no fallback: if it has
+not been built (python -m fp32_gemm_02_amd.build), importing works but the
+first call raises.
+"""
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libphobos_sgemm.so")
+
+SGEMM_OK = 0
+SGEMM_ERR_NO_CONFIG = 2
+SGEMM_ERR_TOO_LARGE = 3
+SGEMM_ERR_ALLOC = 4
+SGEMM_ERR_HIP_BASE = 1000
+SGEMM_KIND_GEMM = 0
+SGEMM_KIND_INIT_LEAF = 1
+
+
+class SgemmError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({status_string(status)})")
+
+
+class sgemm_config(ctypes.Structure):
+    _fields_ = [("bm", ctypes.c_int32), ("bn", ctypes.c_int32), ("bk", ctypes.c_int32),
+                ("wm", ctypes.c_int32), ("wn", ctypes.c_int32)]
+
+    def as_tuple(self):
+        return (self.bm, self.bn, self.bk, self.wm, self.wn)
+
+    def __repr__(self):
+        return "sgemm_config(bm=%d, bn=%d, bk=%d, wm=%d, wn=%d)" % self.as_tuple()
+
+
+_lib = None
+
+_i64, _f32, _i32, _vp = ctypes.c_int64, ctypes.c_float, ctypes.c_int32, ctypes.c_void_p
+_SIGNATURES = {
+    "sgemm": ([_i64, _i64, _i64, _f32, _vp, _i64, _vp, _i64, _f32, _vp, _i64, _vp], ctypes.c_int),
+    "sgemm_supertiled": ([_i64, _i64, _i64, _f32, _vp, _i64, _vp, _i64, _f32, _vp, _i64,
+                          _i64, _i64, _i64, _vp], ctypes.c_int),
+    "sgemm_init_leaf": ([_i64, _i64, _f32, _vp, _i64, _vp], ctypes.c_int),
+    "sgemm_config_count": ([], ctypes.c_int),
+    "sgemm_config_at": ([_i32, ctypes.POINTER(sgemm_config)], ctypes.c_int),
+    "sgemm_get_config": ([_i64, _i64, _i64, _i64, _i64, _i64, ctypes.POINTER(sgemm_config)],
+                         ctypes.c_int),
+    "sgemm_set_config": ([ctypes.POINTER(sgemm_config)], ctypes.c_int),
+    "sgemm_tune_candidates": ([_i64, _i64, _i64, ctypes.POINTER(sgemm_config), _i32],
+                              ctypes.c_int),
+    "sgemm_tune": ([_i64, _i64, _i64, _i64, _i64, _i64, _i32, _vp,
+                    ctypes.POINTER(sgemm_config), ctypes.POINTER(_f32)], ctypes.c_int),
+    "sgemm_trace_begin": ([_i64], ctypes.c_int),
+    "sgemm_trace_end": ([ctypes.POINTER(_f32), ctypes.POINTER(_i32), _i64,
+                         ctypes.POINTER(_i64)], ctypes.c_int),
+    "sgemm_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "sgemm_version": ([], ctypes.c_int),
+}
+
+
+def lib():
+    """The loaded library with its prototypes set (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run python -m fp32_gemm_02_amd.build")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGNATURES.items():
+            fn = getattr(l, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = l
+    return _lib
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if hasattr(x, "data_ptr"):
+        return x.data_ptr()
+    return int(x)
+
+
+def _stream(s):
+    if s is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if hasattr(s, "cuda_stream"):
+        return s.cuda_stream
+    return int(s)
+
+
+def _check(status, where):
+    if status != SGEMM_OK:
+        raise SgemmError(status, where)
+
+
+def status_string(status):
+    return lib().sgemm_status_string(int(status)).decode()
+
+
+def version():
+    return lib().sgemm_version()
+
+
+def sgemm_raw(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None):
+    return lib().sgemm(M, N, K, alpha, _ptr(A), lda, _ptr(B), ldb, beta, _ptr(C), ldc,
+                       _stream(stream))
+
+
+def sgemm(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None):
+    """C <- alpha*A*B + beta*C (row-major, device pointers); asynchronous."""
+    _check(sgemm_raw(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream), "sgemm")
+
+
+def sgemm_supertiled_raw(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, TM, TN, TK,
+                         stream=None):
+    return lib().sgemm_supertiled(M, N, K, alpha, _ptr(A), lda, _ptr(B), ldb, beta, _ptr(C),
+                                  ldc, TM, TN, TK, _stream(stream))
+
+
+def sgemm_supertiled(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, TM, TN, TK, stream=None):
+    """The same product through TM x TN x TK super-tiles (init leaf + K steps)."""
+    _check(sgemm_supertiled_raw(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, TM, TN, TK,
+                                stream), "sgemm_supertiled")
+
+
+def sgemm_init_leaf(M, N, beta, C, ldc, stream=None):
+    """C <- beta*C (C <- 0 without reading C when beta == 0)."""
+    _check(lib().sgemm_init_leaf(M, N, beta, _ptr(C), ldc, _stream(stream)), "sgemm_init_leaf")
+
+
+def configs():
+    """Every compiled configuration, as sgemm_config structures."""
+    out = []
+    for i in range(lib().sgemm_config_count()):
+        c = sgemm_config()
+        _check(lib().sgemm_config_at(i, ctypes.byref(c)), "sgemm_config_at")
+        out.append(c)
+    return out
+
+
+def sgemm_get_config(M, N, K, lda, ldb, ldc):
+    c = sgemm_config()
+    _check(lib().sgemm_get_config(M, N, K, lda, ldb, ldc, ctypes.byref(c)), "sgemm_get_config")
+    return c
+
+
+def sgemm_set_config(cfg):
+    """Force one configuration for every later call (None clears)."""
+    if cfg is None:
+        _check(lib().sgemm_set_config(None), "sgemm_set_config")
+        return
+    if not isinstance(cfg, sgemm_config):
+        cfg = sgemm_config(*cfg)
+    _check(lib().sgemm_set_config(ctypes.byref(cfg)), "sgemm_set_config")
+
+
+def sgemm_tune_candidates(M, N, K):
+    cap = lib().sgemm_config_count()
+    arr = (sgemm_config * cap)()
+    n = lib().sgemm_tune_candidates(M, N, K, arr, cap)
+    if n < 0:
+        raise SgemmError(n, "sgemm_tune_candidates")
+    return [arr[i] for i in range(min(n, cap))]
+
+
+def sgemm_tune(M, N, K, lda, ldb, ldc, reps=20, stream=None):
+    """Time the candidates, record the winner for this shape; returns (config, ms)."""
+    c = sgemm_config()
+    ms = ctypes.c_float()
+    _check(lib().sgemm_tune(M, N, K, lda, ldb, ldc, reps, _stream(stream), ctypes.byref(c),
+                            ctypes.byref(ms)), "sgemm_tune")
+    return c, ms.value
+
+
+def sgemm_trace_begin(capacity):
+    _check(lib().sgemm_trace_begin(capacity), "sgemm_trace_begin")
+
+
+def sgemm_trace_end(cap=1 << 16):
+    """Durations (ms) and kinds of the traced launches, in launch order."""
+    ms = (ctypes.c_float * cap)()
+    kinds = (ctypes.c_int32 * cap)()
+    n = ctypes.c_int64()
+    _check(lib().sgemm_trace_end(ms, kinds, cap, ctypes.byref(n)), "sgemm_trace_end")
+    k = min(n.value, cap)
+    return list(ms[:k]), list(kinds[:k]), n.value

@@ -1,0 +1,468 @@
+// C-ABI layer of the gfx950 SGEMM library: argument checks, quick returns,
+// kernel selection, the super-tile walk, the tile tuner and the launch trace.
+// The public contract is documented in include/phobos_sgemm.h.
+
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <tuple>
+#include <vector>
+
+#include "phobos_sgemm.h"
+#include "sgemm_internal.h"
+
+using phobos::GemmArgs;
+using phobos::KernelEntry;
+
+namespace {
+
+// Dimensions stay well inside int32 so that k0 + BK and similar kernel-side
+// sums cannot overflow; the dispatch grid counts work-items in 32 bits.
+constexpr int64_t kMaxDim = int64_t(1) << 30;
+constexpr int64_t kMaxGridItems = 0xffffffffLL;
+
+struct Table {
+    const KernelEntry* entries;
+    int count;
+    Table() { entries = phobos::kernel_table(&count); }
+};
+const Table& table() {
+    static const Table t;
+    return t;
+}
+#define kKernelTable (table().entries)
+#define kKernelCount (table().count)
+
+int hip_status(hipError_t e) { return e == hipSuccess ? SGEMM_OK : SGEMM_ERR_HIP_BASE + (int)e; }
+
+bool same_cfg(const sgemm_config& a, const sgemm_config& b) {
+    return a.bm == b.bm && a.bn == b.bn && a.bk == b.bk && a.wm == b.wm && a.wn == b.wn;
+}
+
+int find_entry(const sgemm_config& c) {
+    for (int i = 0; i < kKernelCount; ++i)
+        if (same_cfg(kKernelTable[i].cfg, c)) return i;
+    return -1;
+}
+
+// ---- process-wide state (guarded by g_mu) ----
+std::mutex g_mu;
+int g_forced = -1;  // index into kKernelTable, or -1
+using ShapeKey = std::tuple<int64_t, int64_t, int64_t, int64_t, int64_t, int64_t>;
+std::map<ShapeKey, int> g_tuned;
+
+struct TraceRec {
+    hipEvent_t start, stop;
+    int32_t kind;
+};
+bool g_trace_on = false;
+int64_t g_trace_cap = 0;
+std::vector<TraceRec> g_trace;
+
+int env_int(const char* name, int dflt) {
+    const char* v = std::getenv(name);
+    return (v && *v) ? std::atoi(v) : dflt;
+}
+
+// Built-in choice when nothing is forced or tuned: the largest tile that still
+// gives every CU of the chip work, falling back to small tiles for small
+// problems.
+int default_entry(int64_t M, int64_t N, int64_t K) {
+    struct Pick { int bm, bn, bk, wm, wn; };
+    static const Pick order[] = {
+        {256, 256, 16, 2, 2}, {256, 128, 16, 2, 2}, {128, 128, 16, 2, 2},
+        {128, 64, 16, 2, 1},  {64, 64, 16, 1, 1},
+    };
+    (void)K;
+    const int64_t want_tiles = 256;
+    for (const Pick& p : order) {
+        const int64_t tiles = ((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn);
+        if (tiles >= want_tiles) return find_entry({p.bm, p.bn, p.bk, p.wm, p.wn});
+    }
+    if (M <= 32 && N <= 32) return find_entry({32, 32, 16, 1, 1});
+    return find_entry({64, 64, 16, 1, 1});
+}
+
+int choose_entry(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc) {
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        if (g_forced >= 0) return g_forced;
+        auto it = g_tuned.find(ShapeKey{M, N, K, lda, ldb, ldc});
+        if (it != g_tuned.end()) return it->second;
+    }
+    return default_entry(M, N, K);
+}
+
+// Record a trace event pair around a launch when tracing is on.
+struct TraceScope {
+    hipStream_t s;
+    int idx = -1;
+    TraceScope(hipStream_t stream, int32_t kind) : s(stream) {
+        std::lock_guard<std::mutex> lk(g_mu);
+        if (!g_trace_on || (int64_t)g_trace.size() >= g_trace_cap) return;
+        TraceRec r{};
+        if (hipEventCreate(&r.start) != hipSuccess) return;
+        if (hipEventCreate(&r.stop) != hipSuccess) {
+            (void)hipEventDestroy(r.start);
+            return;
+        }
+        r.kind = kind;
+        if (hipEventRecord(r.start, s) != hipSuccess) {
+            (void)hipEventDestroy(r.start);
+            (void)hipEventDestroy(r.stop);
+            return;
+        }
+        idx = (int)g_trace.size();
+        g_trace.push_back(r);
+    }
+    ~TraceScope() {
+        if (idx < 0) return;
+        std::lock_guard<std::mutex> lk(g_mu);
+        (void)hipEventRecord(g_trace[idx].stop, s);
+    }
+};
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// One GEMM launch on already-validated arguments (M, N, K > 0, alpha != 0).
+int launch_gemm(int entry, int64_t M, int64_t N, int64_t K, float alpha, const float* A,
+                int64_t lda, const float* B, int64_t ldb, float beta, float* C, int64_t ldc,
+                hipStream_t stream) {
+    const KernelEntry& e = kKernelTable[entry];
+    GemmArgs p{};
+    p.M = (int32_t)M;
+    p.N = (int32_t)N;
+    p.K = (int32_t)K;
+    p.alpha = alpha;
+    p.beta = beta;
+    p.A = A;
+    p.lda = lda;
+    p.B = B;
+    p.ldb = ldb;
+    p.C = C;
+    p.ldc = ldc;
+    const int64_t tm = (M + e.cfg.bm - 1) / e.cfg.bm;
+    const int64_t tn = (N + e.cfg.bn - 1) / e.cfg.bn;
+    if (tm * tn * e.threads > kMaxGridItems) return SGEMM_ERR_TOO_LARGE;
+    p.tiles_m = (int32_t)tm;
+    p.tiles_n = (int32_t)tn;
+    p.group_m = std::max(1, env_int("SGEMM_GROUP_M", 4));
+    p.xcd_remap = ((tm * tn) % 8 == 0 && env_int("SGEMM_XCD_REMAP", 1) != 0) ? 1 : 0;
+    const bool vec = aligned16(A) && aligned16(B) && aligned16(C) && lda % 4 == 0 &&
+                     ldb % 4 == 0 && ldc % 4 == 0;
+    TraceScope ts(stream, SGEMM_KIND_GEMM);
+    const hipError_t err = vec ? e.vec4(p, stream) : e.scalar(p, stream);
+    return hip_status(err);
+}
+
+int launch_init(int64_t M, int64_t N, float beta, float* C, int64_t ldc, hipStream_t stream) {
+    if (beta == 1.0f) return SGEMM_OK;
+    TraceScope ts(stream, SGEMM_KIND_INIT_LEAF);
+    return hip_status(phobos::launch_init_leaf(M, N, beta, C, ldc, stream));
+}
+
+// Argument checks shared by sgemm and sgemm_supertiled (BLAS-style numbering).
+int check_gemm_args(int64_t M, int64_t N, int64_t K, float alpha, const float* A, int64_t lda,
+                    const float* B, int64_t ldb, const float* C, int64_t ldc) {
+    if (M < 0) return -1;
+    if (N < 0) return -2;
+    if (K < 0) return -3;
+    if (lda < std::max<int64_t>(1, K)) return -6;
+    if (ldb < std::max<int64_t>(1, N)) return -8;
+    if (ldc < std::max<int64_t>(1, N)) return -11;
+    if (M == 0 || N == 0) return SGEMM_OK;
+    const bool reads_ab = K > 0 && alpha != 0.0f;
+    if (reads_ab && A == nullptr) return -5;
+    if (reads_ab && B == nullptr) return -7;
+    if (C == nullptr) return -10;
+    if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return SGEMM_ERR_TOO_LARGE;
+    return SGEMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sgemm(int64_t M, int64_t N, int64_t K, float alpha, const float* A, int64_t lda,
+          const float* B, int64_t ldb, float beta, float* C, int64_t ldc, void* stream) {
+    const int st = check_gemm_args(M, N, K, alpha, A, lda, B, ldb, C, ldc);
+    if (st != SGEMM_OK) return st;
+    if (M == 0 || N == 0) return SGEMM_OK;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (K == 0 || alpha == 0.0f) return launch_init(M, N, beta, C, ldc, s);
+    const int entry = choose_entry(M, N, K, lda, ldb, ldc);
+    if (entry < 0) return SGEMM_ERR_NO_CONFIG;
+    return launch_gemm(entry, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s);
+}
+
+int sgemm_supertiled(int64_t M, int64_t N, int64_t K, float alpha, const float* A,
+                     int64_t lda, const float* B, int64_t ldb, float beta, float* C,
+                     int64_t ldc, int64_t TM, int64_t TN, int64_t TK, void* stream) {
+    int st = check_gemm_args(M, N, K, alpha, A, lda, B, ldb, C, ldc);
+    if (st != SGEMM_OK) return st;
+    if (TM < 1) return -12;
+    if (TN < 1) return -13;
+    if (TK < 1) return -14;
+    if (M == 0 || N == 0) return SGEMM_OK;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const bool steps = K > 0 && alpha != 0.0f;
+    const int64_t tm = std::min(TM, M), tn = std::min(TN, N), tk = std::min(TK, std::max<int64_t>(K, 1));
+    const int64_t gm = (M + tm - 1) / tm, gn = (N + tn - 1) / tn, gk = steps ? (K + tk - 1) / tk : 0;
+    for (int64_t pm = 0; pm < gm; ++pm) {
+        const int64_t r0 = pm * tm, rows = std::min(tm, M - r0);
+        for (int64_t pn = 0; pn < gn; ++pn) {
+            const int64_t c0 = pn * tn, cols = std::min(tn, N - c0);
+            float* Cs = C + r0 * ldc + c0;
+            // init leaf: seed the accumulator (the output's own buffer) with beta*C
+            st = launch_init(rows, cols, beta, Cs, ldc, s);
+            if (st != SGEMM_OK) return st;
+            // step leaves: add one K chunk each, implicit beta of 1
+            for (int64_t kt = 0; kt < gk; ++kt) {
+                const int64_t k0 = kt * tk, depth = std::min(tk, K - k0);
+                const float* As = A + r0 * lda + k0;
+                const float* Bs = B + k0 * ldb + c0;
+                const int entry = choose_entry(rows, cols, depth, lda, ldb, ldc);
+                if (entry < 0) return SGEMM_ERR_NO_CONFIG;
+                st = launch_gemm(entry, rows, cols, depth, alpha, As, lda, Bs, ldb, 1.0f, Cs,
+                                 ldc, s);
+                if (st != SGEMM_OK) return st;
+            }
+        }
+    }
+    return SGEMM_OK;
+}
+
+int sgemm_init_leaf(int64_t M, int64_t N, float beta, float* C, int64_t ldc, void* stream) {
+    if (M < 0) return -1;
+    if (N < 0) return -2;
+    if (ldc < std::max<int64_t>(1, N)) return -5;
+    if (M == 0 || N == 0) return SGEMM_OK;
+    if (C == nullptr) return -4;
+    return launch_init(M, N, beta, C, ldc, reinterpret_cast<hipStream_t>(stream));
+}
+
+int sgemm_config_count(void) { return kKernelCount; }
+
+int sgemm_config_at(int32_t index, sgemm_config* out) {
+    if (index < 0 || index >= kKernelCount) return -1;
+    if (out == nullptr) return -2;
+    *out = kKernelTable[index].cfg;
+    return SGEMM_OK;
+}
+
+int sgemm_get_config(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
+                     sgemm_config* out) {
+    if (M < 0) return -1;
+    if (N < 0) return -2;
+    if (K < 0) return -3;
+    if (lda < std::max<int64_t>(1, K)) return -4;
+    if (ldb < std::max<int64_t>(1, N)) return -5;
+    if (ldc < std::max<int64_t>(1, N)) return -6;
+    if (out == nullptr) return -7;
+    const int e = choose_entry(M, N, K, lda, ldb, ldc);
+    if (e < 0) return SGEMM_ERR_NO_CONFIG;
+    *out = kKernelTable[e].cfg;
+    return SGEMM_OK;
+}
+
+int sgemm_set_config(const sgemm_config* cfg) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (cfg == nullptr) {
+        g_forced = -1;
+        return SGEMM_OK;
+    }
+    const int e = find_entry(*cfg);
+    if (e < 0) return SGEMM_ERR_NO_CONFIG;
+    g_forced = e;
+    return SGEMM_OK;
+}
+
+int sgemm_tune_candidates(int64_t M, int64_t N, int64_t K, sgemm_config* out, int32_t cap) {
+    if (M < 0) return -1;
+    if (N < 0) return -2;
+    if (K < 0) return -3;
+    if (cap < 0) return -5;
+    if (out == nullptr && cap > 0) return -4;
+    auto pow2_in = [](int v, int lo, int hi) {
+        if (v < lo || v > hi) return false;
+        for (int x = lo; x <= hi; x *= 2)
+            if (x == v) return true;
+        return false;
+    };
+    const int64_t mneed = std::max<int64_t>(32, (M + 31) / 32 * 32);
+    const int64_t nneed = std::max<int64_t>(32, (N + 31) / 32 * 32);
+    int n = 0;
+    for (int i = 0; i < kKernelCount; ++i) {
+        const sgemm_config& c = kKernelTable[i].cfg;
+        // the @autotune ranges of the matmul kernel: doubling steps between the bounds
+        if (!pow2_in(c.bm, 32, 256) || !pow2_in(c.bn, 32, 256) || !pow2_in(c.bk, 4, 32)) continue;
+        // no tile larger than the problem needs
+        if (c.bm > mneed || c.bn > nneed) continue;
+        if (kKernelTable[i].lds_bytes > 160 * 1024) continue;
+        if (n < cap) out[n] = c;
+        ++n;
+    }
+    return n;
+}
+
+int sgemm_tune(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
+               int32_t reps, void* stream, sgemm_config* winner, float* winner_ms) {
+    if (M < 1) return -1;
+    if (N < 1) return -2;
+    if (K < 1) return -3;
+    if (lda < K) return -4;
+    if (ldb < N) return -5;
+    if (ldc < N) return -6;
+    if (reps < 1) return -7;
+    if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return SGEMM_ERR_TOO_LARGE;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+
+    std::vector<sgemm_config> cands(kKernelCount);
+    const int nc = sgemm_tune_candidates(M, N, K, cands.data(), kKernelCount);
+    if (nc <= 0) return SGEMM_ERR_NO_CONFIG;
+    cands.resize(nc);
+
+    float *A = nullptr, *B = nullptr, *C = nullptr;
+    const int64_t na = (M - 1) * lda + K, nb = (K - 1) * ldb + N, ncm = (M - 1) * ldc + N;
+    if (hipMalloc(&A, na * sizeof(float)) != hipSuccess) return SGEMM_ERR_ALLOC;
+    if (hipMalloc(&B, nb * sizeof(float)) != hipSuccess) {
+        (void)hipFree(A);
+        return SGEMM_ERR_ALLOC;
+    }
+    if (hipMalloc(&C, ncm * sizeof(float)) != hipSuccess) {
+        (void)hipFree(A);
+        (void)hipFree(B);
+        return SGEMM_ERR_ALLOC;
+    }
+    int st = SGEMM_OK;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    std::vector<std::pair<float, int>> once;
+    auto time_one = [&](int entry, int n, float* ms) -> int {
+        if (hipEventRecord(e0, s) != hipSuccess) return SGEMM_ERR_HIP_BASE;
+        for (int r = 0; r < n; ++r) {
+            const int rc = launch_gemm(entry, M, N, K, 1.0f, A, lda, B, ldb, 0.0f, C, ldc, s);
+            if (rc != SGEMM_OK) return rc;
+        }
+        if (hipEventRecord(e1, s) != hipSuccess) return SGEMM_ERR_HIP_BASE;
+        if (hipEventSynchronize(e1) != hipSuccess) return SGEMM_ERR_HIP_BASE;
+        if (hipEventElapsedTime(ms, e0, e1) != hipSuccess) return SGEMM_ERR_HIP_BASE;
+        *ms /= (float)n;
+        return SGEMM_OK;
+    };
+    st = hip_status(phobos::launch_fill_pattern(A, na, 1u, s));
+    if (st == SGEMM_OK) st = hip_status(phobos::launch_fill_pattern(B, nb, 2u, s));
+    if (st == SGEMM_OK && hipEventCreate(&e0) != hipSuccess) st = SGEMM_ERR_HIP_BASE;
+    if (st == SGEMM_OK && hipEventCreate(&e1) != hipSuccess) st = SGEMM_ERR_HIP_BASE;
+    // every candidate once (after one untimed warm-up launch)
+    for (int i = 0; st == SGEMM_OK && i < nc; ++i) {
+        const int entry = find_entry(cands[i]);
+        float ms = 0.0f;
+        st = launch_gemm(entry, M, N, K, 1.0f, A, lda, B, ldb, 0.0f, C, ldc, s);
+        if (st == SGEMM_OK) st = time_one(entry, 1, &ms);
+        if (st == SGEMM_OK) once.emplace_back(ms, entry);
+    }
+    int best = -1;
+    float best_ms = 0.0f;
+    if (st == SGEMM_OK) {
+        // the best three get the long probe
+        std::sort(once.begin(), once.end());
+        const int top = std::min<int>(3, (int)once.size());
+        for (int i = 0; st == SGEMM_OK && i < top; ++i) {
+            float ms = 0.0f;
+            st = time_one(once[i].second, reps, &ms);
+            if (st == SGEMM_OK && (best < 0 || ms < best_ms)) {
+                best = once[i].second;
+                best_ms = ms;
+            }
+        }
+    }
+    if (e0) (void)hipEventDestroy(e0);
+    if (e1) (void)hipEventDestroy(e1);
+    (void)hipFree(A);
+    (void)hipFree(B);
+    (void)hipFree(C);
+    if (st != SGEMM_OK) return st;
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        g_tuned[ShapeKey{M, N, K, lda, ldb, ldc}] = best;
+    }
+    if (winner) *winner = kKernelTable[best].cfg;
+    if (winner_ms) *winner_ms = best_ms;
+    return SGEMM_OK;
+}
+
+int sgemm_trace_begin(int64_t capacity) {
+    if (capacity < 1) return -1;
+    std::lock_guard<std::mutex> lk(g_mu);
+    for (auto& r : g_trace) {
+        (void)hipEventDestroy(r.start);
+        (void)hipEventDestroy(r.stop);
+    }
+    g_trace.clear();
+    g_trace.reserve((size_t)std::min<int64_t>(capacity, 1 << 20));
+    g_trace_cap = capacity;
+    g_trace_on = true;
+    return SGEMM_OK;
+}
+
+int sgemm_trace_end(float* ms_out, int32_t* kind_out, int64_t cap, int64_t* n_out) {
+    if (cap < 0) return -3;
+    if (cap > 0 && (ms_out == nullptr || kind_out == nullptr)) return ms_out ? -2 : -1;
+    std::vector<TraceRec> recs;
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        g_trace_on = false;
+        recs.swap(g_trace);
+    }
+    int st = SGEMM_OK;
+    for (size_t i = 0; i < recs.size(); ++i) {
+        float ms = 0.0f;
+        if (st == SGEMM_OK) {
+            hipError_t e = hipEventSynchronize(recs[i].stop);
+            if (e == hipSuccess) e = hipEventElapsedTime(&ms, recs[i].start, recs[i].stop);
+            st = hip_status(e);
+        }
+        if ((int64_t)i < cap) {
+            ms_out[i] = ms;
+            kind_out[i] = recs[i].kind;
+        }
+        (void)hipEventDestroy(recs[i].start);
+        (void)hipEventDestroy(recs[i].stop);
+    }
+    if (n_out) *n_out = (int64_t)recs.size();
+    return st;
+}
+
+const char* sgemm_status_string(int status) {
+    if (status == SGEMM_OK) return "success";
+    if (status < 0) {
+        static const char* names[] = {"", "argument 1 is invalid", "argument 2 is invalid",
+                                      "argument 3 is invalid", "argument 4 is invalid",
+                                      "argument 5 is invalid", "argument 6 is invalid",
+                                      "argument 7 is invalid", "argument 8 is invalid",
+                                      "argument 9 is invalid", "argument 10 is invalid",
+                                      "argument 11 is invalid", "argument 12 is invalid",
+                                      "argument 13 is invalid", "argument 14 is invalid",
+                                      "argument 15 is invalid"};
+        if (status >= -15) return names[-status];
+        return "an argument is invalid";
+    }
+    switch (status) {
+        case SGEMM_ERR_NO_CONFIG: return "no compiled kernel configuration matches";
+        case SGEMM_ERR_TOO_LARGE: return "a dimension exceeds 2^30 or the grid 2^32-1 work-items";
+        case SGEMM_ERR_ALLOC: return "could not allocate tuner scratch memory";
+        default: break;
+    }
+    if (status >= SGEMM_ERR_HIP_BASE) return hipGetErrorString((hipError_t)(status - SGEMM_ERR_HIP_BASE));
+    return "unknown status";
+}
+
+int sgemm_version(void) { return PHOBOS_SGEMM_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,185 @@
+/*
+ * phobos_sgemm.h -- C ABI of the MI355X (gfx950) FP32 SGEMM library.
+ *
+ * The operation is C <- alpha*A*B + beta*C on 32-bit floats, as defined in
+ * "Show HN: Phobos - A tiny scale-free kernel language with tile-DAG
+ * support", section "Matrix Multiplication", and its two-level form with
+ * super-tiles and a cluster loop over K from the Phobos "@cluster" attribute
+ * page, section "What the cluster compiler accepts".
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Layout.  All matrices are row-major: element (i, j) of X is X[i*ldx + j].
+ *   A is M x K (lda >= max(1, K)), B is K x N (ldb >= max(1, N)),
+ *   C is M x N (ldc >= max(1, N)).  Elements past the logical width of a row
+ *   (the pads) are never read and never written.
+ * Memory.  A, B and C are device pointers (hipMalloc'ed or equivalent) owned
+ *   by the caller.  The library neither frees nor retains them.  They must
+ *   stay valid until the work enqueued on `stream` has finished.  C must not
+ *   overlap A or B (not checked).  The GEMM entry points allocate nothing.
+ * Streams.  `stream` is a hipStream_t passed as void* (NULL = the null
+ *   stream).  Calls are asynchronous: they enqueue kernels and return without
+ *   synchronising.
+ * beta == 0.  C is write-only: it is never read, so it may hold NaN or Inf,
+ *   and the result is alpha*A*B exactly as if C had been zero.
+ * Quick returns.  M == 0 or N == 0: nothing is enqueued.  K == 0 or
+ *   alpha == 0: A and B are not read and C <- beta*C (beta == 1: nothing is
+ *   enqueued; beta == 0: C <- 0).
+ * Accuracy.  Products and sums are fp32 (MFMA fp32 arithmetic, sums in an
+ *   order of the library's choosing), so results are within
+ *   2*K*2^-24*(|alpha|*(|A||B|)ij + |beta*Cij|) + 1e-30 of the exact value,
+ *   and exact whenever every partial sum is representable in fp32.
+ * Errors.  0 = success.  A negative value -i = the i-th argument is invalid
+ *   (numbered from 1 in the order of the prototype); every argument check
+ *   runs before any HIP call, so argument errors never touch the GPU.
+ *   SGEMM_ERR_* below for the other failures; 1000 + e = HIP error e was
+ *   reported by the runtime (hipGetLastError after the launches).
+ * Threads.  Calls on different streams may run concurrently.  The config
+ *   table and the trace buffer are guarded by a mutex; sgemm_tune must not
+ *   run concurrently with other calls on the same device.
+ */
+#ifndef PHOBOS_SGEMM_H
+#define PHOBOS_SGEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PHOBOS_SGEMM_VERSION 1
+
+#define SGEMM_OK 0
+#define SGEMM_ERR_NO_CONFIG 2      /* no compiled kernel matches the request   */
+#define SGEMM_ERR_TOO_LARGE 3      /* a dimension exceeds 2^30, or the launch   */
+                                   /* grid exceeds 2^32-1 work-items           */
+#define SGEMM_ERR_ALLOC 4          /* sgemm_tune could not allocate scratch    */
+#define SGEMM_ERR_HIP_BASE 1000    /* 1000 + hipError_t                        */
+
+/*
+ * A compiled kernel configuration: the CTA tile bm x bn (rows x columns of
+ * C one workgroup owns) stepped through K in chunks of bk, computed by
+ * wm x wn wavefronts of 64 lanes (workgroup = 64*wm*wn threads).  These are
+ * the TILE_M / TILE_N / TILE_K of the pages' @autotune attribute ("Show HN:
+ * Phobos", sections "Introducing the Phobos Language" and "Runtime").
+ */
+typedef struct sgemm_config {
+    int32_t bm, bn, bk, wm, wn;
+} sgemm_config;
+
+/*
+ * sgemm: C <- alpha*A*B + beta*C in one launch (the single-GPU kernel of
+ * "Show HN: Phobos", section "Matrix Multiplication"; on one GPU the
+ * @cluster line is ignored, "@cluster" page, section "On one GPU").
+ * Arguments: 1 M, 2 N, 3 K, 4 alpha, 5 A, 6 lda, 7 B, 8 ldb, 9 beta, 10 C,
+ * 11 ldc, 12 stream.  A and B may be NULL when they are not read (M, N or K
+ * zero, or alpha == 0); C may be NULL when M or N is zero.
+ */
+int sgemm(int64_t M, int64_t N, int64_t K, float alpha,
+          const float* A, int64_t lda, const float* B, int64_t ldb,
+          float beta, float* C, int64_t ldc, void* stream);
+
+/*
+ * sgemm_supertiled: the same result through the two-level decomposition of
+ * the "@cluster" page ("What the cluster compiler accepts": the matmul kernel
+ * with a cluster loop, split into an init leaf and a step leaf whose
+ * accumulator lives in the output's own buffer) and the conceptual cluster IR
+ * of "Show HN: Phobos", section "The DAG Compiler".
+ * For each output super-tile (pm, pn) of TM x TN, in row-major order
+ * (pm outer, pn inner, as the runtime deals them out, "@cluster" page,
+ * "What runs today"), it enqueues on `stream`:
+ *   one init leaf:  C[pm,pn] <- beta*C[pm,pn]   (0 when beta == 0, C unread)
+ *   then for kt = 0 .. ceil(K/TK)-1, one step leaf:
+ *                   C[pm,pn] <- alpha*A[pm,kt]*B[kt,pn] + C[pm,pn]
+ * i.e. beta is hoisted into the init leaf and every step stores with an
+ * implicit beta of 1 ("Show HN: Phobos", section "Clustering").  C holds the
+ * fp32 partial sum between steps.  Stream order makes each super-tile's steps
+ * a chain.  Edge super-tiles are clipped to the matrix (the pages' runtime
+ * rejects sizes that are not whole multiples; this library accepts them).
+ * Arguments: 1..11 as sgemm, 12 TM, 13 TN, 14 TK (each >= 1), 15 stream.
+ */
+int sgemm_supertiled(int64_t M, int64_t N, int64_t K, float alpha,
+                     const float* A, int64_t lda, const float* B, int64_t ldb,
+                     float beta, float* C, int64_t ldc,
+                     int64_t TM, int64_t TN, int64_t TK, void* stream);
+
+/*
+ * sgemm_init_leaf: the init leaf on its own, C <- beta*C over an M x N view
+ * (C <- 0 without reading C when beta == 0; nothing is enqueued when
+ * beta == 1).  "@cluster" page, "What the cluster compiler accepts": the init
+ * leaf zeroes the output super-tile or scales it by beta.
+ * Arguments: 1 M, 2 N, 3 beta, 4 C, 5 ldc, 6 stream.
+ */
+int sgemm_init_leaf(int64_t M, int64_t N, float beta, float* C, int64_t ldc,
+                    void* stream);
+
+/*
+ * Kernel configurations.
+ * sgemm_config_count / sgemm_config_at list the compiled configurations
+ * (index 0 .. count-1; -1 for a bad index).
+ * sgemm_get_config reports the configuration sgemm would launch for this
+ * shape and these leading dimensions (a forced one, else a tuned one, else
+ * the built-in default); returns 0 or a negative argument error
+ * (1 M, 2 N, 3 K, 4 lda, 5 ldb, 6 ldc, 7 out).
+ * sgemm_set_config forces one compiled configuration for every later call in
+ * the process (NULL clears the forcing); returns SGEMM_ERR_NO_CONFIG when
+ * `cfg` names no compiled configuration.
+ */
+int sgemm_config_count(void);
+int sgemm_config_at(int32_t index, sgemm_config* out);
+int sgemm_get_config(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
+                     int64_t ldc, sgemm_config* out);
+int sgemm_set_config(const sgemm_config* cfg);
+
+/*
+ * The tile tuner, after "Show HN: Phobos", section "Runtime": every candidate
+ * tile is built ahead of time; each is timed once, the best three get a
+ * longer run, and the fastest of those wins.
+ * sgemm_tune_candidates (host only, no GPU work) writes into `out` (room for
+ * `cap`) the compiled configurations that survive pruning for this shape:
+ * tile extents inside the @autotune ranges of the "@cluster" page's matmul
+ * (TILE_M, TILE_N in [32, 256], TILE_K in [4, 32]) and no tile larger than the
+ * problem needs (bm <= max(32, roundup32(M)), bn <= max(32, roundup32(N))).
+ * Returns the number of candidates, or a negative argument error
+ * (1 M, 2 N, 3 K, 4 out, 5 cap).
+ * sgemm_tune times the candidates on scratch buffers it allocates and frees
+ * itself (inputs filled with a fixed pseudo-random pattern), then records
+ * the winner for this (M, N, K, lda, ldb, ldc) so that later sgemm calls of
+ * that shape use it.  `reps` is the number of timed runs of each of the top
+ * three (>= 1; the pages' long probe).  `winner` (may be NULL) receives the
+ * choice and `winner_ms` (may be NULL) its mean time.  Synchronises
+ * `stream`.  Arguments: 1 M, 2 N, 3 K, 4 lda, 5 ldb, 6 ldc, 7 reps,
+ * 8 stream, 9 winner, 10 winner_ms.
+ */
+int sgemm_tune_candidates(int64_t M, int64_t N, int64_t K, sgemm_config* out,
+                          int32_t cap);
+int sgemm_tune(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
+               int32_t reps, void* stream, sgemm_config* winner, float* winner_ms);
+
+/*
+ * Launch trace.  Between sgemm_trace_begin(capacity) and sgemm_trace_end,
+ * every kernel the library enqueues is bracketed by a pair of HIP events
+ * recorded on the launch's own stream (up to `capacity` launches; later ones
+ * are not traced).  sgemm_trace_end waits for those events, writes each
+ * launch's duration in milliseconds to ms_out[i] and its kind to kind_out[i]
+ * (SGEMM_KIND_*), for i < min(count, cap), stores the count in *n_out and
+ * frees the events.  Arguments of begin: 1 capacity (>= 1).  Of end:
+ * 1 ms_out, 2 kind_out, 3 cap, 4 n_out (the output arrays may be NULL when
+ * cap is 0).
+ */
+#define SGEMM_KIND_GEMM 0
+#define SGEMM_KIND_INIT_LEAF 1
+int sgemm_trace_begin(int64_t capacity);
+int sgemm_trace_end(float* ms_out, int32_t* kind_out, int64_t cap, int64_t* n_out);
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char* sgemm_status_string(int status);
+
+/* PHOBOS_SGEMM_VERSION of the built library. */
+int sgemm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PHOBOS_SGEMM_H */

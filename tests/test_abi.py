@@ -1,0 +1,170 @@
+"""The C-ABI library on the CPU: it loads, exports every declared entry point,
+and checks its arguments before any HIP call (no GPU work is started here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import fp32_gemm_02_amd as g
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "phobos_sgemm.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w]*\s*\*?\s*(sgemm\w*)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for want in ("sgemm", "sgemm_supertiled", "sgemm_init_leaf", "sgemm_tune",
+                 "sgemm_tune_candidates", "sgemm_set_config", "sgemm_get_config",
+                 "sgemm_config_count", "sgemm_config_at", "sgemm_trace_begin",
+                 "sgemm_trace_end", "sgemm_status_string", "sgemm_version"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(g.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    # and the binding carries a prototype for each
+    assert set(declared_functions()) == set(g._SIGNATURES)
+
+
+def test_version():
+    assert g.version() == 1
+
+
+NULL = None
+
+
+@pytest.mark.parametrize("args,want", [
+    ((-1, 4, 4, 1.0, 8, 4, 8, 4, 0.0, 8, 4), -1),
+    ((4, -1, 4, 1.0, 8, 4, 8, 4, 0.0, 8, 4), -2),
+    ((4, 4, -1, 1.0, 8, 4, 8, 4, 0.0, 8, 4), -3),
+    ((4, 4, 5, 1.0, 8, 4, 8, 4, 0.0, 8, 4), -6),     # lda < K
+    ((4, 4, 0, 1.0, 8, 0, 8, 4, 0.0, 8, 4), -6),     # lda < 1
+    ((4, 6, 4, 1.0, 8, 4, 8, 5, 0.0, 8, 6), -8),     # ldb < N
+    ((4, 6, 4, 1.0, 8, 4, 8, 6, 0.0, 8, 5), -11),    # ldc < N
+    ((4, 4, 4, 1.0, NULL, 4, 8, 4, 0.0, 8, 4), -5),  # A read but NULL
+    ((4, 4, 4, 1.0, 8, 4, NULL, 4, 0.0, 8, 4), -7),  # B read but NULL
+    ((4, 4, 4, 1.0, 8, 4, 8, 4, 0.0, NULL, 4), -10),  # C NULL
+    ((0, 4, 4, 1.0, NULL, 4, NULL, 4, 0.0, NULL, 4), 0),  # M == 0: no-op
+    ((4, 0, 4, 1.0, NULL, 4, NULL, 1, 0.0, NULL, 1), 0),  # N == 0: no-op
+    ((1 << 31, 4, 4, 1.0, 8, 4, 8, 4, 0.0, 8, 4), g.SGEMM_ERR_TOO_LARGE),
+])
+def test_sgemm_argument_checks(args, want):
+    assert g.sgemm_raw(*args, stream=0) == want
+
+
+@pytest.mark.parametrize("tiles,want", [((0, 4, 4), -12), ((4, 0, 4), -13), ((4, 4, 0), -14),
+                                        ((-3, 4, 4), -12)])
+def test_supertiled_argument_checks(tiles, want):
+    assert g.sgemm_supertiled_raw(4, 4, 4, 1.0, 8, 4, 8, 4, 1.0, 8, 4, *tiles, stream=0) == want
+    # the GEMM arguments are checked first, with the same numbering as sgemm
+    assert g.sgemm_supertiled_raw(4, 4, 4, 1.0, 8, 3, 8, 4, 1.0, 8, 4, *tiles, stream=0) == -6
+
+
+def test_init_leaf_argument_checks():
+    lib = g.lib()
+    assert lib.sgemm_init_leaf(-1, 4, 1.0, 8, 4, None) == -1
+    assert lib.sgemm_init_leaf(4, -1, 1.0, 8, 4, None) == -2
+    assert lib.sgemm_init_leaf(4, 4, 1.0, None, 4, None) == -4
+    assert lib.sgemm_init_leaf(4, 4, 1.0, 8, 3, None) == -5
+    assert lib.sgemm_init_leaf(0, 4, 0.0, None, 4, None) == 0
+
+
+def test_status_strings():
+    assert g.status_string(0) == "success"
+    assert g.status_string(-6) == "argument 6 is invalid"
+    assert "no compiled kernel" in g.status_string(g.SGEMM_ERR_NO_CONFIG)
+    assert g.status_string(g.SGEMM_ERR_HIP_BASE + 1)  # HIP's own text
+    assert g.status_string(500) == "unknown status"
+
+
+def test_config_table_and_forcing():
+    cfgs = g.configs()
+    assert len(cfgs) >= 4
+    for c in cfgs:
+        # each tile is whole 32x32 MFMA blocks per wave, B reads 1, 2 or 4 wide
+        assert c.bm % (32 * c.wm) == 0 and c.bn % (32 * c.wn) == 0
+        assert (c.bn // c.wn // 32) in (1, 2, 4)
+        assert c.bk % 8 == 0
+    lib = g.lib()
+    assert lib.sgemm_config_at(-1, ctypes.byref(g.sgemm_config())) == -1
+    assert lib.sgemm_config_at(len(cfgs), ctypes.byref(g.sgemm_config())) == -1
+    try:
+        for c in cfgs:
+            g.sgemm_set_config(c)
+            assert g.sgemm_get_config(4096, 4096, 4096, 4096, 4096, 4096).as_tuple() == c.as_tuple()
+        with pytest.raises(g.SgemmError) as e:
+            g.sgemm_set_config((48, 48, 16, 1, 1))
+        assert e.value.status == g.SGEMM_ERR_NO_CONFIG
+    finally:
+        g.sgemm_set_config(None)
+
+
+def test_get_config_checks():
+    lib = g.lib()
+    out = g.sgemm_config()
+    assert lib.sgemm_get_config(-1, 4, 4, 4, 4, 4, ctypes.byref(out)) == -1
+    assert lib.sgemm_get_config(4, 4, 8, 4, 4, 4, ctypes.byref(out)) == -4
+    assert lib.sgemm_get_config(4, 8, 4, 4, 4, 8, ctypes.byref(out)) == -5
+    assert lib.sgemm_get_config(4, 8, 4, 4, 8, 4, ctypes.byref(out)) == -6
+    assert lib.sgemm_get_config(4, 4, 4, 4, 4, 4, None) == -7
+
+
+def test_default_config_fits_the_shape():
+    names = {c.as_tuple() for c in g.configs()}
+    for shape in [(1, 1, 1), (31, 17, 5), (256, 256, 256), (4096, 4096, 4096),
+                  (65536, 512, 4096), (5003, 3001, 2047)]:
+        M, N, K = shape
+        c = g.sgemm_get_config(M, N, K, K, N, N)
+        assert c.as_tuple() in names
+        # a small problem never gets a tile much larger than itself
+        assert c.bm <= max(64, 2 * M) and c.bn <= max(64, 2 * N)
+
+
+def _pow2_between(v, lo, hi):
+    return lo <= v <= hi and (v & (v - 1)) == 0
+
+
+def test_tune_candidates_follow_the_autotune_ranges():
+    all_cfgs = g.configs()
+    cands = g.sgemm_tune_candidates(4096, 4096, 4096)
+    assert len(cands) >= 4
+    for c in cands:
+        assert _pow2_between(c.bm, 32, 256) and _pow2_between(c.bn, 32, 256)
+        assert _pow2_between(c.bk, 4, 32)
+    # a small problem prunes tiles larger than it needs
+    small = g.sgemm_tune_candidates(40, 70, 100)
+    assert small and all(c.bm <= 64 and c.bn <= 96 for c in small)
+    assert len(small) < len(all_cfgs)
+    tiny = g.sgemm_tune_candidates(1, 1, 1)
+    assert [c.as_tuple()[:2] for c in tiny] == [(32, 32)]
+
+
+def test_tune_candidates_and_tune_argument_checks():
+    lib = g.lib()
+    assert lib.sgemm_tune_candidates(-1, 4, 4, None, 0) == -1
+    assert lib.sgemm_tune_candidates(4, 4, 4, None, 3) == -4
+    assert lib.sgemm_tune_candidates(4, 4, 4, None, -1) == -5
+    assert lib.sgemm_tune_candidates(4, 4, 4, None, 0) > 0   # count only
+    assert lib.sgemm_tune(0, 4, 4, 4, 4, 4, 5, None, None, None) == -1
+    assert lib.sgemm_tune(4, 4, 4, 3, 4, 4, 5, None, None, None) == -4
+    assert lib.sgemm_tune(4, 4, 4, 4, 4, 4, 0, None, None, None) == -7
+
+
+def test_trace_argument_checks():
+    lib = g.lib()
+    assert lib.sgemm_trace_begin(0) == -1
+    assert lib.sgemm_trace_begin(4) == 0
+    n = ctypes.c_int64(-1)
+    assert lib.sgemm_trace_end(None, None, 0, ctypes.byref(n)) == 0
+    assert n.value == 0
+    assert lib.sgemm_trace_end(None, None, -1, None) == -3

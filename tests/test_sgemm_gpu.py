@@ -1,0 +1,215 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle on the GPU."""
+import numpy as np
+import pytest
+import torch
+
+import fp32_gemm_02_amd as g
+import sgemm_workloads as wl
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+def _forced(cfg):
+    class _Ctx:
+        def __enter__(self):
+            g.sgemm_set_config(cfg)
+
+        def __exit__(self, *a):
+            g.sgemm_set_config(None)
+    return _Ctx()
+
+
+# ---------------------------------------------------------------------------
+# init leaf
+@pytest.mark.parametrize("M,N,ldc,offset", [(1, 1, 1, 0), (37, 53, 60, 0), (300, 1030, 1032, 0),
+                                            (129, 259, 263, 1), (64, 8, 8, 3)])
+@pytest.mark.parametrize("beta", [0.0, 0.5, -3.0, 1.0])
+def test_init_leaf_bit_exact(M, N, ldc, offset, beta):
+    w = wl.custom(M, N, 1, 1.0, beta, ("U", "U", "NaN" if beta == 0 else "U"), seed=M + N,
+                  ldc=ldc)
+    x = wl.make_inputs(w)
+    buf = np.concatenate([np.full(offset, 7.0, np.float32), x.C])
+    d = gu.to_dev(buf)
+    g.sgemm_init_leaf(M, N, beta, d[offset:], ldc)
+    torch.cuda.synchronize()
+    out = d.cpu().numpy()
+    assert np.array_equal(out[:offset], buf[:offset])
+    out = out[offset:]
+    got = gu.logical_c(w, out)
+    c = x.logical("C")
+    if beta == 0:
+        assert np.all(got == 0) and not np.isnan(got).any()
+    else:
+        want = (np.float32(beta) * c).astype(np.float32)
+        assert np.array_equal(got.view(np.int32), want.view(np.int32))
+    gu.check_pads(w, x, out)
+
+
+# ---------------------------------------------------------------------------
+# every compiled configuration, shapes around its tile edges, both load paths
+def _cfg_id(c):
+    return "%dx%dx%d_w%dx%d" % c.as_tuple()
+
+
+def _all_cfgs():
+    try:
+        return g.configs()
+    except Exception:   # library not built: the other tests fail loudly
+        return []
+
+
+@pytest.mark.parametrize("cfg", _all_cfgs(), ids=_cfg_id)
+def test_tile_edges_every_config(cfg):
+    bm, bn, bk = cfg.bm, cfg.bn, cfg.bk
+    shapes = [(1, bn + 1, 1), (bm + 1, bn - 1, bk + 1), (2 * bm + 3, 2 * bn + 5, 3 * bk + 5),
+              (bm - 1, 1, 2), (bm, bn, bk), (3, 7, 2 * bk - 1)]
+    with _forced(cfg):
+        for i, (M, N, K) in enumerate(shapes):
+            vec = i % 2 == 0
+            lda = K + (4 - K % 4) % 4 + 4 if vec else K + 1 + (K % 2)
+            ldb = N + (4 - N % 4) % 4 if vec else N + 3
+            ldc = N + (4 - N % 4) % 4 + 8 if vec else N + 1
+            if not vec:
+                lda |= 1
+                ldb |= 1
+                ldc |= 1
+            w = wl.custom(M, N, K, 1.25, -0.5, seed=100 + i, lda=lda, ldb=ldb, ldc=ldc,
+                          name=f"{_cfg_id(cfg)}_{M}x{N}x{K}")
+            x = wl.make_inputs(w)
+            gu.check_full(w, x, gu.run(w, x), relaxed=True)
+            wi = w.integer_variant()
+            xi = wl.make_inputs(wi)
+            gu.check_full(wi, xi, gu.run(wi, xi), exact=True)
+
+
+# ---------------------------------------------------------------------------
+# the five workloads, at full size, in the configuration the benchmark uses
+def test_workload_256():
+    w = wl.BY_NAME["sgemm_256"]
+    x = wl.make_inputs(w)
+    gu.check_full(w, x, gu.run(w, x))
+    wi = w.integer_variant()
+    xi = wl.make_inputs(wi)
+    gu.check_full(wi, xi, gu.run(wi, xi), exact=True)
+
+
+def test_workload_4096_beta0_nan_c():
+    w = wl.BY_NAME["sgemm_4096_beta0"]
+    x = wl.make_inputs(w)
+    out = gu.run(w, x)
+    assert not np.isnan(gu.logical_c(w, out)).any()
+    gu.check_sampled(w, x, out)
+    gu.check_freivalds(w, x, out)
+    gu.check_pads(w, x, out)
+    # beta = 0 never reads C: a finite C gives the same bits
+    wf = w.with_dists(("N", "N", "U"), "_finite_c")
+    xf = wl.make_inputs(wf)
+    assert np.array_equal(xf.A.view(np.int32), x.A.view(np.int32))
+    assert np.array_equal(xf.B.view(np.int32), x.B.view(np.int32))
+    outf = gu.run(wf, xf)
+    assert np.array_equal(gu.logical_c(w, out).view(np.int32),
+                          gu.logical_c(wf, outf).view(np.int32))
+    wi = w.integer_variant()
+    xi = wl.make_inputs(wi)
+    outi = gu.run(wi, xi)
+    gu.check_sampled(wi, xi, outi, exact=True)
+    gu.check_freivalds(wi, xi, outi)
+
+
+def test_workload_tall_skinny():
+    w = wl.BY_NAME["tall_skinny_65536x512x4096"]
+    x = wl.make_inputs(w)
+    out = gu.run(w, x)
+    gu.check_sampled(w, x, out)
+    gu.check_freivalds(w, x, out)
+    gu.check_pads(w, x, out)
+    wi = w.integer_variant()
+    xi = wl.make_inputs(wi)
+    gu.check_sampled(wi, xi, gu.run(wi, xi), exact=True)
+
+
+def _slab(w, x, r0, rows):
+    """The workload restricted to rows r0 .. r0+rows-1 (same buffers, offset)."""
+    ws = wl.Workload(w.name + f"_rows{r0}", w.entry, rows, w.N, w.K, w.lda, w.ldb, w.ldc,
+                     w.alpha, w.beta, w.dists, w.seed)
+    xs = wl.Inputs(ws, x.A[r0 * w.lda:], x.B, x.C[r0 * w.ldc:])
+    return ws, xs
+
+
+def test_workload_unaligned_padded():
+    w = wl.BY_NAME["unaligned_5003x3001x2047"]
+    x = wl.make_inputs(w)
+    out = gu.run(w, x)
+    gu.check_pads(w, x, out)
+    gu.check_sampled(w, x, out)
+    gu.check_freivalds(w, x, out)
+    # every element of the first and the last (ragged) row slabs, against the full oracle
+    for r0, rows in ((0, 96), (w.M - 139, 139)):
+        ws, xs = _slab(w, x, r0, rows)
+        outs = out[r0 * w.ldc:]
+        ref, bnd = gu.oracle.sgemm(rows, w.N, w.K, w.alpha, xs.A, xs.B, w.beta, xs.C,
+                                   lda=w.lda, ldb=w.ldb, ldc=w.ldc)
+        got = outs[: rows * w.ldc].reshape(rows, w.ldc)[:, : w.N]
+        err = np.abs(got.astype(np.float64) - ref)
+        assert np.all(err <= bnd), (r0, (err / bnd).max())
+    wi = w.integer_variant()
+    xi = wl.make_inputs(wi)
+    outi = gu.run(wi, xi)
+    gu.check_sampled(wi, xi, outi, exact=True)
+    gu.check_pads(wi, xi, outi)
+
+
+# ---------------------------------------------------------------------------
+# quick returns and special scalars
+@pytest.mark.parametrize("alpha,K", [(0.0, 37), (1.5, 0)])
+@pytest.mark.parametrize("beta", [0.0, 1.0, -0.75])
+def test_quick_returns(alpha, K, beta):
+    w = wl.custom(70, 45, K, alpha, beta, ("U", "U", "NaN" if beta == 0 else "U"), seed=5,
+                  lda=max(K, 1) + 3, ldc=48)
+    x = wl.make_inputs(w)
+    out = gu.run(w, x)
+    got = gu.logical_c(w, out)
+    c = x.logical("C")
+    if beta == 0:
+        assert np.all(got == 0)
+    else:
+        want = (np.float32(beta) * c).astype(np.float32)
+        assert np.array_equal(got.view(np.int32), want.view(np.int32))
+    gu.check_pads(w, x, out)
+
+
+def test_misaligned_pointers_take_the_scalar_path():
+    w = wl.custom(211, 157, 93, 0.75, 1.5, seed=21, lda=96, ldb=160, ldc=160)
+    x = wl.make_inputs(w)
+    pad = np.full(1, 3.0, np.float32)
+    dA = gu.to_dev(np.concatenate([pad, x.A]))
+    dB = gu.to_dev(np.concatenate([pad, pad, x.B]))
+    dC = gu.to_dev(np.concatenate([pad, x.C]))
+    g.sgemm(w.M, w.N, w.K, w.alpha, dA[1:], w.lda, dB[2:], w.ldb, w.beta, dC[1:], w.ldc)
+    torch.cuda.synchronize()
+    out = dC.cpu().numpy()
+    assert out[0] == 3.0
+    gu.check_full(w, x, out[1:])
+
+
+def test_runs_on_a_side_stream():
+    w = wl.custom(260, 190, 150, 1.0, 0.5, seed=31)
+    x = wl.make_inputs(w)
+    dA, dB, dC = gu.to_dev(x.A), gu.to_dev(x.B), gu.to_dev(x.C)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g.sgemm(w.M, w.N, w.K, w.alpha, dA, w.lda, dB, w.ldb, w.beta, dC, w.ldc, stream=s)
+    s.synchronize()
+    gu.check_full(w, x, dC.cpu().numpy())
+
+
+def test_tuner_records_a_winner_that_is_correct():
+    M, N, K = 600, 520, 300
+    cands = {c.as_tuple() for c in g.sgemm_tune_candidates(M, N, K)}
+    cfg, ms = g.sgemm_tune(M, N, K, K, N, N, reps=5)
+    assert cfg.as_tuple() in cands and ms > 0
+    assert g.sgemm_get_config(M, N, K, K, N, N).as_tuple() == cfg.as_tuple()
+    w = wl.custom(M, N, K, -1.0, 2.0, seed=41)
+    x = wl.make_inputs(w)
+    gu.check_full(w, x, gu.run(w, x))
