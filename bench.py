@@ -1,0 +1,196 @@
+"""Benchmark: super-tiled FP32 SGEMM, M = N = K = 16384, 4096^3 super-tiles, 1 GPU.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step is one sgemm_supertiled call through the C ABI: argument checks,
+the row-major walk over the 4 x 4 grid of output super-tiles, and per
+super-tile the init leaf (a no-op launch-free identity at beta = 1) and four
+step leaves of 4096^3 each (64 GEMM launches per step).  Inputs are seeded
+synthetic uniform[-1, 1) matrices (the oracle's generators), resident in HBM
+before the timed region.  C keeps accumulating across steps (beta = 1); that
+changes no timing and the result is checked separately by the GPU tests.
+
+Printed: one JSON line with the metric (GFLOP/s = 2*M*N*K / time per step),
+the roofline of the dominant kernel (the step leaf; its duration per launch
+from HIP events the library records on the launch stream during the timed
+region) and the CPU oracle's rate on a bounded slab of the same product.
+
+Options for profiling runs: --copy-calibration runs one plain device copy of
+1 GiB first (a known-size reference for the HBM byte counters);
+--skip-cpu-baseline leaves the oracle leg out.
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP32_MFMA_TFLOPS = 157.3     # MI355X published dense FP32 matrix peak
+PEAK_HBM_GBS = 8000.0             # MI355X published HBM3E bandwidth
+WORKLOAD = "supertiled_16384_t4096"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sgemm_step_4096_ld16384.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "fp32_gemm_02_amd", "csrc", "sgemm_kernels.hip")]
+
+
+def gflops(M, N, K, ms):
+    """The pages' convention: 2*M*N*K floating-point operations per product."""
+    return 2.0 * M * N * K / (ms * 1e-3) / 1e9
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per step-leaf launch from the committed counter summary, if it
+    was taken on the current kernel source; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    m_hash = re.search(r"^kernel_source_sha256_16:\s*(\S+)", text, re.M)
+    m_bytes = re.search(r"^hbm_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+def cpu_baseline(x, w, target_s=15.0):
+    """The oracle as it stands, on a slab of rows of the same product."""
+    import oracle
+
+    orc = oracle.default()
+    threads = orc.max_threads()
+
+    def run(rows):
+        t0 = time.perf_counter()
+        orc.sgemm(rows, w.N, w.K, w.alpha, x.A, x.B, w.beta, x.C, lda=w.lda, ldb=w.ldb,
+                  ldc=w.ldc)
+        return time.perf_counter() - t0
+
+    probe_rows = max(8, threads)
+    t = run(probe_rows)
+    rows = int(min(w.M, max(probe_rows, probe_rows * target_s / max(t, 1e-3))))
+    rows = max(threads, rows - rows % max(1, threads))
+    t = run(rows)
+    return {
+        "value": round(gflops(rows, w.N, w.K, t * 1e3), 3),
+        "unit": "GFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"rows 0..{rows - 1} of the {w.M}x{w.N}x{w.K} product "
+                  f"({rows}x{w.N}x{w.K}, {t:.1f} s, fp64 accumulation and bound)",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--skip-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: the super-tile grid of this workload is one "
+              "GPU's share, and no multi-GPU path is built (use --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import fp32_gemm_02_amd as g
+    import sgemm_workloads as wl
+
+    w = wl.BY_NAME[WORKLOAD]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.Stream(device=dev)
+
+    x = wl.make_inputs(w)
+    with torch.cuda.stream(stream):
+        dA = torch.from_numpy(x.A).to(dev, non_blocking=False)
+        dB = torch.from_numpy(x.B).to(dev, non_blocking=False)
+        dC = torch.from_numpy(x.C).to(dev, non_blocking=False)
+        if args.copy_calibration:
+            src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+            dst = torch.empty_like(src)
+            dst.copy_(src)
+            del src, dst
+    stream.synchronize()
+
+    def step():
+        g.sgemm_supertiled(w.M, w.N, w.K, w.alpha, dA, w.lda, dB, w.ldb, w.beta, dC, w.ldc,
+                           w.TM, w.TN, w.TK, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    stream.synchronize()
+
+    launches_per_step = (w.M // w.TM) * (w.N // w.TN) * (w.K // w.TK)
+    g.sgemm_trace_begin(args.steps * launches_per_step * 2 + 16)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    stream.synchronize()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = e0.elapsed_time(e1)
+    ms_kern, kinds, n = g.sgemm_trace_end(cap=args.steps * launches_per_step * 2 + 16)
+    ms_per_step = ms_total / args.steps
+    value = gflops(w.M, w.N, w.K, ms_per_step)
+
+    step_ms = [t for t, k in zip(ms_kern, kinds) if k == g.SGEMM_KIND_GEMM]
+    avg_launch_ms = float(np.mean(step_ms))
+    step_flops = 2.0 * w.TM * w.TN * w.TK
+    achieved_tflops = step_flops / (avg_launch_ms * 1e-3) / 1e12
+    traffic = measured_traffic()
+
+    out = {
+        "metric": "SGEMM GFLOP/s and % of MI355X FP32 matrix peak at 16384^3, 1 GPU",
+        "value": round(value, 1),
+        "unit": "GFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD, "entry": "sgemm_supertiled", "M": w.M, "N": w.N,
+                   "K": w.K, "TM": w.TM, "TN": w.TN, "TK": w.TK, "alpha": w.alpha,
+                   "beta": w.beta, "inputs": "uniform[-1,1) seed 2",
+                   "step_leaf_config": "bm=%d bn=%d bk=%d wm=%d wn=%d" %
+                   g.sgemm_get_config(w.TM, w.TN, w.TK, w.lda, w.ldb, w.ldc).as_tuple(),
+                   "launches_per_step": launches_per_step,
+                   "pct_of_fp32_matrix_peak": round(100.0 * value / 1e3 / PEAK_FP32_MFMA_TFLOPS, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved_tflops, 2),
+                     "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved_tflops / PEAK_FP32_MFMA_TFLOPS, 4),
+                     "traffic": traffic},
+    }
+    if not args.skip_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(x, w)
+    print(f"# timed {args.steps} steps: {ms_total:.2f} ms on the stream ({wall * 1e3:.2f} ms "
+          f"wall); {len(step_ms)} step-leaf launches traced, mean {avg_launch_ms:.4f} ms",
+          file=sys.stderr, flush=True)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
