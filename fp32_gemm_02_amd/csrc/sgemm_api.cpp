@@ -76,7 +76,7 @@ int env_int(const char* name, int dflt) {
 int default_entry(int64_t M, int64_t N, int64_t K) {
     struct Pick { int bm, bn, bk, wm, wn; };
     static const Pick order[] = {
-        {256, 256, 16, 2, 2}, {256, 128, 16, 2, 2}, {128, 128, 16, 2, 2},
+        {256, 256, 16, 4, 2}, {256, 128, 16, 4, 2}, {128, 128, 16, 2, 2},
         {128, 64, 16, 2, 1},  {64, 64, 16, 1, 1},
     };
     (void)K;
@@ -89,10 +89,33 @@ int default_entry(int64_t M, int64_t N, int64_t K) {
     return find_entry({64, 64, 16, 1, 1});
 }
 
+// SGEMM_FORCE_CFG="BMxBNxBKxWMxWN" (e.g. 256x256x32x2x2) forces a compiled
+// configuration for the whole process, like sgemm_set_config; read once.
+int env_forced_entry() {
+    static const int entry = [] {
+        const char* v = std::getenv("SGEMM_FORCE_CFG");
+        if (!v || !*v) return -1;
+        sgemm_config c{};
+        if (std::sscanf(v, "%dx%dx%dx%dx%d", &c.bm, &c.bn, &c.bk, &c.wm, &c.wn) != 5) {
+            std::fprintf(stderr, "phobos_sgemm: ignoring malformed SGEMM_FORCE_CFG=%s\n", v);
+            return -1;
+        }
+        const int e = find_entry(c);
+        if (e < 0) std::fprintf(stderr, "phobos_sgemm: SGEMM_FORCE_CFG=%s is not compiled\n", v);
+        return e;
+    }();
+    return entry;
+}
+
 int choose_entry(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc) {
     {
         std::lock_guard<std::mutex> lk(g_mu);
         if (g_forced >= 0) return g_forced;
+    }
+    const int env = env_forced_entry();
+    if (env >= 0) return env;
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
         auto it = g_tuned.find(ShapeKey{M, N, K, lda, ldb, ldc});
         if (it != g_tuned.end()) return it->second;
     }

@@ -6,14 +6,22 @@
 // Multiplication"), then stores alpha*acc + beta*C.  The techniques the blog
 // lists in "GPU Performance" (coalescing, a shared-memory tile per CTA, a
 // per-warp register micro-tile free of bank conflicts, the matrix units) and
-// the ping-pong buffering of "Are we cuBLAS yet?" map onto CDNA4 as:
+// the ping-pong buffering and XOR swizzling of "Are we cuBLAS yet?" map onto
+// CDNA4 as:
 //   - global -> LDS with 128-bit loads, consecutive lanes on consecutive
-//     addresses; one stage in flight in registers while the other is used;
+//     addresses.  Interior chunks use gfx950's direct global-to-LDS loads
+//     (global_load_lds_dwordx4: each lane fetches 16 bytes, the wave writes
+//     its 64 x 16 bytes contiguously into LDS, no registers in between);
+//     chunks at an edge of M, N or K go through registers with per-element
+//     bounds checks and zero fill;
 //   - two LDS stages (double buffering), one barrier per K chunk;
 //   - each 64-lane wavefront owns a TWM x TWN sub-tile made of MB x NB blocks
 //     of 32 x 32, accumulated by v_mfma_f32_32x32x2_f32 in registers for the
 //     whole K loop;
-//   - LDS rows of A padded so that the MFMA operand reads are conflict free.
+//   - the A tile is stored row-major without padding, its 16-byte pieces
+//     XOR-swizzled within each row, so that the MFMA operand reads are free of
+//     LDS bank conflicts (the swizzle is applied to the global addresses of
+//     the direct loads, since those write LDS in lane order).
 //
 // MFMA 32x32x2 f32 operand layout (one block, 64 lanes, l = lane):
 //   src A: lane l holds A'[l % 32][l / 32]      (32 x 2)
@@ -32,6 +40,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "sgemm_internal.h"
 
 namespace phobos {
@@ -39,29 +49,62 @@ namespace phobos {
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void global_cvoid_t;
+
+// NB consecutive floats of B read with one LDS instruction, and element n of it.
+template <int NB> struct BVec;
+template <> struct BVec<1> {
+    using type = float;
+    static __device__ __forceinline__ float get(float v, int) { return v; }
+};
+template <> struct BVec<2> {
+    using type = f32x2;
+    static __device__ __forceinline__ float get(f32x2 v, int n) { return v[n]; }
+};
+template <> struct BVec<4> {
+    using type = f32x4;
+    static __device__ __forceinline__ float get(f32x4 v, int n) { return v[n]; }
+};
+
+// XOR swizzle of the 16-byte pieces of one A-tile row in LDS (QA pieces per
+// row): piece q of row r is stored at position q ^ swz(r).  It depends on
+// r mod 16 only.  For the MFMA reads (32 rows, one piece each) any 8
+// consecutive lanes then touch 8 different 16-byte bank groups of a 128-byte
+// line, and any 16 consecutive lanes 16 different groups of a 256-byte line,
+// so the reads are conflict free whether the LDS serves 8 or 16 lanes of a
+// 128-bit read per cycle.
+template <int QA>
+__device__ __forceinline__ int swz(int r) {
+    if constexpr (QA == 8) return (r & 7) ^ ((r >> 3) & 1);
+    else return ((r >> 1) & 3) ^ ((r >> 3) & 1);
+}
 
 template <int BM, int BN, int BK, int WM, int WN>
 struct TileShape {
     static constexpr int NT = 64 * WM * WN;      // threads per workgroup
+    static constexpr int NW = WM * WN;           // waves per workgroup
     static constexpr int TWM = BM / WM;          // wave tile rows
     static constexpr int TWN = BN / WN;          // wave tile columns
     static constexpr int MB = TWM / 32;          // 32x32 blocks per wave, rows
     static constexpr int NB = TWN / 32;          // 32x32 blocks per wave, columns
-    static constexpr int LDA_S = BK + 4;         // A row stride in LDS (floats)
-    static constexpr int LDB_S = BN;             // B row stride in LDS (floats)
-    static constexpr int A_FLOATS = BM * LDA_S;
-    static constexpr int B_FLOATS = BK * LDB_S;
+    static constexpr int A_FLOATS = BM * BK;     // A tile, row-major, swizzled
+    static constexpr int B_FLOATS = BK * BN;     // B tile, row-major
     static constexpr int STAGE = A_FLOATS + B_FLOATS;
     static constexpr int LDS_BYTES = 2 * STAGE * 4;
-    static constexpr int QA = BK / 4;            // float4 per A tile row
-    static constexpr int LA = BM * QA / NT;      // float4 of A per thread per stage
-    static constexpr int QB = BN / 4;            // float4 per B tile row
-    static constexpr int LB = BK * QB / NT;      // float4 of B per thread per stage
+    static constexpr int QA = BK / 4;            // 16-byte pieces per A tile row
+    static constexpr int LA = BM * QA / NT;      // pieces of A per thread per stage
+    static constexpr int QB = BN / 4;            // 16-byte pieces per B tile row
+    static constexpr int LB = BK * QB / NT;      // pieces of B per thread per stage
+    static constexpr int DA = BM * QA / 64 / NW; // direct loads of A per wave per stage
+    static constexpr int DB = BK * QB / 64 / NW; // direct loads of B per wave per stage
     static_assert(BM % WM == 0 && BN % WN == 0, "wave grid must divide the tile");
     static_assert(TWM % 32 == 0 && TWN % 32 == 0, "wave tile is whole 32x32 blocks");
     static_assert(NB == 1 || NB == 2 || NB == 4, "B reads are 1, 2 or 4 floats wide");
-    static_assert(BK % 8 == 0, "BK/2 must be a multiple of 4 (b128 A reads)");
+    static_assert(QA == 4 || QA == 8, "BK is 16 or 32");
     static_assert((BM * QA) % NT == 0 && (BK * QB) % NT == 0, "whole loads per thread");
+    static_assert(DA * 64 * NW == BM * QA && DB * 64 * NW == BK * QB,
+                  "whole direct loads per wave");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS of one CU");
 };
 
@@ -112,56 +155,93 @@ __global__ __launch_bounds__(64 * WM * WN) void sgemm_mfma_kernel(GemmArgs p) {
     const int n0 = tn * BN;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN;
     const int wn = wave % WN;
     const int l32 = lane & 31;
     const int h = lane >> 5;
+    // tile fully inside M and N: every chunk but a partial last one in K is
+    // loaded without bounds checks
+    const bool interior = (m0 + BM <= p.M) && (n0 + BN <= p.N);
 
-    // ---- global -> register staging (one K chunk) ----
-    f32x4 ra[T::LA], rb[T::LB];
-    auto load_stage = [&](int k0) {
+    // ---- register path: global -> registers -> LDS (edges of M, N, K) ----
+    struct Staged {
+        f32x4 a[T::LA], b[T::LB];
+    };
+    auto load_regs = [&](Staged& r, int k0) {
 #pragma unroll
         for (int i = 0; i < T::LA; ++i) {
             const int idx = tid + i * T::NT;
             const int row = idx / T::QA;
-            const int kq = (idx % T::QA) * 4;
+            const int gk = k0 + (idx % T::QA) * 4;
             const int grow = m0 + row;
-            const int gk = k0 + kq;
             const int nvalid = (grow < p.M) ? (p.K - gk) : 0;
             const float* src = p.A + (int64_t)(grow < p.M ? grow : 0) * p.lda + gk;
-            ra[i] = load4<VEC>(src, nvalid);
+            r.a[i] = load4<VEC>(src, nvalid);
         }
 #pragma unroll
         for (int i = 0; i < T::LB; ++i) {
             const int idx = tid + i * T::NT;
-            const int kr = idx / T::QB;
-            const int nq = (idx % T::QB) * 4;
-            const int gk = k0 + kr;
-            const int gn = n0 + nq;
+            const int gk = k0 + idx / T::QB;
+            const int gn = n0 + (idx % T::QB) * 4;
             const int nvalid = (gk < p.K) ? (p.N - gn) : 0;
             const float* src = p.B + (int64_t)(gk < p.K ? gk : 0) * p.ldb + gn;
-            rb[i] = load4<VEC>(src, nvalid);
+            r.b[i] = load4<VEC>(src, nvalid);
         }
     };
-    auto store_stage = [&](int s) {
+    auto store_regs = [&](const Staged& r, int s) {
         float* As = smem + s * T::STAGE;
         float* Bs = As + T::A_FLOATS;
 #pragma unroll
         for (int i = 0; i < T::LA; ++i) {
             const int idx = tid + i * T::NT;
             const int row = idx / T::QA;
-            const int kq = (idx % T::QA) * 4;
-            *reinterpret_cast<f32x4*>(As + row * T::LDA_S + kq) = ra[i];
+            const int q = (idx % T::QA) ^ swz<T::QA>(row);
+            *reinterpret_cast<f32x4*>(As + row * BK + 4 * q) = r.a[i];
         }
 #pragma unroll
         for (int i = 0; i < T::LB; ++i) {
             const int idx = tid + i * T::NT;
-            const int kr = idx / T::QB;
-            const int nq = (idx % T::QB) * 4;
-            *reinterpret_cast<f32x4*>(Bs + kr * T::LDB_S + nq) = rb[i];
+            *reinterpret_cast<f32x4*>(Bs + 4 * idx) = r.b[i];
         }
     };
+
+    // ---- direct path: global -> LDS, interior chunks of aligned operands ----
+    // Wave w's j-th load of A fills the 64 consecutive 16-byte slots
+    // (j*NW + w)*64 .. +63 of the A tile; slot g holds row g / QA, stored
+    // piece g % QA, i.e. logical piece (g % QA) ^ swz(row).  B's slots are
+    // its pieces in row-major order.  Offsets are relative to k0 = 0.
+    int64_t da_off[T::DA], db_off[T::DB];
+#pragma unroll
+    for (int j = 0; j < T::DA; ++j) {
+        const int g = (j * T::NW + wave) * 64 + lane;
+        const int row = g / T::QA;
+        const int q = (g % T::QA) ^ swz<T::QA>(row);
+        da_off[j] = (int64_t)(m0 + row) * p.lda + 4 * q;
+    }
+#pragma unroll
+    for (int j = 0; j < T::DB; ++j) {
+        const int g = (j * T::NW + wave) * 64 + lane;
+        db_off[j] = (int64_t)(g / T::QB) * p.ldb + n0 + 4 * (g % T::QB);
+    }
+    auto load_direct = [&](int k0, int s) {
+        float* As = smem + s * T::STAGE;
+        float* Bs = As + T::A_FLOATS;
+        const float* a = p.A + k0;
+        const float* b = p.B + (int64_t)k0 * p.ldb;
+#pragma unroll
+        for (int j = 0; j < T::DA; ++j)
+            __builtin_amdgcn_global_load_lds((global_cvoid_t*)(a + da_off[j]),
+                                             (lds_void_t*)(As + (j * T::NW + wave) * 256),
+                                             16, 0, 0);
+#pragma unroll
+        for (int j = 0; j < T::DB; ++j)
+            __builtin_amdgcn_global_load_lds((global_cvoid_t*)(b + db_off[j]),
+                                             (lds_void_t*)(Bs + (j * T::NW + wave) * 256),
+                                             16, 0, 0);
+    };
+    // A chunk k0 .. k0+BK-1 goes direct when it is whole and inside the tile.
+    auto direct_ok = [&](int k0) { return VEC && interior && k0 + BK <= p.K; };
 
     f32x16 acc[T::MB][T::NB];
 #pragma unroll
@@ -171,52 +251,90 @@ __global__ __launch_bounds__(64 * WM * WN) void sgemm_mfma_kernel(GemmArgs p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    // Per-lane LDS offsets of the MFMA operands inside one stage.
-    const int a_off = (wm * T::TWM + l32) * T::LDA_S + h * (BK / 2);
-    const int b_off = T::A_FLOATS + h * (BK / 2) * T::LDB_S + wn * T::TWN + T::NB * l32;
+    // Per-lane LDS offsets of the MFMA operands inside one stage.  The A row
+    // of a lane is wm*TWM + i*32 + l32 for block i; its swizzle is that of
+    // l32 (TWM and 32 are multiples of 16).  Chunk c of the stage covers the
+    // k-steps 4c..4c+3, i.e. logical piece h*QA/2 + c of the row.
+    const int a_row = (wm * T::TWM + l32) * BK;
+    int a_piece[T::QA / 2];
+#pragma unroll
+    for (int c = 0; c < T::QA / 2; ++c) a_piece[c] = 4 * ((h * (T::QA / 2) + c) ^ swz<T::QA>(l32));
+    const int b_off = T::A_FLOATS + h * (BK / 2) * BN + wn * T::TWN + T::NB * l32;
 
-    auto compute_stage = [&](int s) {
-        const float* base = smem + s * T::STAGE;
+    // Operand fragments, double-buffered in registers: fa holds the A values
+    // of one chunk of 4 k-steps (one ds_read_b128 per 32-row block), fb the B
+    // values of one k-step (one NB-wide read).  Reads for step kk+1 are issued
+    // before the MFMAs of step kk, so LDS latency hides behind 64-cycle MFMAs.
+    using BV = typename BVec<T::NB>::type;
+    f32x4 fa[2][T::MB];
+    BV fb[2];
+    auto read_a = [&](const float* base, int c, f32x4* dst) {
 #pragma unroll
-        for (int c = 0; c < BK / 8; ++c) {
-            f32x4 a[T::MB];
+        for (int i = 0; i < T::MB; ++i)
+            dst[i] = *reinterpret_cast<const f32x4*>(base + a_row + i * 32 * BK + a_piece[c]);
+    };
+    auto read_b = [&](const float* base, int kk) -> BV {
+        return *reinterpret_cast<const BV*>(base + b_off + kk * BN);
+    };
+    auto mfma_step = [&](const f32x4* a, int j, BV b) {
 #pragma unroll
-            for (int i = 0; i < T::MB; ++i)
-                a[i] = *reinterpret_cast<const f32x4*>(base + a_off + i * 32 * T::LDA_S + 4 * c);
+        for (int i = 0; i < T::MB; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float* bp = base + b_off + (4 * c + j) * T::LDB_S;
-                float b[T::NB];
-                if constexpr (T::NB == 4) {
-                    const f32x4 v = *reinterpret_cast<const f32x4*>(bp);
-                    b[0] = v[0]; b[1] = v[1]; b[2] = v[2]; b[3] = v[3];
-                } else if constexpr (T::NB == 2) {
-                    const f32x2 v = *reinterpret_cast<const f32x2*>(bp);
-                    b[0] = v[0]; b[1] = v[1];
-                } else {
-                    b[0] = bp[0];
-                }
-#pragma unroll
-                for (int i = 0; i < T::MB; ++i)
-#pragma unroll
-                    for (int n = 0; n < T::NB; ++n)
-                        acc[i][n] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][j], b[n],
-                                                                         acc[i][n], 0, 0, 0);
-            }
-        }
+            for (int n = 0; n < T::NB; ++n)
+                acc[i][n] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][j], BVec<T::NB>::get(b, n),
+                                                                 acc[i][n], 0, 0, 0);
     };
 
+    // K loop.  Stage kt lives in LDS buffer kt&1.  During stage kt the loads
+    // of stage kt+1 are issued after the first k-step's reads (into the other
+    // buffer, last read in stage kt-1, before the barrier that ended it):
+    // direct loads land in LDS by themselves; register loads are written to
+    // LDS four k-steps before the end of the stage.  The barrier that ends
+    // stage kt sits before its last k-step's MFMAs, after every read of the
+    // stage has returned and every load of stage kt+1 has landed, so the first
+    // reads of stage kt+1 are issued right after it and overlap those MFMAs.
+    constexpr int KS = BK / 2;         // k-steps per stage (2 k each)
     const int nk = (p.K + BK - 1) / BK;
-    load_stage(0);
-    store_stage(0);
+    if (direct_ok(0)) {
+        load_direct(0, 0);
+    } else {
+        Staged st;
+        load_regs(st, 0);
+        store_regs(st, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);     // all counters: the direct loads have landed
     __syncthreads();
+    read_a(smem, 0, fa[0]);
+    fb[0] = read_b(smem, 0);
     for (int kt = 0; kt < nk; ++kt) {
         const int cur = kt & 1;
+        const float* base = smem + cur * T::STAGE;
+        const float* nbase = smem + (cur ^ 1) * T::STAGE;
+        const int nk0 = (kt + 1) * BK;
         const bool more = kt + 1 < nk;
-        if (more) load_stage((kt + 1) * BK);
-        compute_stage(cur);
-        if (more) store_stage(cur ^ 1);
-        __syncthreads();
+        const bool direct = more && direct_ok(nk0);
+        const bool staged = more && !direct;
+        Staged st;   // register path only; dead outside this iteration
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+            if (kk + 1 < KS) {
+                if ((kk + 1) % 4 == 0) read_a(base, (kk + 1) / 4, fa[((kk + 1) / 4) & 1]);
+                fb[(kk + 1) & 1] = read_b(base, kk + 1);
+            } else if (more) {
+                __builtin_amdgcn_s_waitcnt(0);
+                __syncthreads();
+                read_a(nbase, 0, fa[0]);
+                fb[0] = read_b(nbase, 0);
+            }
+            if (kk == 0) {
+                if (direct) load_direct(nk0, cur ^ 1);
+                if (staged) load_regs(st, nk0);
+            }
+            if (kk == KS - 4 && staged) store_regs(st, cur ^ 1);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_step(fa[(kk / 4) & 1], kk % 4, fb[kk & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
 
     // ---- epilogue: C <- alpha*acc + beta*C (beta == 0: C not read) ----
@@ -287,14 +405,18 @@ hipError_t launch_gemm(const GemmArgs& p, hipStream_t stream) {
 // device pass never sees the host launch functions it points to.
 const KernelEntry* kernel_table(int* count) {
     static const KernelEntry table[] = {
+        PHOBOS_CFG(256, 256, 16, 4, 2),
+        PHOBOS_CFG(256, 256, 32, 4, 2),
+        PHOBOS_CFG(256, 256, 16, 2, 4),
+        PHOBOS_CFG(256, 256, 16, 4, 4),
         PHOBOS_CFG(256, 256, 16, 2, 2),
         PHOBOS_CFG(256, 256, 32, 2, 2),
-        PHOBOS_CFG(256, 256, 16, 4, 2),
+        PHOBOS_CFG(256, 128, 16, 4, 2),
         PHOBOS_CFG(256, 128, 16, 2, 2),
+        PHOBOS_CFG(128, 256, 16, 2, 4),
         PHOBOS_CFG(128, 256, 16, 2, 2),
         PHOBOS_CFG(128, 128, 16, 2, 2),
         PHOBOS_CFG(128, 128, 32, 2, 2),
-        PHOBOS_CFG(128, 128, 8, 2, 2),
         PHOBOS_CFG(128, 64, 16, 2, 1),
         PHOBOS_CFG(64, 128, 16, 1, 2),
         PHOBOS_CFG(64, 64, 16, 1, 1),

@@ -123,7 +123,10 @@ int sgemm_init_leaf(int64_t M, int64_t N, float beta, float* C, int64_t ldc,
  * (1 M, 2 N, 3 K, 4 lda, 5 ldb, 6 ldc, 7 out).
  * sgemm_set_config forces one compiled configuration for every later call in
  * the process (NULL clears the forcing); returns SGEMM_ERR_NO_CONFIG when
- * `cfg` names no compiled configuration.
+ * `cfg` names no compiled configuration.  Order of precedence: a config set
+ * here, then the environment variable SGEMM_FORCE_CFG="BMxBNxBKxWMxWN" (read
+ * once per process; ignored with a message on stderr when malformed or not
+ * compiled), then a tuned config for the exact shape, then the default.
  */
 int sgemm_config_count(void);
 int sgemm_config_at(int32_t index, sgemm_config* out);
