@@ -76,7 +76,7 @@ int env_int(const char* name, int dflt) {
 int default_entry(int64_t M, int64_t N, int64_t K) {
     struct Pick { int bm, bn, bk, wm, wn; };
     static const Pick order[] = {
-        {256, 256, 16, 4, 2}, {256, 128, 16, 4, 2}, {128, 128, 16, 2, 2},
+        {256, 256, 32, 4, 2}, {256, 128, 16, 4, 2}, {128, 128, 16, 2, 2},
         {128, 64, 16, 2, 1},  {64, 64, 16, 1, 1},
     };
     (void)K;
@@ -242,10 +242,10 @@ int sgemm_supertiled(int64_t M, int64_t N, int64_t K, float alpha, const float* 
         for (int64_t pn = 0; pn < gn; ++pn) {
             const int64_t c0 = pn * tn, cols = std::min(tn, N - c0);
             float* Cs = C + r0 * ldc + c0;
-            // init leaf: seed the accumulator (the output's own buffer) with beta*C
+            // init leaf: C itself holds the running sum; it starts as beta*C
             st = launch_init(rows, cols, beta, Cs, ldc, s);
             if (st != SGEMM_OK) return st;
-            // step leaves: add one K chunk each, implicit beta of 1
+            // step leaves: add alpha times one K chunk each, onto C as it stands (beta = 1)
             for (int64_t kt = 0; kt < gk; ++kt) {
                 const int64_t k0 = kt * tk, depth = std::min(tk, K - k0);
                 const float* As = A + r0 * lda + k0;

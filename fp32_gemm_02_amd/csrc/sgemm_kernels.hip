@@ -44,13 +44,16 @@
 
 #include "sgemm_internal.h"
 
+// Upper bound on the LDS ring depth of the GEMM kernel (2 or 3).
+#ifndef PHOBOS_MAX_STAGES
+#define PHOBOS_MAX_STAGES 2
+#endif
+
 namespace phobos {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) const void global_cvoid_t;
 
 // NB consecutive floats of B read with one LDS instruction, and element n of it.
 template <int NB> struct BVec;
@@ -66,6 +69,26 @@ template <> struct BVec<4> {
     using type = f32x4;
     static __device__ __forceinline__ float get(f32x4 v, int n) { return v[n]; }
 };
+
+// One direct global-to-LDS load: every lane fetches the 16 bytes at its `src`
+// and the wave writes them to LDS at lds_dst + 16*lane (lds_dst is the same
+// for the whole wave; it goes in M0).  Issued as inline assembly so that the
+// compiler's wait-count analysis does not see an instruction that touches
+// both memory and LDS: that would make it wait for every outstanding LDS read
+// (lgkmcnt(0)) at each use, where one k-step of lookahead is intended.  The
+// kernel therefore waits for these loads itself (vmcnt) before the barrier
+// that publishes a stage.  Vector-memory loads complete in issue order, so
+// loads the compiler does not track can only make its own waits stricter.
+__device__ __forceinline__ void dma16(const float* src, float* lds_dst) {
+    const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) float*)lds_dst;
+    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0) : "memory");
+}
+
+// s_waitcnt immediate (gfx9 encoding) waiting for at most N outstanding
+// vector-memory loads and for every LDS access; exports are not waited for.
+template <int N>
+constexpr int kWaitVm = (N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8);
+static_assert(kWaitVm<0> == 0x70 && kWaitVm<4> == 0x74, "s_waitcnt encoding");
 
 // XOR swizzle of the 16-byte pieces of one A-tile row in LDS (QA pieces per
 // row): piece q of row r is stored at position q ^ swz(r).  It depends on
@@ -91,7 +114,10 @@ struct TileShape {
     static constexpr int A_FLOATS = BM * BK;     // A tile, row-major, swizzled
     static constexpr int B_FLOATS = BK * BN;     // B tile, row-major
     static constexpr int STAGE = A_FLOATS + B_FLOATS;
-    static constexpr int LDS_BYTES = 2 * STAGE * 4;
+    // LDS ring of NS stages: three when they fit (loads run two stages
+    // ahead of the MFMAs), else two.
+    static constexpr int NS = (3 * STAGE * 4 <= 160 * 1024 && PHOBOS_MAX_STAGES >= 3) ? 3 : 2;
+    static constexpr int LDS_BYTES = NS * STAGE * 4;
     static constexpr int QA = BK / 4;            // 16-byte pieces per A tile row
     static constexpr int LA = BM * QA / NT;      // pieces of A per thread per stage
     static constexpr int QB = BN / 4;            // 16-byte pieces per B tile row
@@ -147,7 +173,7 @@ __device__ __forceinline__ f32x4 load4(const float* src, int nvalid) {
 template <int BM, int BN, int BK, int WM, int WN, bool VEC>
 __global__ __launch_bounds__(64 * WM * WN) void sgemm_mfma_kernel(GemmArgs p) {
     using T = TileShape<BM, BN, BK, WM, WN>;
-    __shared__ __attribute__((aligned(16))) float smem[2 * T::STAGE];
+    __shared__ __attribute__((aligned(16))) float smem[T::NS * T::STAGE];
 
     int tm, tn;
     tile_of(p, tm, tn);
@@ -230,15 +256,9 @@ __global__ __launch_bounds__(64 * WM * WN) void sgemm_mfma_kernel(GemmArgs p) {
         const float* a = p.A + k0;
         const float* b = p.B + (int64_t)k0 * p.ldb;
 #pragma unroll
-        for (int j = 0; j < T::DA; ++j)
-            __builtin_amdgcn_global_load_lds((global_cvoid_t*)(a + da_off[j]),
-                                             (lds_void_t*)(As + (j * T::NW + wave) * 256),
-                                             16, 0, 0);
+        for (int j = 0; j < T::DA; ++j) dma16(a + da_off[j], As + (j * T::NW + wave) * 256);
 #pragma unroll
-        for (int j = 0; j < T::DB; ++j)
-            __builtin_amdgcn_global_load_lds((global_cvoid_t*)(b + db_off[j]),
-                                             (lds_void_t*)(Bs + (j * T::NW + wave) * 256),
-                                             16, 0, 0);
+        for (int j = 0; j < T::DB; ++j) dma16(b + db_off[j], Bs + (j * T::NW + wave) * 256);
     };
     // A chunk k0 .. k0+BK-1 goes direct when it is whole and inside the tile.
     auto direct_ok = [&](int k0) { return VEC && interior && k0 + BK <= p.K; };
@@ -285,35 +305,56 @@ __global__ __launch_bounds__(64 * WM * WN) void sgemm_mfma_kernel(GemmArgs p) {
                                                                  acc[i][n], 0, 0, 0);
     };
 
-    // K loop.  Stage kt lives in LDS buffer kt&1.  During stage kt the loads
-    // of stage kt+1 are issued after the first k-step's reads (into the other
-    // buffer, last read in stage kt-1, before the barrier that ended it):
-    // direct loads land in LDS by themselves; register loads are written to
-    // LDS four k-steps before the end of the stage.  The barrier that ends
-    // stage kt sits before its last k-step's MFMAs, after every read of the
-    // stage has returned and every load of stage kt+1 has landed, so the first
-    // reads of stage kt+1 are issued right after it and overlap those MFMAs.
+    // K loop over a ring of NS LDS buffers; stage kt lives in buffer kt % NS.
+    // During stage kt the loads of stage kt+NS-1 are issued after the first
+    // k-step's reads, into the buffer stage kt-1 used (everyone finished
+    // reading it before the barrier that ended stage kt-1): direct loads land
+    // in LDS by themselves; register loads are written to LDS four k-steps
+    // before the end of the stage.  The barrier that ends stage kt sits before
+    // its last k-step's MFMAs, after every read of the stage has returned and
+    // once the loads of stage kt+1 have landed (those of later stages may
+    // still be in flight), so the first reads of stage kt+1 are issued right
+    // after it and overlap those MFMAs.
     constexpr int KS = BK / 2;         // k-steps per stage (2 k each)
+    constexpr int NS = T::NS;
+    constexpr int DIRECT_LOADS = T::DA + T::DB;   // per wave per stage
     const int nk = (p.K + BK - 1) / BK;
-    if (direct_ok(0)) {
-        load_direct(0, 0);
-    } else {
+    // Wait until at most `pending` direct loads of this wave are in flight and
+    // every LDS access has returned, then meet the other waves.
+    auto wait_and_barrier = [&](bool pending) {
+        if (NS == 3 && pending)
+            __builtin_amdgcn_s_waitcnt(kWaitVm<DIRECT_LOADS>);
+        else
+            __builtin_amdgcn_s_waitcnt(kWaitVm<0>);
+        __syncthreads();
+    };
+    auto issue = [&](int stage, int buf) {       // prologue loads, register path stored at once
+        if (direct_ok(stage * BK)) {
+            load_direct(stage * BK, buf);
+            return true;
+        }
         Staged st;
-        load_regs(st, 0);
-        store_regs(st, 0);
-    }
-    __builtin_amdgcn_s_waitcnt(0);     // all counters: the direct loads have landed
-    __syncthreads();
+        load_regs(st, stage * BK);
+        store_regs(st, buf);
+        return false;
+    };
+    bool pend = false;
+    issue(0, 0);
+    if (NS == 3 && nk > 1) pend = issue(1, 1);
+    wait_and_barrier(pend);
     read_a(smem, 0, fa[0]);
     fb[0] = read_b(smem, 0);
+    int cur = 0;                       // buffer of stage kt
     for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
+        const int nxt = (cur + 1 == NS) ? 0 : cur + 1;
+        const int lbuf = (cur == 0) ? NS - 1 : cur - 1;   // buffer of stage kt+NS-1
         const float* base = smem + cur * T::STAGE;
-        const float* nbase = smem + (cur ^ 1) * T::STAGE;
-        const int nk0 = (kt + 1) * BK;
+        const float* nbase = smem + nxt * T::STAGE;
+        const int lk0 = (kt + NS - 1) * BK;
         const bool more = kt + 1 < nk;
-        const bool direct = more && direct_ok(nk0);
-        const bool staged = more && !direct;
+        const bool load = kt + NS - 1 < nk;
+        const bool direct = load && direct_ok(lk0);
+        const bool staged = load && !direct;
         Staged st;   // register path only; dead outside this iteration
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
@@ -321,20 +362,20 @@ __global__ __launch_bounds__(64 * WM * WN) void sgemm_mfma_kernel(GemmArgs p) {
                 if ((kk + 1) % 4 == 0) read_a(base, (kk + 1) / 4, fa[((kk + 1) / 4) & 1]);
                 fb[(kk + 1) & 1] = read_b(base, kk + 1);
             } else if (more) {
-                __builtin_amdgcn_s_waitcnt(0);
-                __syncthreads();
+                wait_and_barrier(direct);
                 read_a(nbase, 0, fa[0]);
                 fb[0] = read_b(nbase, 0);
             }
             if (kk == 0) {
-                if (direct) load_direct(nk0, cur ^ 1);
-                if (staged) load_regs(st, nk0);
+                if (direct) load_direct(lk0, lbuf);
+                if (staged) load_regs(st, lk0);
             }
-            if (kk == KS - 4 && staged) store_regs(st, cur ^ 1);
+            if (kk == KS - 4 && staged) store_regs(st, lbuf);
             __builtin_amdgcn_sched_barrier(0);
             mfma_step(fa[(kk / 4) & 1], kk % 4, fb[kk & 1]);
             __builtin_amdgcn_sched_barrier(0);
         }
+        cur = nxt;
     }
 
     // ---- epilogue: C <- alpha*acc + beta*C (beta == 0: C not read) ----

@@ -82,8 +82,8 @@ int sgemm(int64_t M, int64_t N, int64_t K, float alpha,
 /*
  * sgemm_supertiled: the same result through the two-level decomposition of
  * the "@cluster" page ("What the cluster compiler accepts": the matmul kernel
- * with a cluster loop, split into an init leaf and a step leaf whose
- * accumulator lives in the output's own buffer) and the conceptual cluster IR
+ * with a cluster loop, split into an init leaf and a step leaf, the running
+ * sum kept in C itself) and the conceptual cluster IR
  * of "Show HN: Phobos", section "The DAG Compiler".
  * For each output super-tile (pm, pn) of TM x TN, in row-major order
  * (pm outer, pn inner, as the runtime deals them out, "@cluster" page,
@@ -91,8 +91,8 @@ int sgemm(int64_t M, int64_t N, int64_t K, float alpha,
  *   one init leaf:  C[pm,pn] <- beta*C[pm,pn]   (0 when beta == 0, C unread)
  *   then for kt = 0 .. ceil(K/TK)-1, one step leaf:
  *                   C[pm,pn] <- alpha*A[pm,kt]*B[kt,pn] + C[pm,pn]
- * i.e. beta is hoisted into the init leaf and every step stores with an
- * implicit beta of 1 ("Show HN: Phobos", section "Clustering").  C holds the
+ * i.e. beta is hoisted into the init leaf and every step adds onto C with
+ * beta = 1 ("Show HN: Phobos", section "Clustering").  C holds the
  * fp32 partial sum between steps.  Stream order makes each super-tile's steps
  * a chain.  Edge super-tiles are clipped to the matrix (the pages' runtime
  * rejects sizes that are not whole multiples; this library accepts them).
@@ -107,7 +107,7 @@ int sgemm_supertiled(int64_t M, int64_t N, int64_t K, float alpha,
  * sgemm_init_leaf: the init leaf on its own, C <- beta*C over an M x N view
  * (C <- 0 without reading C when beta == 0; nothing is enqueued when
  * beta == 1).  "@cluster" page, "What the cluster compiler accepts": the init
- * leaf zeroes the output super-tile or scales it by beta.
+ * leaf prepares the output super-tile (zero, or beta times its old value).
  * Arguments: 1 M, 2 N, 3 beta, 4 C, 5 ldc, 6 stream.
  */
 int sgemm_init_leaf(int64_t M, int64_t N, float beta, float* C, int64_t ldc,
