@@ -1,6 +1,6 @@
 """Benchmark: super-tiled FP32 SGEMM, M = N = K = 16384, 4096^3 super-tiles, 1 GPU.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--tune]
 
 One step is one sgemm_supertiled call through the C ABI: argument checks,
 the row-major walk over the 4 x 4 grid of output super-tiles, and per
@@ -15,9 +15,12 @@ the roofline of the dominant kernel (the step leaf; its duration per launch
 from HIP events the library records on the launch stream during the timed
 region) and the CPU oracle's rate on a bounded slab of the same product.
 
-Options for profiling runs: --copy-calibration runs one plain device copy of
-1 GiB first (a known-size reference for the HBM byte counters);
---skip-cpu-baseline leaves the oracle leg out.
+Other options: --workload runs one of the other seeded workloads of
+sgemm_workloads.py instead (one step = one sgemm call); --tune runs the tile
+tuner on the step shape first (untimed) and times the winner.  For profiling
+runs: --copy-calibration runs one plain device copy of 1 GiB first (a
+known-size reference for the HBM byte counters); --skip-cpu-baseline leaves
+the oracle leg out.
 """
 import argparse
 import hashlib
@@ -32,7 +35,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_FP32_MFMA_TFLOPS = 157.3     # MI355X published dense FP32 matrix peak
 PEAK_HBM_GBS = 8000.0             # MI355X published HBM3E bandwidth
-WORKLOAD = "supertiled_16384_t4096"
+DEFAULT_WORKLOAD = "supertiled_16384_t4096"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sgemm_step_4096_ld16384.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "fp32_gemm_02_amd", "csrc", "sgemm_kernels.hip")]
 
@@ -50,10 +53,10 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
+def measured_traffic(workload):
     """HBM bytes per step-leaf launch from the committed counter summary, if it
-    was taken on the current kernel source; else None."""
-    if not os.path.exists(TRAFFIC_FILE):
+    was taken on the current kernel source for this workload; else None."""
+    if workload != DEFAULT_WORKLOAD or not os.path.exists(TRAFFIC_FILE):
         return None
     text = open(TRAFFIC_FILE).read()
     m_hash = re.search(r"^kernel_source_sha256_16:\s*(\S+)", text, re.M)
@@ -96,6 +99,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--tune", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -110,7 +115,14 @@ def main():
     import fp32_gemm_02_amd as g
     import sgemm_workloads as wl
 
-    w = wl.BY_NAME[WORKLOAD]
+    if args.workload not in wl.BY_NAME:
+        print(f"unknown workload {args.workload!r}; choose from {sorted(wl.BY_NAME)}",
+              file=sys.stderr)
+        sys.exit(2)
+    w = wl.BY_NAME[args.workload]
+    supertiled = w.entry == "sgemm_supertiled"
+    # the GEMM launches of one step: one per super-tile and K chunk, else one
+    step_shape = (w.TM, w.TN, w.TK) if supertiled else (w.M, w.N, w.K)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.Stream(device=dev)
@@ -128,14 +140,25 @@ def main():
     stream.synchronize()
 
     def step():
-        g.sgemm_supertiled(w.M, w.N, w.K, w.alpha, dA, w.lda, dB, w.ldb, w.beta, dC, w.ldc,
-                           w.TM, w.TN, w.TK, stream=stream)
+        if supertiled:
+            g.sgemm_supertiled(w.M, w.N, w.K, w.alpha, dA, w.lda, dB, w.ldb, w.beta, dC,
+                               w.ldc, w.TM, w.TN, w.TK, stream=stream)
+        else:
+            g.sgemm(w.M, w.N, w.K, w.alpha, dA, w.lda, dB, w.ldb, w.beta, dC, w.ldc,
+                    stream=stream)
+
+    tuned = None
+    if args.tune:
+        tuned, _ = g.sgemm_tune(*step_shape, w.lda, w.ldb, w.ldc, reps=10, stream=stream)
 
     for _ in range(args.warmup):
         step()
     stream.synchronize()
 
-    launches_per_step = (w.M // w.TM) * (w.N // w.TN) * (w.K // w.TK)
+    if supertiled:
+        launches_per_step = (-(-w.M // w.TM)) * (-(-w.N // w.TN)) * (-(-w.K // w.TK))
+    else:
+        launches_per_step = 1
     g.sgemm_trace_begin(args.steps * launches_per_step * 2 + 16)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -155,9 +178,9 @@ def main():
 
     step_ms = [t for t, k in zip(ms_kern, kinds) if k == g.SGEMM_KIND_GEMM]
     avg_launch_ms = float(np.mean(step_ms))
-    step_flops = 2.0 * w.TM * w.TN * w.TK
+    step_flops = 2.0 * step_shape[0] * step_shape[1] * step_shape[2]
     achieved_tflops = step_flops / (avg_launch_ms * 1e-3) / 1e12
-    traffic = measured_traffic()
+    traffic = measured_traffic(args.workload)
 
     out = {
         "metric": "SGEMM GFLOP/s and % of MI355X FP32 matrix peak at 16384^3, 1 GPU",
@@ -172,11 +195,14 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": WORKLOAD, "entry": "sgemm_supertiled", "M": w.M, "N": w.N,
-                   "K": w.K, "TM": w.TM, "TN": w.TN, "TK": w.TK, "alpha": w.alpha,
-                   "beta": w.beta, "inputs": "uniform[-1,1) seed 2",
-                   "step_leaf_config": "bm=%d bn=%d bk=%d wm=%d wn=%d" %
-                   g.sgemm_get_config(w.TM, w.TN, w.TK, w.lda, w.ldb, w.ldc).as_tuple(),
+        "config": {"workload": w.name, "entry": w.entry, "M": w.M, "N": w.N, "K": w.K,
+                   "lda": w.lda, "ldb": w.ldb, "ldc": w.ldc,
+                   **({"TM": w.TM, "TN": w.TN, "TK": w.TK} if supertiled else {}),
+                   "alpha": w.alpha, "beta": w.beta,
+                   "inputs": "A/B/C %s/%s/%s, seed %d" % (*w.dists, w.seed),
+                   "leaf_config": "bm=%d bn=%d bk=%d wm=%d wn=%d" %
+                   g.sgemm_get_config(*step_shape, w.lda, w.ldb, w.ldc).as_tuple(),
+                   "tuned": tuned is not None,
                    "launches_per_step": launches_per_step,
                    "pct_of_fp32_matrix_peak": round(100.0 * value / 1e3 / PEAK_FP32_MFMA_TFLOPS, 2)},
         "roofline": {"bound": "mfma", "achieved": round(achieved_tflops, 2),
@@ -186,6 +212,8 @@ def main():
     }
     if not args.skip_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x, w)
+    if tuned is not None:
+        g.sgemm_set_config(None)
     print(f"# timed {args.steps} steps: {ms_total:.2f} ms on the stream ({wall * 1e3:.2f} ms "
           f"wall); {len(step_ms)} step-leaf launches traced, mean {avg_launch_ms:.4f} ms",
           file=sys.stderr, flush=True)
