@@ -44,6 +44,14 @@
 
 #include "sgemm_internal.h"
 
+// The direct global-to-LDS loads of a stage are issued spread over its first
+// PHOBOS_DMA_SPREAD k-steps when a stage has 16 k-steps or more (BK = 32), and
+// all at the first k-step otherwise (a BK = 16 stage has too few k-steps left
+// before its barrier for the last loads to land).
+#ifndef PHOBOS_DMA_SPREAD
+#define PHOBOS_DMA_SPREAD 4
+#endif
+
 // Upper bound on the LDS ring depth of the GEMM kernel (2 or 3).
 #ifndef PHOBOS_MAX_STAGES
 #define PHOBOS_MAX_STAGES 2
@@ -250,15 +258,19 @@ __global__ __launch_bounds__(64 * WM * WN) void sgemm_mfma_kernel(GemmArgs p) {
         const int g = (j * T::NW + wave) * 64 + lane;
         db_off[j] = (int64_t)(g / T::QB) * p.ldb + n0 + 4 * (g % T::QB);
     }
-    auto load_direct = [&](int k0, int s) {
+    // Direct load number j (0 .. DA+DB-1) of the chunk at k0 into buffer s.
+    auto load_direct_one = [&](int k0, int s, int j) {
         float* As = smem + s * T::STAGE;
         float* Bs = As + T::A_FLOATS;
-        const float* a = p.A + k0;
-        const float* b = p.B + (int64_t)k0 * p.ldb;
+        if (j < T::DA)
+            dma16(p.A + k0 + da_off[j], As + (j * T::NW + wave) * 256);
+        else
+            dma16(p.B + (int64_t)k0 * p.ldb + db_off[j - T::DA],
+                  Bs + ((j - T::DA) * T::NW + wave) * 256);
+    };
+    auto load_direct = [&](int k0, int s) {
 #pragma unroll
-        for (int j = 0; j < T::DA; ++j) dma16(a + da_off[j], As + (j * T::NW + wave) * 256);
-#pragma unroll
-        for (int j = 0; j < T::DB; ++j) dma16(b + db_off[j], Bs + (j * T::NW + wave) * 256);
+        for (int j = 0; j < T::DA + T::DB; ++j) load_direct_one(k0, s, j);
     };
     // A chunk k0 .. k0+BK-1 goes direct when it is whole and inside the tile.
     auto direct_ok = [&](int k0) { return VEC && interior && k0 + BK <= p.K; };
@@ -318,6 +330,9 @@ __global__ __launch_bounds__(64 * WM * WN) void sgemm_mfma_kernel(GemmArgs p) {
     constexpr int KS = BK / 2;         // k-steps per stage (2 k each)
     constexpr int NS = T::NS;
     constexpr int DIRECT_LOADS = T::DA + T::DB;   // per wave per stage
+    constexpr int DMA_STEPS = (KS >= 16) ? PHOBOS_DMA_SPREAD : 1;
+    constexpr int DMA_PER_STEP = (DIRECT_LOADS + DMA_STEPS - 1) / DMA_STEPS;
+    static_assert(DMA_STEPS >= 1 && DMA_STEPS <= KS - 4, "loads land well before the barrier");
     const int nk = (p.K + BK - 1) / BK;
     // Wait until at most `pending` direct loads of this wave are in flight and
     // every LDS access has returned, then meet the other waves.
@@ -366,10 +381,12 @@ __global__ __launch_bounds__(64 * WM * WN) void sgemm_mfma_kernel(GemmArgs p) {
                 read_a(nbase, 0, fa[0]);
                 fb[0] = read_b(nbase, 0);
             }
-            if (kk == 0) {
-                if (direct) load_direct(lk0, lbuf);
-                if (staged) load_regs(st, lk0);
+            if (direct) {
+#pragma unroll
+                for (int j = kk * DMA_PER_STEP; j < (kk + 1) * DMA_PER_STEP; ++j)
+                    if (j < DIRECT_LOADS) load_direct_one(lk0, lbuf, j);
             }
+            if (kk == 0 && staged) load_regs(st, lk0);
             if (kk == KS - 4 && staged) store_regs(st, lbuf);
             __builtin_amdgcn_sched_barrier(0);
             mfma_step(fa[(kk / 4) & 1], kk % 4, fb[kk & 1]);
