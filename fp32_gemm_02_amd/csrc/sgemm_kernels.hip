@@ -194,9 +194,6 @@ __global__ __launch_bounds__(64 * WM * WN) void sgemm_mfma_kernel(GemmArgs p) {
     const int wn = wave % WN;
     const int l32 = lane & 31;
     const int h = lane >> 5;
-    // tile fully inside M and N: every chunk but a partial last one in K is
-    // loaded without bounds checks
-    const bool interior = (m0 + BM <= p.M) && (n0 + BN <= p.N);
 
     // ---- register path: global -> registers -> LDS (edges of M, N, K) ----
     struct Staged {
@@ -240,23 +237,32 @@ __global__ __launch_bounds__(64 * WM * WN) void sgemm_mfma_kernel(GemmArgs p) {
         }
     };
 
-    // ---- direct path: global -> LDS, interior chunks of aligned operands ----
+    // ---- direct path: global -> LDS, whole K chunks of aligned operands ----
     // Wave w's j-th load of A fills the 64 consecutive 16-byte slots
     // (j*NW + w)*64 .. +63 of the A tile; slot g holds row g / QA, stored
     // piece g % QA, i.e. logical piece (g % QA) ^ swz(row).  B's slots are
     // its pieces in row-major order.  Offsets are relative to k0 = 0.
+    // Tiles at the M or N edge load too: a row of A past M reads row M-1 and
+    // a piece of B wholly past N reads the tile's first piece instead; both
+    // only feed rows or columns of C that are never stored.  A piece of B
+    // that straddles N reads the pad floats after column N-1 of the same row
+    // (ldb is a multiple of 4 here, so they lie before the next row); for the
+    // last row of B that could pass the end of the buffer, so a chunk that
+    // holds row K-1 of an N-edge tile takes the register path.
     int64_t da_off[T::DA], db_off[T::DB];
 #pragma unroll
     for (int j = 0; j < T::DA; ++j) {
         const int g = (j * T::NW + wave) * 64 + lane;
         const int row = g / T::QA;
         const int q = (g % T::QA) ^ swz<T::QA>(row);
-        da_off[j] = (int64_t)(m0 + row) * p.lda + 4 * q;
+        const int grow = min(m0 + row, p.M - 1);
+        da_off[j] = (int64_t)grow * p.lda + 4 * q;
     }
 #pragma unroll
     for (int j = 0; j < T::DB; ++j) {
         const int g = (j * T::NW + wave) * 64 + lane;
-        db_off[j] = (int64_t)(g / T::QB) * p.ldb + n0 + 4 * (g % T::QB);
+        const int gn = n0 + 4 * (g % T::QB);
+        db_off[j] = (int64_t)(g / T::QB) * p.ldb + (gn < p.N ? gn : n0);
     }
     // Direct load number j (0 .. DA+DB-1) of the chunk at k0 into buffer s.
     auto load_direct_one = [&](int k0, int s, int j) {
@@ -272,8 +278,12 @@ __global__ __launch_bounds__(64 * WM * WN) void sgemm_mfma_kernel(GemmArgs p) {
 #pragma unroll
         for (int j = 0; j < T::DA + T::DB; ++j) load_direct_one(k0, s, j);
     };
-    // A chunk k0 .. k0+BK-1 goes direct when it is whole and inside the tile.
-    auto direct_ok = [&](int k0) { return VEC && interior && k0 + BK <= p.K; };
+    // The chunk k0 .. k0+BK-1 goes direct when it lies wholly inside K, and,
+    // for a tile at the N edge, does not hold the last row of B.
+    const bool n_inside = n0 + BN <= p.N;
+    auto direct_ok = [&](int k0) {
+        return VEC && (n_inside ? k0 + BK <= p.K : k0 + BK < p.K);
+    };
 
     f32x16 acc[T::MB][T::NB];
 #pragma unroll

@@ -62,8 +62,12 @@ def _all_cfgs():
 @pytest.mark.parametrize("cfg", _all_cfgs(), ids=_cfg_id)
 def test_tile_edges_every_config(cfg):
     bm, bn, bk = cfg.bm, cfg.bn, cfg.bk
+    # even positions use 16-byte aligned leading dimensions (direct LDS loads,
+    # also on edge tiles), odd ones odd leading dimensions (scalar loads); the
+    # last shape has K a whole number of chunks, so an N-edge tile's last chunk
+    # holds the last row of B
     shapes = [(1, bn + 1, 1), (bm + 1, bn - 1, bk + 1), (2 * bm + 3, 2 * bn + 5, 3 * bk + 5),
-              (bm - 1, 1, 2), (bm, bn, bk), (3, 7, 2 * bk - 1)]
+              (bm - 1, 1, 2), (bm, bn, bk), (3, 7, 2 * bk - 1), (bm + 7, 2 * bn + 3, 4 * bk)]
     with _forced(cfg):
         for i, (M, N, K) in enumerate(shapes):
             vec = i % 2 == 0
