@@ -217,3 +217,84 @@ def test_tuner_records_a_winner_that_is_correct():
     w = wl.custom(M, N, K, -1.0, 2.0, seed=41)
     x = wl.make_inputs(w)
     gu.check_full(w, x, gu.run(w, x))
+
+
+# ---------------------------------------------------------------------------
+# IEEE special values inside the logical A and B (not the pads)
+@pytest.mark.parametrize("special", [np.nan, np.inf])
+def test_special_values_reach_exactly_their_row_and_column(special):
+    M, N, K = 300, 260, 96
+    w = wl.custom(M, N, K, 1.0, 0.5, ("I7", "I7", "I7"), seed=61, lda=K + 4, ldb=N + 4,
+                  ldc=N + 4)
+    x = wl.make_inputs(w)
+    A = x.logical("A")
+    B = x.logical("B")
+    A[:, :] = np.abs(A) + 1          # positive entries: an Inf cannot cancel to NaN
+    B[:, :] = np.abs(B) + 1
+    r, c = 137, 201
+    A[r, 5] = special                # poisons row r of C
+    B[7, c] = special                # poisons column c of C
+    out = gu.logical_c(w, gu.run(w, x))
+    bad = ~np.isfinite(out)
+    want_bad = np.zeros_like(bad)
+    want_bad[r, :] = True
+    want_bad[:, c] = True
+    assert np.array_equal(bad, want_bad)
+    if special == np.inf:
+        assert np.all(out[r, :] == np.inf) and np.all(out[:, c] == np.inf)
+    # everything else is the exact integer result
+    A2, B2 = A.copy(), B.copy()
+    A2[r, 5] = 0
+    B2[7, c] = 0
+    ok = ~want_bad
+    ref = (A2.astype(np.int64) @ B2.astype(np.int64) + 0.5 * x.logical("C").astype(np.float64))
+    assert np.array_equal(out[ok], ref.astype(np.float32)[ok])
+
+
+def test_alpha_zero_never_reads_a_or_b():
+    w = wl.custom(90, 70, 40, 0.0, 1.5, ("NaN", "NaN", "U"), seed=62)
+    x = wl.make_inputs(w)
+    out = gu.run(w, x)
+    want = (np.float32(1.5) * x.logical("C")).astype(np.float32)
+    assert np.array_equal(gu.logical_c(w, out).view(np.int32), want.view(np.int32))
+
+
+def test_concurrent_calls_on_two_streams():
+    """Two products on two streams at once: each matches its own oracle."""
+    ws = [wl.custom(700, 650, 500, 1.0, -1.0, seed=71, lda=504, ldb=652, ldc=656),
+          wl.custom(520, 900, 300, -0.5, 2.0, seed=72, entry="sgemm_supertiled", TM=256,
+                    TN=384, TK=128)]
+    xs = [wl.make_inputs(w) for w in ws]
+    devs = [(gu.to_dev(x.A), gu.to_dev(x.B), gu.to_dev(x.C)) for x in xs]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    for _ in range(3):   # repeated, interleaved enqueues: C accumulates alpha*A*B + beta*C
+        for w, (dA, dB, dC), s in zip(ws, devs, streams):
+            if w.entry == "sgemm":
+                g.sgemm(w.M, w.N, w.K, w.alpha, dA, w.lda, dB, w.ldb, w.beta, dC, w.ldc, stream=s)
+            else:
+                g.sgemm_supertiled(w.M, w.N, w.K, w.alpha, dA, w.lda, dB, w.ldb, w.beta, dC,
+                                   w.ldc, w.TM, w.TN, w.TK, stream=s)
+    torch.cuda.synchronize()
+    for w, x, (dA, dB, dC) in zip(ws, xs, devs):
+        # the same three calls, one at a time on the default stream, from the same inputs
+        dC2 = gu.to_dev(x.C)
+        for _ in range(3):
+            if w.entry == "sgemm":
+                g.sgemm(w.M, w.N, w.K, w.alpha, dA, w.lda, dB, w.ldb, w.beta, dC2, w.ldc)
+            else:
+                g.sgemm_supertiled(w.M, w.N, w.K, w.alpha, dA, w.lda, dB, w.ldb, w.beta, dC2,
+                                   w.ldc, w.TM, w.TN, w.TK)
+        torch.cuda.synchronize()
+        # same kernels, same order per stream: bit-identical
+        assert torch.equal(dC.view(torch.int32), dC2.view(torch.int32))
+        # and the first call alone agrees with the oracle
+        dC3 = gu.to_dev(x.C)
+        if w.entry == "sgemm":
+            g.sgemm(w.M, w.N, w.K, w.alpha, dA, w.lda, dB, w.ldb, w.beta, dC3, w.ldc)
+        else:
+            g.sgemm_supertiled(w.M, w.N, w.K, w.alpha, dA, w.lda, dB, w.ldb, w.beta, dC3,
+                               w.ldc, w.TM, w.TN, w.TK)
+        torch.cuda.synchronize()
+        steps = 1 if w.entry == "sgemm" else -(-w.K // w.TK)
+        gu.check_full(w, x, dC3.cpu().numpy(), steps=steps, relaxed=True)
