@@ -17,7 +17,11 @@ region) and the CPU oracle's rate on a bounded slab of the same product.
 
 Other options: --workload runs one of the other seeded workloads of
 sgemm_workloads.py instead (one step = one sgemm call); --tune runs the tile
-tuner on the step shape first (untimed) and times the winner.  For profiling
+tuner on the step shape first (untimed) and times the winner;
+--host-resident MIB keeps A, B and C in pinned host memory and times
+sgemm_supertiled_host with the planner's plan for a device budget of MIB MiB
+(a rate that includes every host<->device transfer; the workload's own
+super-tile extents are replaced by the plan's).  For profiling
 runs: --copy-calibration runs one plain device copy of 1 GiB first (a
 known-size reference for the HBM byte counters); --skip-cpu-baseline leaves
 the oracle leg out.
@@ -101,6 +105,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--tune", action="store_true")
+    ap.add_argument("--host-resident", type=int, default=None, metavar="MIB")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -121,17 +126,31 @@ def main():
         sys.exit(2)
     w = wl.BY_NAME[args.workload]
     supertiled = w.entry == "sgemm_supertiled"
+    host = args.host_resident is not None
+    plan = None
+    if host:
+        if not supertiled:
+            print("--host-resident needs a super-tiled workload", file=sys.stderr)
+            sys.exit(2)
+        plan = g.sgemm_plan_supertiles(w.M, w.N, w.K, w.beta, args.host_resident << 20)
+        tiles = (min(plan.TM, w.M), min(plan.TN, w.N), min(plan.TK, w.K))
+    else:
+        tiles = (w.TM, w.TN, w.TK) if supertiled else None
     # the GEMM launches of one step: one per super-tile and K chunk, else one
-    step_shape = (w.TM, w.TN, w.TK) if supertiled else (w.M, w.N, w.K)
+    step_shape = tiles if supertiled else (w.M, w.N, w.K)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.Stream(device=dev)
 
     x = wl.make_inputs(w)
     with torch.cuda.stream(stream):
-        dA = torch.from_numpy(x.A).to(dev, non_blocking=False)
-        dB = torch.from_numpy(x.B).to(dev, non_blocking=False)
-        dC = torch.from_numpy(x.C).to(dev, non_blocking=False)
+        if host:
+            # pinned host buffers (freshly allocated, then filled)
+            dA, dB, dC = (torch.from_numpy(a).pin_memory() for a in (x.A, x.B, x.C))
+        else:
+            dA = torch.from_numpy(x.A).to(dev, non_blocking=False)
+            dB = torch.from_numpy(x.B).to(dev, non_blocking=False)
+            dC = torch.from_numpy(x.C).to(dev, non_blocking=False)
         if args.copy_calibration:
             src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
             dst = torch.empty_like(src)
@@ -140,7 +159,10 @@ def main():
     stream.synchronize()
 
     def step():
-        if supertiled:
+        if host:
+            g.sgemm_supertiled_host(w.M, w.N, w.K, w.alpha, dA, w.lda, dB, w.ldb, w.beta, dC,
+                                    w.ldc, plan, stream=stream)
+        elif supertiled:
             g.sgemm_supertiled(w.M, w.N, w.K, w.alpha, dA, w.lda, dB, w.ldb, w.beta, dC,
                                w.ldc, w.TM, w.TN, w.TK, stream=stream)
         else:
@@ -156,7 +178,7 @@ def main():
     stream.synchronize()
 
     if supertiled:
-        launches_per_step = (-(-w.M // w.TM)) * (-(-w.N // w.TN)) * (-(-w.K // w.TK))
+        launches_per_step = (-(-w.M // tiles[0])) * (-(-w.N // tiles[1])) * (-(-w.K // tiles[2]))
     else:
         launches_per_step = 1
     g.sgemm_trace_begin(args.steps * launches_per_step * 2 + 16)
@@ -180,7 +202,7 @@ def main():
     avg_launch_ms = float(np.mean(step_ms))
     step_flops = 2.0 * step_shape[0] * step_shape[1] * step_shape[2]
     achieved_tflops = step_flops / (avg_launch_ms * 1e-3) / 1e12
-    traffic = measured_traffic(args.workload)
+    traffic = None if host else measured_traffic(args.workload)
 
     out = {
         "metric": "SGEMM GFLOP/s and % of MI355X FP32 matrix peak at 16384^3, 1 GPU",
@@ -195,9 +217,17 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": w.name, "entry": w.entry, "M": w.M, "N": w.N, "K": w.K,
+        "config": {"workload": w.name + ("_host_resident" if host else ""),
+                   "entry": "sgemm_supertiled_host" if host else w.entry,
+                   "M": w.M, "N": w.N, "K": w.K,
                    "lda": w.lda, "ldb": w.ldb, "ldc": w.ldc,
-                   **({"TM": w.TM, "TN": w.TN, "TK": w.TK} if supertiled else {}),
+                   **(dict(zip(("TM", "TN", "TK"), tiles)) if supertiled else {}),
+                   **({"device_budget_mib": args.host_resident,
+                       "slots_a_b_c": [plan.a_slots, plan.b_slots, plan.c_slots],
+                       "planned_transfer_bytes": plan.transfer_bytes,
+                       "modeled_ms": round(plan.modeled_ms, 3),
+                       "inputs_in": "pinned host memory (rate includes all transfers)"}
+                      if host else {}),
                    "alpha": w.alpha, "beta": w.beta,
                    "inputs": "A/B/C %s/%s/%s, seed %d" % (*w.dists, w.seed),
                    "leaf_config": "bm=%d bn=%d bk=%d wm=%d wn=%d" %

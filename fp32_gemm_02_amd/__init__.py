@@ -22,6 +22,7 @@ SGEMM_OK = 0
 SGEMM_ERR_NO_CONFIG = 2
 SGEMM_ERR_TOO_LARGE = 3
 SGEMM_ERR_ALLOC = 4
+SGEMM_ERR_BUDGET = 5
 SGEMM_ERR_HIP_BASE = 1000
 SGEMM_KIND_GEMM = 0
 SGEMM_KIND_INIT_LEAF = 1
@@ -44,6 +45,23 @@ class sgemm_config(ctypes.Structure):
         return "sgemm_config(bm=%d, bn=%d, bk=%d, wm=%d, wn=%d)" % self.as_tuple()
 
 
+class sgemm_plan_model(ctypes.Structure):
+    _fields_ = [("gemm_tflops", ctypes.c_double), ("link_gbs", ctypes.c_double)]
+
+
+class sgemm_plan(ctypes.Structure):
+    _fields_ = [("TM", ctypes.c_int64), ("TN", ctypes.c_int64), ("TK", ctypes.c_int64),
+                ("a_slots", ctypes.c_int32), ("b_slots", ctypes.c_int32),
+                ("c_slots", ctypes.c_int32), ("device_bytes", ctypes.c_int64),
+                ("transfer_bytes", ctypes.c_double), ("modeled_ms", ctypes.c_double)]
+
+    def __repr__(self):
+        return ("sgemm_plan(TM=%d, TN=%d, TK=%d, slots a/b/c=%d/%d/%d, device_bytes=%d, "
+                "transfer_bytes=%.4g, modeled_ms=%.4g)" % (
+                    self.TM, self.TN, self.TK, self.a_slots, self.b_slots, self.c_slots,
+                    self.device_bytes, self.transfer_bytes, self.modeled_ms))
+
+
 _lib = None
 
 _i64, _f32, _i32, _vp = ctypes.c_int64, ctypes.c_float, ctypes.c_int32, ctypes.c_void_p
@@ -61,6 +79,10 @@ _SIGNATURES = {
                               ctypes.c_int),
     "sgemm_tune": ([_i64, _i64, _i64, _i64, _i64, _i64, _i32, _vp,
                     ctypes.POINTER(sgemm_config), ctypes.POINTER(_f32)], ctypes.c_int),
+    "sgemm_plan_supertiles": ([_i64, _i64, _i64, _f32, _i64, ctypes.POINTER(sgemm_plan_model),
+                               ctypes.POINTER(sgemm_plan)], ctypes.c_int),
+    "sgemm_supertiled_host": ([_i64, _i64, _i64, _f32, _vp, _i64, _vp, _i64, _f32, _vp, _i64,
+                               ctypes.POINTER(sgemm_plan), _vp], ctypes.c_int),
     "sgemm_trace_begin": ([_i64], ctypes.c_int),
     "sgemm_trace_end": ([ctypes.POINTER(_f32), ctypes.POINTER(_i32), _i64,
                          ctypes.POINTER(_i64)], ctypes.c_int),
@@ -183,6 +205,41 @@ def sgemm_tune(M, N, K, lda, ldb, ldc, reps=20, stream=None):
     _check(lib().sgemm_tune(M, N, K, lda, ldb, ldc, reps, _stream(stream), ctypes.byref(c),
                             ctypes.byref(ms)), "sgemm_tune")
     return c, ms.value
+
+
+def sgemm_plan_supertiles(M, N, K, beta, device_bytes, gemm_tflops=None, link_gbs=None):
+    """Super-tile extents and device slots for the host-resident product (host only)."""
+    model = None
+    if gemm_tflops is not None or link_gbs is not None:
+        model = ctypes.byref(sgemm_plan_model(gemm_tflops or 140.0, link_gbs or 50.0))
+    plan = sgemm_plan()
+    _check(lib().sgemm_plan_supertiles(M, N, K, beta, device_bytes, model, ctypes.byref(plan)),
+           "sgemm_plan_supertiles")
+    return plan
+
+
+def _host_ptr(x):
+    """Address of a host buffer (numpy array, CPU tensor or integer)."""
+    if x is None:
+        return None
+    if hasattr(x, "ctypes"):
+        return x.ctypes.data
+    if hasattr(x, "data_ptr"):
+        return x.data_ptr()
+    return int(x)
+
+
+def sgemm_supertiled_host_raw(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, plan, stream=None):
+    return lib().sgemm_supertiled_host(M, N, K, alpha, _host_ptr(A), lda, _host_ptr(B), ldb,
+                                       beta, _host_ptr(C), ldc,
+                                       None if plan is None else ctypes.byref(plan),
+                                       _stream(stream))
+
+
+def sgemm_supertiled_host(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, plan, stream=None):
+    """C <- alpha*A*B + beta*C with A, B, C in host memory; synchronous."""
+    _check(sgemm_supertiled_host_raw(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, plan, stream),
+           "sgemm_supertiled_host")
 
 
 def sgemm_trace_begin(capacity):

@@ -213,6 +213,22 @@ int check_gemm_args(int64_t M, int64_t N, int64_t K, float alpha, const float* A
 
 }  // namespace
 
+namespace phobos {
+// Launches for the host-resident executor (sgemm_host.cpp): arguments are
+// already checked there.
+int host_launch_gemm(int64_t M, int64_t N, int64_t K, float alpha, const float* A,
+                     int64_t lda, const float* B, int64_t ldb, float beta, float* C,
+                     int64_t ldc, hipStream_t stream) {
+    const int entry = choose_entry(M, N, K, lda, ldb, ldc);
+    if (entry < 0) return SGEMM_ERR_NO_CONFIG;
+    return launch_gemm(entry, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+}
+int host_launch_init(int64_t M, int64_t N, float beta, float* C, int64_t ldc,
+                     hipStream_t stream) {
+    return launch_init(M, N, beta, C, ldc, stream);
+}
+}  // namespace phobos
+
 extern "C" {
 
 int sgemm(int64_t M, int64_t N, int64_t K, float alpha, const float* A, int64_t lda,
@@ -356,14 +372,13 @@ int sgemm_tune(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_
 
     float *A = nullptr, *B = nullptr, *C = nullptr;
     const int64_t na = (M - 1) * lda + K, nb = (K - 1) * ldb + N, ncm = (M - 1) * ldc + N;
-    if (hipMalloc(&A, na * sizeof(float)) != hipSuccess) return SGEMM_ERR_ALLOC;
-    if (hipMalloc(&B, nb * sizeof(float)) != hipSuccess) {
-        (void)hipFree(A);
-        return SGEMM_ERR_ALLOC;
-    }
-    if (hipMalloc(&C, ncm * sizeof(float)) != hipSuccess) {
+    if (hipMalloc(&A, na * sizeof(float)) != hipSuccess ||
+        hipMalloc(&B, nb * sizeof(float)) != hipSuccess ||
+        hipMalloc(&C, ncm * sizeof(float)) != hipSuccess) {
+        (void)hipGetLastError();   // a failed allocation must not fail later launches
         (void)hipFree(A);
         (void)hipFree(B);
+        (void)hipFree(C);
         return SGEMM_ERR_ALLOC;
     }
     int st = SGEMM_OK;
@@ -482,7 +497,8 @@ const char* sgemm_status_string(int status) {
     switch (status) {
         case SGEMM_ERR_NO_CONFIG: return "no compiled kernel configuration matches";
         case SGEMM_ERR_TOO_LARGE: return "a dimension exceeds 2^30 or the grid 2^32-1 work-items";
-        case SGEMM_ERR_ALLOC: return "could not allocate tuner scratch memory";
+        case SGEMM_ERR_ALLOC: return "a device allocation failed";
+        case SGEMM_ERR_BUDGET: return "no plan fits the device memory budget";
         default: break;
     }
     if (status >= SGEMM_ERR_HIP_BASE) return hipGetErrorString((hipError_t)(status - SGEMM_ERR_HIP_BASE));

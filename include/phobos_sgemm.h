@@ -53,7 +53,8 @@ extern "C" {
 #define SGEMM_ERR_NO_CONFIG 2      /* no compiled kernel matches the request   */
 #define SGEMM_ERR_TOO_LARGE 3      /* a dimension exceeds 2^30, or the launch   */
                                    /* grid exceeds 2^32-1 work-items           */
-#define SGEMM_ERR_ALLOC 4          /* sgemm_tune could not allocate scratch    */
+#define SGEMM_ERR_ALLOC 4          /* a device allocation failed               */
+#define SGEMM_ERR_BUDGET 5         /* no plan fits the device memory budget    */
 #define SGEMM_ERR_HIP_BASE 1000    /* 1000 + hipError_t                        */
 
 /*
@@ -158,6 +159,74 @@ int sgemm_tune_candidates(int64_t M, int64_t N, int64_t K, sgemm_config* out,
                           int32_t cap);
 int sgemm_tune(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
                int32_t reps, void* stream, sgemm_config* winner, float* winner_ms);
+
+/*
+ * Host-resident super-tiled SGEMM, the single-GPU form of the pages' cluster
+ * runtime ("@cluster" page, "What runs today": per node, allocate tile
+ * buffers, load super-tiles, compute the init and step leaves as their inputs
+ * arrive, store the outputs, free the buffers; "Show HN: Phobos", section
+ * "The DAG Compiler": a super-tile is the unit that moves, and the next
+ * block's loads are issued while the current one computes).  For products
+ * whose operands live in host memory, e.g. larger than the GPU.
+ *
+ * sgemm_plan_supertiles chooses super-tile extents and device tile slots the
+ * way the pages' cluster tuner plans ("@cluster" page, "What runs today",
+ * Tuning): every candidate TM x TN x TK (powers of two from 256 below each
+ * dimension, and the dimension itself) with A slots in {2, ceil(K/TK)} (the
+ * latter keeps a row of A super-tiles resident across the row of outputs)
+ * and B slots in {2, all of B}, and two C slots, is dropped if its device
+ * buffers exceed `device_bytes`, and the rest are ranked by a model of
+ * max(compute, loads, stores) time plus the first loads and last store, built
+ * from `model` (NULL: 140 TFLOP/s GEMM rate, 50 GB/s each way host<->device;
+ * loads and stores overlap).  Compute time
+ * counts the rate scaled by how full a step launch keeps the 256 CUs
+ * (ceil(TM/256)*ceil(TN/256) workgroups in waves of 256), 15 us per launch
+ * and each launch's read and write of its C super-tile at 5 TB/s.  Nothing is
+ * run.  Host-only.  Arguments: 1 M, 2 N, 3 K, 4 beta (0: C is only written),
+ * 5 device_bytes, 6 model, 7 out.  SGEMM_ERR_BUDGET if nothing fits.
+ *
+ * sgemm_supertiled_host computes C <- alpha*A*B + beta*C with A, B and C in
+ * host memory (row-major, leading dimensions as for sgemm; pinned memory,
+ * e.g. hipHostMalloc'ed, gives full link speed) using `plan`.  It allocates
+ * the plan's device slots, walks the super-tiles in row-major order: per
+ * output super-tile load C (unless beta == 0), run the init leaf and the K
+ * step leaves (the same kernels as sgemm_supertiled, so the result is bit for
+ * bit that of sgemm_supertiled with the same extents on the same values),
+ * store C.  A and B super-tiles are loaded into the least recently used slot
+ * of their kind on a load stream of its own, which runs ahead of the compute
+ * (`stream`) as far as free slots allow; C stores run on a store stream;
+ * events order every load after the last compute or store that used its
+ * slot.  Device slot pitches are the tile widths rounded up to 4 floats, each
+ * slot starting on a 256-byte boundary; slot counts above the number of
+ * distinct tiles of their kind are cut to it: for a plan that sgemm_plan_supertiles
+ * returned for the same M, N, K and beta, at most the plan's `device_bytes`
+ * are allocated.  Synchronous: returns once C is complete in host memory,
+ * after freeing everything it allocated.  Arguments: 1..11 as sgemm (host
+ * pointers), 12 plan, 13 stream.  Errors: negative argument index as sgemm
+ * (-12: plan NULL or an extent or slot count below 1), SGEMM_ERR_TOO_LARGE,
+ * SGEMM_ERR_ALLOC, or a HIP status; after a failure every stream is drained
+ * and everything freed, and C may hold finished super-tiles next to
+ * unchanged ones.
+ */
+typedef struct sgemm_plan_model {
+    double gemm_tflops;   /* sustained GEMM rate of one step leaf, TFLOP/s */
+    double link_gbs;      /* host<->device copy bandwidth, GB/s */
+} sgemm_plan_model;
+
+typedef struct sgemm_plan {
+    int64_t TM, TN, TK;                /* super-tile extents */
+    int32_t a_slots, b_slots, c_slots; /* device tile buffers of each kind */
+    int64_t device_bytes;              /* device memory the slots take */
+    double transfer_bytes;             /* modeled host<->device traffic */
+    double modeled_ms;                 /* modeled time of the whole product */
+} sgemm_plan;
+
+int sgemm_plan_supertiles(int64_t M, int64_t N, int64_t K, float beta, int64_t device_bytes,
+                          const sgemm_plan_model* model, sgemm_plan* out);
+int sgemm_supertiled_host(int64_t M, int64_t N, int64_t K, float alpha,
+                          const float* A, int64_t lda, const float* B, int64_t ldb,
+                          float beta, float* C, int64_t ldc, const sgemm_plan* plan,
+                          void* stream);
 
 /*
  * Launch trace.  Between sgemm_trace_begin(capacity) and sgemm_trace_end,

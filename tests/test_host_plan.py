@@ -1,0 +1,161 @@
+"""The super-tile planner and the host-resident executor's argument checks,
+on the CPU (the planner is host-only; the checks return before any HIP call).
+
+The planner follows the tuner of the "@cluster" page ("What runs today",
+Tuning): candidates are enumerated, those that do not fit the memory budget
+are dropped, and the rest are ranked by a cost model."""
+import itertools
+
+import pytest
+
+import fp32_gemm_02_amd as g
+
+
+def _extents(dim):
+    v, p = [], 256
+    while p < dim:
+        v.append(p)
+        p *= 2
+    return v + [dim]
+
+
+def _cdiv(a, b):
+    return -(-a // b)
+
+
+def _slot_bytes(rows, cols):
+    # rows x pitch, pitch rounded up to 4 floats, slot rounded up to 256 bytes
+    return 4 * ((rows * (_cdiv(cols, 4) * 4) + 63) // 64 * 64)
+
+
+def _device_bytes(p):
+    return (p.a_slots * _slot_bytes(p.TM, p.TK) + p.b_slots * _slot_bytes(p.TK, p.TN)
+            + p.c_slots * _slot_bytes(p.TM, p.TN))
+
+
+SHAPES = [(16384, 16384, 16384), (5003, 3001, 2047), (65536, 512, 4096), (300, 270, 200),
+          (1, 1, 1), (4096, 4096, 100000)]
+BUDGETS = [1 << 34, 2 << 30, 1 << 30, 256 << 20, 64 << 20, 8 << 20]
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_plan_is_a_candidate_and_fits_the_budget(M, N, K):
+    for budget, beta in itertools.product(BUDGETS, (0.0, 1.0)):
+        try:
+            p = g.sgemm_plan_supertiles(M, N, K, beta, budget)
+        except RuntimeError as e:
+            assert "no plan fits" in str(e)
+            continue
+        assert p.TM in _extents(M) and p.TN in _extents(N) and p.TK in _extents(K)
+        gm, gn, nk = _cdiv(M, p.TM), _cdiv(N, p.TN), _cdiv(K, p.TK)
+        assert p.a_slots in (min(2, nk), nk)
+        assert p.b_slots in (min(2, nk), nk * gn)
+        assert p.c_slots == min(2, gm * gn)
+        # the slot bytes the executor allocates, within the budget
+        assert p.device_bytes == _device_bytes(p) <= budget
+        # host<->device bytes: A once or once per column of super-tiles, B
+        # once or once per row, C out (and in unless beta == 0)
+        a = 4 * M * K * (1 if p.a_slots >= nk else gn)
+        b = 4 * K * N * (1 if p.b_slots >= nk * gn else gm)
+        c = 4 * M * N * (2 if beta else 1)
+        assert p.transfer_bytes == pytest.approx(a + b + c, rel=1e-12)
+        assert p.modeled_ms > 0
+
+
+def test_more_memory_never_models_slower():
+    for M, N, K in SHAPES:
+        prev = None
+        for budget in sorted(BUDGETS):
+            try:
+                p = g.sgemm_plan_supertiles(M, N, K, 1.0, budget)
+            except RuntimeError:
+                assert prev is None     # once something fits, a larger budget fits too
+                continue
+            if prev is not None:
+                assert p.modeled_ms <= prev.modeled_ms * (1 + 1e-9)
+            prev = p
+
+
+def test_plan_when_everything_fits_keeps_operands_resident():
+    """With room for all of B and a row of A, each element of A and B crosses
+    the link once, and loads and stores overlap, so the modeled time is the
+    larger of compute and loads plus the pipeline's fill."""
+    M = N = K = 16384
+    p = g.sgemm_plan_supertiles(M, N, K, 1.0, 16 << 30)
+    nk, gn = _cdiv(K, p.TK), _cdiv(N, p.TN)
+    assert p.a_slots == nk and p.b_slots == nk * gn
+    assert p.transfer_bytes == 4.0 * (M * K + K * N + 2 * M * N)
+    # super-tiles large enough to fill the 256 CUs with 256x256 workgroup tiles
+    assert _cdiv(p.TM, 256) * _cdiv(p.TN, 256) >= 256
+    # a faster link moves the plan toward fewer, larger tiles, never slower
+    q = g.sgemm_plan_supertiles(M, N, K, 1.0, 16 << 30, link_gbs=1e6)
+    assert q.modeled_ms < p.modeled_ms
+
+
+def test_plan_streams_when_memory_is_short():
+    M = N = K = 16384
+    p = g.sgemm_plan_supertiles(M, N, K, 1.0, 64 << 20)
+    assert p.device_bytes <= 64 << 20
+    assert p.transfer_bytes > 4.0 * (M * K + K * N + 2 * M * N)   # some re-loads
+
+
+def test_plan_budget_error():
+    with pytest.raises(RuntimeError, match="no plan fits"):
+        g.sgemm_plan_supertiles(16384, 16384, 16384, 1.0, 1 << 20)
+    assert g.lib().sgemm_status_string(g.SGEMM_ERR_BUDGET) == b"no plan fits the device memory budget"
+
+
+def test_plan_argument_checks():
+    import ctypes
+    lib = g.lib()
+    out = g.sgemm_plan()
+    ok_model = g.sgemm_plan_model(100.0, 20.0)
+    bad_models = [g.sgemm_plan_model(0.0, 20.0), g.sgemm_plan_model(100.0, -1.0),
+                  g.sgemm_plan_model(float("nan"), 20.0)]
+    assert lib.sgemm_plan_supertiles(0, 4, 4, 1.0, 1 << 30, None, ctypes.byref(out)) == -1
+    assert lib.sgemm_plan_supertiles(4, 0, 4, 1.0, 1 << 30, None, ctypes.byref(out)) == -2
+    assert lib.sgemm_plan_supertiles(4, 4, 0, 1.0, 1 << 30, None, ctypes.byref(out)) == -3
+    assert lib.sgemm_plan_supertiles(4, 4, 4, 1.0, 0, None, ctypes.byref(out)) == -5
+    for m in bad_models:
+        assert lib.sgemm_plan_supertiles(4, 4, 4, 1.0, 1 << 30, ctypes.byref(m),
+                                         ctypes.byref(out)) == -6
+    assert lib.sgemm_plan_supertiles(4, 4, 4, 1.0, 1 << 30, ctypes.byref(ok_model), None) == -7
+    assert lib.sgemm_plan_supertiles(4, 4, 4, 1.0, 1 << 30, ctypes.byref(ok_model),
+                                     ctypes.byref(out)) == 0
+    assert (out.TM, out.TN, out.TK) == (4, 4, 4)
+
+
+def _plan(TM=64, TN=64, TK=64, a=2, b=2, c=2):
+    p = g.sgemm_plan()
+    p.TM, p.TN, p.TK, p.a_slots, p.b_slots, p.c_slots = TM, TN, TK, a, b, c
+    return p
+
+
+NULL = None
+
+
+@pytest.mark.parametrize("args,want", [
+    ((-1, 4, 4, 1.0, 8, 4, 8, 4, 0.0, 8, 4), -1),
+    ((4, -1, 4, 1.0, 8, 4, 8, 4, 0.0, 8, 4), -2),
+    ((4, 4, -1, 1.0, 8, 4, 8, 4, 0.0, 8, 4), -3),
+    ((4, 4, 5, 1.0, 8, 4, 8, 4, 0.0, 8, 4), -6),     # lda < K
+    ((4, 6, 4, 1.0, 8, 4, 8, 5, 0.0, 8, 6), -8),     # ldb < N
+    ((4, 6, 4, 1.0, 8, 4, 8, 6, 0.0, 8, 5), -11),    # ldc < N
+    ((4, 4, 4, 1.0, NULL, 4, 8, 4, 0.0, 8, 4), -5),  # A read but NULL
+    ((4, 4, 4, 1.0, 8, 4, NULL, 4, 0.0, 8, 4), -7),  # B read but NULL
+    ((4, 4, 4, 1.0, 8, 4, 8, 4, 0.0, NULL, 4), -10),  # C NULL
+    ((0, 4, 4, 1.0, NULL, 4, NULL, 4, 0.0, NULL, 4), 0),  # M == 0: no-op
+    ((4, 0, 4, 1.0, NULL, 4, NULL, 1, 0.0, NULL, 1), 0),  # N == 0: no-op
+    ((4, 4, 4, 0.0, NULL, 4, NULL, 4, 1.0, 8, 4), 0),     # alpha = 0, beta = 1: C unchanged
+    ((4, 4, 0, 1.0, NULL, 1, NULL, 4, 1.0, 8, 4), 0),     # K = 0, beta = 1: C unchanged
+    ((1 << 31, 4, 4, 1.0, 8, 4, 8, 4, 0.0, 8, 4), g.SGEMM_ERR_TOO_LARGE),
+])
+def test_host_executor_argument_checks(args, want):
+    assert g.sgemm_supertiled_host_raw(*args, plan=_plan(), stream=0) == want
+
+
+@pytest.mark.parametrize("plan", [None, _plan(TM=0), _plan(TN=-1), _plan(TK=0), _plan(a=0),
+                                  _plan(b=0), _plan(c=0)])
+def test_host_executor_plan_checks(plan):
+    assert g.sgemm_supertiled_host_raw(4, 4, 4, 1.0, 8, 4, 8, 4, 1.0, 8, 4, plan,
+                                       stream=0) == -12
