@@ -24,6 +24,8 @@ SGEMM_ERR_TOO_LARGE = 3
 SGEMM_ERR_ALLOC = 4
 SGEMM_ERR_BUDGET = 5
 SGEMM_ERR_HIP_BASE = 1000
+SGEMM_WALK_ROWS = 0
+SGEMM_WALK_SHELLS = 1
 SGEMM_KIND_GEMM = 0
 SGEMM_KIND_INIT_LEAF = 1
 
@@ -52,13 +54,15 @@ class sgemm_plan_model(ctypes.Structure):
 class sgemm_plan(ctypes.Structure):
     _fields_ = [("TM", ctypes.c_int64), ("TN", ctypes.c_int64), ("TK", ctypes.c_int64),
                 ("a_slots", ctypes.c_int32), ("b_slots", ctypes.c_int32),
-                ("c_slots", ctypes.c_int32), ("device_bytes", ctypes.c_int64),
+                ("c_slots", ctypes.c_int32), ("walk", ctypes.c_int32),
+                ("device_bytes", ctypes.c_int64),
                 ("transfer_bytes", ctypes.c_double), ("modeled_ms", ctypes.c_double)]
 
     def __repr__(self):
-        return ("sgemm_plan(TM=%d, TN=%d, TK=%d, slots a/b/c=%d/%d/%d, device_bytes=%d, "
-                "transfer_bytes=%.4g, modeled_ms=%.4g)" % (
+        return ("sgemm_plan(TM=%d, TN=%d, TK=%d, slots a/b/c=%d/%d/%d, walk=%s, "
+                "device_bytes=%d, transfer_bytes=%.4g, modeled_ms=%.4g)" % (
                     self.TM, self.TN, self.TK, self.a_slots, self.b_slots, self.c_slots,
+                    {SGEMM_WALK_ROWS: "rows", SGEMM_WALK_SHELLS: "shells"}.get(self.walk, self.walk),
                     self.device_bytes, self.transfer_bytes, self.modeled_ms))
 
 
@@ -211,7 +215,7 @@ def sgemm_plan_supertiles(M, N, K, beta, device_bytes, gemm_tflops=None, link_gb
     """Super-tile extents and device slots for the host-resident product (host only)."""
     model = None
     if gemm_tflops is not None or link_gbs is not None:
-        model = ctypes.byref(sgemm_plan_model(gemm_tflops or 140.0, link_gbs or 50.0))
+        model = ctypes.byref(sgemm_plan_model(gemm_tflops or 140.0, link_gbs or 55.0))
     plan = sgemm_plan()
     _check(lib().sgemm_plan_supertiles(M, N, K, beta, device_bytes, model, ctypes.byref(plan)),
            "sgemm_plan_supertiles")

@@ -8,15 +8,20 @@
 // that works ahead of the compute stream as far as free slots allow, stores
 // on another (the link carries both directions at once).
 //
-// The planner picks the super-tile extents and slot counts the way the pages'
-// cluster tuner does: enumerate candidates, drop those whose working set does
-// not fit the device budget, rank the rest by a model of compute and transfer
-// time built from figures the caller supplies.
+// The planner picks the super-tile extents, slot counts and walk order the
+// way the pages' cluster tuner does: enumerate candidates, drop those whose
+// working set does not fit the device budget, rank the rest by modeled time.
+// The model is a replay of the executor's own schedule (the same walk, the
+// same slot replacement, in-order load and store streams) with durations
+// from a few rates, so what the planner ranks is what the executor issues.
 
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
 #include <cmath>
+#include <list>
+#include <unordered_map>
+#include <utility>
 #include <vector>
 
 #include "phobos_sgemm.h"
@@ -33,12 +38,16 @@ int host_launch_init(int64_t M, int64_t N, float beta, float* C, int64_t ldc,
 
 namespace {
 
-constexpr double kDefaultTflops = 140.0;   // sustained step-leaf rate on MI355X
-constexpr double kDefaultLinkGBs = 50.0;   // pinned host<->device copies
+// Default model rates (MI355X, PCIe 5.0 x16 host link, pinned memory).
+constexpr double kDefaultTflops = 140.0;   // sustained step-leaf rate
+constexpr double kDefaultLinkGBs = 55.0;   // one direction
+constexpr double kDuplex = 1.7;            // both directions at once: this many times one
+constexpr double kCopyMs = 0.010;          // fixed cost of one copy call
 constexpr double kLaunchMs = 0.015;        // per-launch ramp and gap
+constexpr double kHbmGBs = 5000.0;         // effective HBM rate of a leaf's C traffic
 constexpr int64_t kCtaTile = 256;          // output tile of one workgroup (large shapes)
-constexpr int64_t kCUs = 256;              // compute units of an MI355X
-constexpr double kHbmGBs = 5000.0;         // effective HBM rate of a step leaf's C traffic
+constexpr int64_t kCUs = 256;              // compute units
+constexpr int64_t kMaxLaunches = int64_t(1) << 20;   // larger candidates are not planned
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t up4(int64_t x) { return (x + 3) / 4 * 4; }
@@ -56,50 +65,145 @@ std::vector<int64_t> extents(int64_t dim) {
     return v;
 }
 
-struct Modeled {
-    int64_t device_bytes;
-    double transfer_bytes, ms;
+// Output super-tiles (pm, pn) in the order they are computed.  Rows: the
+// pages' row-major placement.  Shells: growing squares, shell s = the tiles
+// with max(pm, pn) == s, first row s left of the diagonal, then column s
+// above it, then (s, s); each shell brings one new row of A super-tiles and
+// one new column of B super-tiles, so loads spread over the whole run
+// instead of all of B arriving during the first row of outputs.
+std::vector<std::pair<int64_t, int64_t>> walk_order(int64_t gm, int64_t gn, int32_t walk) {
+    std::vector<std::pair<int64_t, int64_t>> v;
+    v.reserve((size_t)(gm * gn));
+    if (walk == SGEMM_WALK_ROWS) {
+        for (int64_t pm = 0; pm < gm; ++pm)
+            for (int64_t pn = 0; pn < gn; ++pn) v.emplace_back(pm, pn);
+        return v;
+    }
+    for (int64_t s = 0; s < std::max(gm, gn); ++s) {
+        if (s < gm)
+            for (int64_t pn = 0; pn < std::min(s, gn); ++pn) v.emplace_back(s, pn);
+        if (s < gn)
+            for (int64_t pm = 0; pm < std::min(s, gm); ++pm) v.emplace_back(pm, s);
+        if (s < gm && s < gn) v.emplace_back(s, s);
+    }
+    return v;
+}
+
+// Least-recently-used assignment of tiles of one kind to a fixed set of slots.
+class SlotTable {
+public:
+    explicit SlotTable(int64_t slots) : holds_(slots, -1), pos_(slots) {
+        for (int64_t s = 0; s < slots; ++s) pos_[s] = lru_.insert(lru_.end(), s);
+    }
+    // Slot that holds tile `id` after the call; *load is set when the tile
+    // has to be loaded into it first (the slot held another tile, or none).
+    int64_t acquire(int64_t id, bool* load) {
+        auto it = where_.find(id);
+        int64_t s;
+        if (it != where_.end()) {
+            s = it->second;
+            *load = false;
+        } else {
+            s = lru_.front();
+            if (holds_[s] >= 0) where_.erase(holds_[s]);
+            holds_[s] = id;
+            where_[id] = s;
+            *load = true;
+        }
+        lru_.splice(lru_.end(), lru_, pos_[s]);
+        return s;
+    }
+
+private:
+    std::vector<int64_t> holds_;                     // slot -> tile id, -1: empty
+    std::unordered_map<int64_t, int64_t> where_;     // tile id -> slot
+    std::list<int64_t> lru_;                         // slots, least recently used first
+    std::vector<std::list<int64_t>::iterator> pos_;  // slot -> its place in lru_
 };
 
-Modeled model_plan(int64_t M, int64_t N, int64_t K, float beta, int64_t TM, int64_t TN,
-                   int64_t TK, int32_t a_slots, int32_t b_slots, int32_t c_slots,
-                   const sgemm_plan_model& m) {
-    const int64_t gm = cdiv(M, TM), gn = cdiv(N, TN), nk = cdiv(K, TK);
-    const int64_t a_tile = 4 * slot_floats(TM, TK), b_tile = 4 * slot_floats(TK, TN),
-                  c_tile = 4 * slot_floats(TM, TN);
-    Modeled r{};
-    r.device_bytes = a_slots * a_tile + b_slots * b_tile + c_slots * c_tile;
-    const double a_bytes = 4.0 * M * K * (a_slots >= nk ? 1 : gn);
-    const double b_bytes = 4.0 * K * N * (b_slots >= nk * gn ? 1 : gm);
-    const double c_in = beta != 0.0f ? 4.0 * M * N : 0.0, c_out = 4.0 * M * N;
-    r.transfer_bytes = a_bytes + b_bytes + c_in + c_out;
-    // a step leaf runs ceil(TM/256)*ceil(TN/256) workgroups in waves of one per
-    // CU: a super-tile with fewer workgroups than CUs leaves the rest idle
-    const int64_t ctas = cdiv(TM, kCtaTile) * cdiv(TN, kCtaTile);
-    const double fill = (double)ctas / (double)(cdiv(ctas, kCUs) * kCUs);
-    // every step leaf also reads and writes its C super-tile in device memory
-    const double c_rw_ms = 2.0 * 4.0 * TM * TN / (kHbmGBs * 1e9) * 1e3;
-    const double compute_ms = 2.0 * M * N * K / (m.gemm_tflops * 1e12 * fill) * 1e3 +
-                              gm * gn * nk * (kLaunchMs + c_rw_ms);
-    // the link is full duplex: loads and stores run on streams of their own
-    const double link = m.link_gbs * 1e9;
-    const double transfer_ms = std::max(a_bytes + b_bytes + c_in, c_out) / link * 1e3;
-    // the first A, B (and C) tiles are loaded before any compute, the last C
-    // tile is stored after it
-    const double fill_ms = (a_tile + b_tile + (beta != 0.0f ? c_tile : 0) + c_tile) / link * 1e3;
-    r.ms = std::max(compute_ms, transfer_ms) + fill_ms;
-    return r;
+struct Candidate {
+    int64_t TM, TN, TK, na, nb, nc;
+    int32_t walk;
+    int64_t device_bytes;
+    double lower_ms;   // no schedule of this candidate can be faster
+};
+
+struct Modeled {
+    double ms, h2d_bytes, d2h_bytes;
+};
+
+double fill_of(int64_t rows, int64_t cols) {
+    // a step leaf runs ceil(rows/256)*ceil(cols/256) workgroups in waves of
+    // one per CU: a super-tile with fewer workgroups than CUs leaves the rest idle
+    const int64_t ctas = cdiv(rows, kCtaTile) * cdiv(cols, kCtaTile);
+    return (double)ctas / (double)(cdiv(ctas, kCUs) * kCUs);
 }
+
+// Replays the executor's schedule: the compute stream runs init and step
+// leaves in walk order; the load stream runs loads in the order they are
+// issued, each after the last use of its slot; the store stream stores each
+// finished super-tile.  Returns the modeled time and the bytes moved.
+Modeled simulate(int64_t M, int64_t N, int64_t K, float beta, const Candidate& c,
+                 const sgemm_plan_model& m) {
+    const int64_t gm = cdiv(M, c.TM), gn = cdiv(N, c.TN), nk = cdiv(K, c.TK);
+    const double link = m.link_gbs * 1e9;
+    auto copy_ms = [&](double bytes) { return bytes / link * 1e3 + kCopyMs; };
+    auto step_ms = [&](int64_t rows, int64_t cols, int64_t depth) {
+        return 2.0 * rows * cols * depth / (m.gemm_tflops * 1e12 * fill_of(rows, cols)) * 1e3 +
+               kLaunchMs + 8.0 * rows * cols / (kHbmGBs * 1e9) * 1e3;
+    };
+    SlotTable ta(c.na), tb(c.nb);
+    std::vector<double> a_ready(c.na, 0), a_free(c.na, 0), b_ready(c.nb, 0), b_free(c.nb, 0),
+        c_free(c.nc, 0);
+    double h2d = 0, d2h = 0, comp = 0, h2d_bytes = 0, d2h_bytes = 0;
+    int64_t ci = 0;
+    for (const auto& t : walk_order(gm, gn, c.walk)) {
+        const int64_t pm = t.first, pn = t.second;
+        const int64_t rows = std::min(c.TM, M - pm * c.TM), cols = std::min(c.TN, N - pn * c.TN);
+        const int64_t slot = ci++ % c.nc;
+        const double cb = 4.0 * rows * cols;
+        if (beta != 0.0f) {
+            h2d = std::max(h2d, c_free[slot]) + copy_ms(cb);
+            h2d_bytes += cb;
+            comp = std::max(comp, h2d);
+        } else {
+            comp = std::max(comp, c_free[slot]);
+        }
+        if (beta != 1.0f) comp += kLaunchMs + (beta != 0.0f ? 2 : 1) * cb / (kHbmGBs * 1e9) * 1e3;
+        for (int64_t kt = 0; kt < nk; ++kt) {
+            const int64_t depth = std::min(c.TK, K - kt * c.TK);
+            bool load;
+            const int64_t sa = ta.acquire(pm * nk + kt, &load);
+            if (load) {
+                h2d = std::max(h2d, a_free[sa]) + copy_ms(4.0 * rows * depth);
+                h2d_bytes += 4.0 * rows * depth;
+                a_ready[sa] = h2d;
+            }
+            const int64_t sb = tb.acquire(kt * gn + pn, &load);
+            if (load) {
+                h2d = std::max(h2d, b_free[sb]) + copy_ms(4.0 * depth * cols);
+                h2d_bytes += 4.0 * depth * cols;
+                b_ready[sb] = h2d;
+            }
+            comp = std::max({comp, a_ready[sa], b_ready[sb]}) + step_ms(rows, cols, depth);
+            a_free[sa] = b_free[sb] = comp;
+        }
+        d2h = std::max(d2h, comp) + copy_ms(cb);
+        d2h_bytes += cb;
+        c_free[slot] = d2h;
+    }
+    // both directions together move at most kDuplex times one direction's rate
+    const double both = (h2d_bytes + d2h_bytes) / (kDuplex * link) * 1e3;
+    return Modeled{std::max({comp, d2h, both}), h2d_bytes, d2h_bytes};
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? SGEMM_OK : SGEMM_ERR_HIP_BASE + (int)e; }
 
 struct Slot {
     float* dev = nullptr;
-    int64_t i = -1, j = -1;        // tile coordinates held (-1: none)
-    uint64_t last = 0;             // LRU stamp
     hipEvent_t ready = nullptr;    // recorded on the load stream after a load
     hipEvent_t free = nullptr;     // recorded after the slot's last use (compute, or a C store)
 };
-
-int hip_status(hipError_t e) { return e == hipSuccess ? SGEMM_OK : SGEMM_ERR_HIP_BASE + (int)e; }
 
 }  // namespace
 
@@ -117,32 +221,60 @@ int sgemm_plan_supertiles(int64_t M, int64_t N, int64_t K, float beta, int64_t d
         if (!(model->gemm_tflops > 0.0) || !(model->link_gbs > 0.0)) return -6;
         m = *model;
     }
-    bool found = false;
-    sgemm_plan best{};
+    if (M > (int64_t(1) << 30) || N > (int64_t(1) << 30) || K > (int64_t(1) << 30))
+        return SGEMM_ERR_TOO_LARGE;
+    const double link = m.link_gbs * 1e9;
+    // every element of A and B crosses the link at least once, C once each way
+    const double min_h2d = 4.0 * ((double)M * K + (double)K * N + (beta != 0.0f ? (double)M * N : 0));
+    const double min_d2h = 4.0 * (double)M * N;
+    const double min_link_ms =
+        std::max({min_h2d / link, min_d2h / link, (min_h2d + min_d2h) / (kDuplex * link)}) * 1e3;
+    const double min_flop_ms = 2.0 * M * N * K / (m.gemm_tflops * 1e12) * 1e3;
+
+    std::vector<Candidate> cands;
     for (int64_t TM : extents(M))
         for (int64_t TN : extents(N))
             for (int64_t TK : extents(K)) {
                 const int64_t gm = cdiv(M, TM), gn = cdiv(N, TN), nk = cdiv(K, TK);
-                const int32_t c_slots = (int32_t)std::min<int64_t>(2, gm * gn);
-                const int64_t a_opts[2] = {std::min<int64_t>(2, nk), nk};
-                const int64_t b_opts[2] = {std::min<int64_t>(2, nk), nk * gn};
-                for (int64_t na : a_opts)
-                    for (int64_t nb : b_opts) {
-                        if (na > (1 << 20) || nb > (1 << 20)) continue;
-                        const Modeled r = model_plan(M, N, K, beta, TM, TN, TK, (int32_t)na,
-                                                     (int32_t)nb, c_slots, m);
-                        if (r.device_bytes > device_bytes) continue;
-                        const bool better =
-                            !found || r.ms < best.modeled_ms * (1 - 1e-9) ||
-                            (r.ms <= best.modeled_ms * (1 + 1e-9) && r.device_bytes < best.device_bytes);
-                        if (better) {
-                            best = sgemm_plan{TM, TN, TK, (int32_t)na, (int32_t)nb, c_slots,
-                                              r.device_bytes, r.transfer_bytes, r.ms};
-                            found = true;
-                        }
+                if (gm * gn * nk > kMaxLaunches) continue;
+                const int64_t nc = std::min<int64_t>(2, gm * gn);
+                const int64_t a_all = gm * nk, b_all = nk * gn;
+                const int64_t a_opts[3] = {std::min<int64_t>(2, nk), nk, a_all};
+                const int64_t b_opts[2] = {std::min<int64_t>(2, nk), b_all};
+                for (int ia = 0; ia < 3; ++ia)
+                    for (int ib = 0; ib < 2; ++ib) {
+                        const int64_t na = a_opts[ia], nb = b_opts[ib];
+                        if ((ia > 0 && na == a_opts[ia - 1]) || (ib > 0 && nb == b_opts[0])) continue;
+                        const int64_t bytes = 4 * (na * slot_floats(TM, TK) +
+                                                   nb * slot_floats(TK, TN) + nc * slot_floats(TM, TN));
+                        if (bytes > device_bytes) continue;
+                        const double lower =
+                            std::max(min_flop_ms + gm * gn * nk * kLaunchMs, min_link_ms);
+                        // row-major walks keep one row of A resident at most;
+                        // shells need all of A and B resident
+                        if (na <= nk)
+                            cands.push_back({TM, TN, TK, na, nb, nc, SGEMM_WALK_ROWS, bytes, lower});
+                        if (na == a_all && nb == b_all && gm > 1 && gn > 1)
+                            cands.push_back({TM, TN, TK, na, nb, nc, SGEMM_WALK_SHELLS, bytes, lower});
                     }
             }
-    if (!found) return SGEMM_ERR_BUDGET;
+    if (cands.empty()) return SGEMM_ERR_BUDGET;
+    std::stable_sort(cands.begin(), cands.end(), [](const Candidate& x, const Candidate& y) {
+        return x.lower_ms < y.lower_ms;
+    });
+    bool found = false;
+    sgemm_plan best{};
+    for (const Candidate& c : cands) {
+        if (found && c.lower_ms > best.modeled_ms) break;   // no later candidate can win
+        const Modeled r = simulate(M, N, K, beta, c, m);
+        const bool better = !found || r.ms < best.modeled_ms * (1 - 1e-9) ||
+                            (r.ms <= best.modeled_ms * (1 + 1e-9) && c.device_bytes < best.device_bytes);
+        if (better) {
+            best = sgemm_plan{c.TM, c.TN, c.TK, (int32_t)c.na, (int32_t)c.nb, (int32_t)c.nc,
+                              c.walk, c.device_bytes, r.h2d_bytes + r.d2h_bytes, r.ms};
+            found = true;
+        }
+    }
     *out = best;
     return SGEMM_OK;
 }
@@ -157,7 +289,8 @@ int sgemm_supertiled_host(int64_t M, int64_t N, int64_t K, float alpha, const fl
     if (ldb < std::max<int64_t>(1, N)) return -8;
     if (ldc < std::max<int64_t>(1, N)) return -11;
     if (plan == nullptr || plan->TM < 1 || plan->TN < 1 || plan->TK < 1 || plan->a_slots < 1 ||
-        plan->b_slots < 1 || plan->c_slots < 1)
+        plan->b_slots < 1 || plan->c_slots < 1 ||
+        (plan->walk != SGEMM_WALK_ROWS && plan->walk != SGEMM_WALK_SHELLS))
         return -12;
     if (M == 0 || N == 0) return SGEMM_OK;
     const bool steps = K > 0 && alpha != 0.0f;
@@ -182,26 +315,26 @@ int sgemm_supertiled_host(int64_t M, int64_t N, int64_t K, float alpha, const fl
     const int64_t total = na * a_tile + nb * b_tile + nc * c_tile;
 
     float* pool = nullptr;
-    hipStream_t h2d = nullptr, d2h = nullptr;   // loads, stores
-    hipEvent_t start = nullptr;
-    std::vector<Slot> sa(na), sb(nb), sc(nc);
-    std::vector<hipEvent_t> c_done(nc, nullptr);
-    int st = SGEMM_OK;
-    // runs `call` only while nothing has failed; keeps the first failure
-#define PHOBOS_CHK(call)                                        \
-    do {                                                        \
-        if (st == SGEMM_OK) st = hip_status(call);              \
-    } while (0)
     if (hipMalloc(&pool, total * sizeof(float)) != hipSuccess) {
         (void)hipGetLastError();   // a failed allocation must not fail later launches
         return SGEMM_ERR_ALLOC;
     }
+    hipStream_t h2d = nullptr, d2h = nullptr;   // loads, stores
+    hipEvent_t start = nullptr;
+    std::vector<Slot> sa(na), sb(nb), sc(nc);
+    std::vector<hipEvent_t> c_done(nc, nullptr);
     {
         float* p = pool;
         for (auto& s : sa) { s.dev = p; p += a_tile; }
         for (auto& s : sb) { s.dev = p; p += b_tile; }
         for (auto& s : sc) { s.dev = p; p += c_tile; }
     }
+    int st = SGEMM_OK;
+    // runs `call` only while nothing has failed; keeps the first failure
+#define PHOBOS_CHK(call)                                        \
+    do {                                                        \
+        if (st == SGEMM_OK) st = hip_status(call);              \
+    } while (0)
     PHOBOS_CHK(hipStreamCreateWithFlags(&h2d, hipStreamNonBlocking));
     PHOBOS_CHK(hipStreamCreateWithFlags(&d2h, hipStreamNonBlocking));
     PHOBOS_CHK(hipEventCreateWithFlags(&start, hipEventDisableTiming));
@@ -218,73 +351,65 @@ int sgemm_supertiled_host(int64_t M, int64_t N, int64_t K, float alpha, const fl
     for (auto* v : {&sa, &sb, &sc})
         for (auto& s : *v) PHOBOS_CHK(hipEventRecord(s.free, comp));
 
-    uint64_t clock = 0;
-    // Make tile (i, j) of a host matrix resident in one of `slots`, loading it
-    // on the load stream into the least recently used slot once no queued
-    // compute uses that slot any more.
-    auto acquire = [&](std::vector<Slot>& slots, int64_t i, int64_t j, const float* host,
+    // Make a tile resident in one of `slots`, loading it on the load stream
+    // into the least recently used slot once no queued work uses that slot.
+    auto acquire = [&](SlotTable& table, std::vector<Slot>& slots, int64_t id, const float* host,
                        int64_t ldh, int64_t r0, int64_t c0, int64_t rows, int64_t cols,
                        int64_t pitch) -> Slot* {
-        for (auto& s : slots)
-            if (s.i == i && s.j == j) {
-                s.last = ++clock;
-                return &s;
-            }
-        Slot* v = &slots[0];
-        for (auto& s : slots)
-            if (s.last < v->last) v = &s;
-        PHOBOS_CHK(hipStreamWaitEvent(h2d, v->free, 0));
-        PHOBOS_CHK(hipMemcpy2DAsync(v->dev, pitch * sizeof(float), host + r0 * ldh + c0,
-                                    ldh * sizeof(float), cols * sizeof(float), rows,
-                                    hipMemcpyHostToDevice, h2d));
-        PHOBOS_CHK(hipEventRecord(v->ready, h2d));
-        v->i = i;
-        v->j = j;
-        v->last = ++clock;
+        bool load;
+        Slot* v = &slots[table.acquire(id, &load)];
+        if (load) {
+            PHOBOS_CHK(hipStreamWaitEvent(h2d, v->free, 0));
+            PHOBOS_CHK(hipMemcpy2DAsync(v->dev, pitch * sizeof(float), host + r0 * ldh + c0,
+                                        ldh * sizeof(float), cols * sizeof(float), rows,
+                                        hipMemcpyHostToDevice, h2d));
+            PHOBOS_CHK(hipEventRecord(v->ready, h2d));
+        }
         return v;
     };
 
+    SlotTable ta(std::max<int64_t>(na, 1)), tb(std::max<int64_t>(nb, 1));
     int64_t ci = 0;
-    for (int64_t pm = 0; pm < gm && st == SGEMM_OK; ++pm) {
+    for (const auto& t : walk_order(gm, gn, plan->walk)) {
+        if (st != SGEMM_OK) break;
+        const int64_t pm = t.first, pn = t.second;
         const int64_t r0 = pm * TM, rows = std::min(TM, M - r0);
-        for (int64_t pn = 0; pn < gn && st == SGEMM_OK; ++pn) {
-            const int64_t c0 = pn * TN, cols = std::min(TN, N - c0);
-            const int64_t slot = ci++ % nc;
-            Slot& cs = sc[slot];
-            // cs.free is recorded after the store of the slot's previous tile
-            // (or at the start): nothing overwrites the slot before that
-            if (beta != 0.0f) {
-                PHOBOS_CHK(hipStreamWaitEvent(h2d, cs.free, 0));
-                PHOBOS_CHK(hipMemcpy2DAsync(cs.dev, ldc_t * sizeof(float), C + r0 * ldc + c0,
-                                            ldc * sizeof(float), cols * sizeof(float), rows,
-                                            hipMemcpyHostToDevice, h2d));
-                PHOBOS_CHK(hipEventRecord(cs.ready, h2d));
-                PHOBOS_CHK(hipStreamWaitEvent(comp, cs.ready, 0));
-            } else {
-                PHOBOS_CHK(hipStreamWaitEvent(comp, cs.free, 0));
-            }
-            // init leaf, then one step leaf per K chunk
-            if (st == SGEMM_OK) st = phobos::host_launch_init(rows, cols, beta, cs.dev, ldc_t, comp);
-            for (int64_t kt = 0; kt < nk && st == SGEMM_OK; ++kt) {
-                const int64_t k0 = kt * TK, depth = std::min(TK, K - k0);
-                Slot* a = acquire(sa, pm, kt, A, lda, r0, k0, rows, depth, lda_t);
-                Slot* b = acquire(sb, kt, pn, B, ldb, k0, c0, depth, cols, ldb_t);
-                PHOBOS_CHK(hipStreamWaitEvent(comp, a->ready, 0));
-                PHOBOS_CHK(hipStreamWaitEvent(comp, b->ready, 0));
-                if (st != SGEMM_OK) break;
-                st = phobos::host_launch_gemm(rows, cols, depth, alpha, a->dev, lda_t, b->dev,
-                                              ldb_t, 1.0f, cs.dev, ldc_t, comp);
-                PHOBOS_CHK(hipEventRecord(a->free, comp));
-                PHOBOS_CHK(hipEventRecord(b->free, comp));
-            }
-            // store the finished super-tile on the store stream
-            PHOBOS_CHK(hipEventRecord(c_done[slot], comp));
-            PHOBOS_CHK(hipStreamWaitEvent(d2h, c_done[slot], 0));
-            PHOBOS_CHK(hipMemcpy2DAsync(C + r0 * ldc + c0, ldc * sizeof(float), cs.dev,
-                                        ldc_t * sizeof(float), cols * sizeof(float), rows,
-                                        hipMemcpyDeviceToHost, d2h));
-            PHOBOS_CHK(hipEventRecord(cs.free, d2h));
+        const int64_t c0 = pn * TN, cols = std::min(TN, N - c0);
+        const int64_t slot = ci++ % nc;
+        Slot& cs = sc[slot];
+        // cs.free is recorded after the store of the slot's previous tile (or
+        // at the start): nothing overwrites the slot before that
+        if (beta != 0.0f) {
+            PHOBOS_CHK(hipStreamWaitEvent(h2d, cs.free, 0));
+            PHOBOS_CHK(hipMemcpy2DAsync(cs.dev, ldc_t * sizeof(float), C + r0 * ldc + c0,
+                                        ldc * sizeof(float), cols * sizeof(float), rows,
+                                        hipMemcpyHostToDevice, h2d));
+            PHOBOS_CHK(hipEventRecord(cs.ready, h2d));
+            PHOBOS_CHK(hipStreamWaitEvent(comp, cs.ready, 0));
+        } else {
+            PHOBOS_CHK(hipStreamWaitEvent(comp, cs.free, 0));
         }
+        // init leaf, then one step leaf per K chunk
+        if (st == SGEMM_OK) st = phobos::host_launch_init(rows, cols, beta, cs.dev, ldc_t, comp);
+        for (int64_t kt = 0; kt < nk && st == SGEMM_OK; ++kt) {
+            const int64_t k0 = kt * TK, depth = std::min(TK, K - k0);
+            Slot* a = acquire(ta, sa, pm * nk + kt, A, lda, r0, k0, rows, depth, lda_t);
+            Slot* b = acquire(tb, sb, kt * gn + pn, B, ldb, k0, c0, depth, cols, ldb_t);
+            PHOBOS_CHK(hipStreamWaitEvent(comp, a->ready, 0));
+            PHOBOS_CHK(hipStreamWaitEvent(comp, b->ready, 0));
+            if (st != SGEMM_OK) break;
+            st = phobos::host_launch_gemm(rows, cols, depth, alpha, a->dev, lda_t, b->dev, ldb_t,
+                                          1.0f, cs.dev, ldc_t, comp);
+            PHOBOS_CHK(hipEventRecord(a->free, comp));
+            PHOBOS_CHK(hipEventRecord(b->free, comp));
+        }
+        // store the finished super-tile on the store stream
+        PHOBOS_CHK(hipEventRecord(c_done[slot], comp));
+        PHOBOS_CHK(hipStreamWaitEvent(d2h, c_done[slot], 0));
+        PHOBOS_CHK(hipMemcpy2DAsync(C + r0 * ldc + c0, ldc * sizeof(float), cs.dev,
+                                    ldc_t * sizeof(float), cols * sizeof(float), rows,
+                                    hipMemcpyDeviceToHost, d2h));
+        PHOBOS_CHK(hipEventRecord(cs.free, d2h));
     }
 #undef PHOBOS_CHK
     // the call returns with C complete in host memory; every stream is

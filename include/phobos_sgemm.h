@@ -169,55 +169,64 @@ int sgemm_tune(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_
  * block's loads are issued while the current one computes).  For products
  * whose operands live in host memory, e.g. larger than the GPU.
  *
- * sgemm_plan_supertiles chooses super-tile extents and device tile slots the
- * way the pages' cluster tuner plans ("@cluster" page, "What runs today",
- * Tuning): every candidate TM x TN x TK (powers of two from 256 below each
- * dimension, and the dimension itself) with A slots in {2, ceil(K/TK)} (the
- * latter keeps a row of A super-tiles resident across the row of outputs)
- * and B slots in {2, all of B}, and two C slots, is dropped if its device
- * buffers exceed `device_bytes`, and the rest are ranked by a model of
- * max(compute, loads, stores) time plus the first loads and last store, built
- * from `model` (NULL: 140 TFLOP/s GEMM rate, 50 GB/s each way host<->device;
- * loads and stores overlap).  Compute time
- * counts the rate scaled by how full a step launch keeps the 256 CUs
- * (ceil(TM/256)*ceil(TN/256) workgroups in waves of 256), 15 us per launch
- * and each launch's read and write of its C super-tile at 5 TB/s.  Nothing is
- * run.  Host-only.  Arguments: 1 M, 2 N, 3 K, 4 beta (0: C is only written),
- * 5 device_bytes, 6 model, 7 out.  SGEMM_ERR_BUDGET if nothing fits.
+ * sgemm_plan_supertiles chooses super-tile extents, device tile slots and the
+ * walk order the way the pages' cluster tuner plans ("@cluster" page, "What
+ * runs today", Tuning): every candidate TM x TN x TK (powers of two from 256
+ * below each dimension, and the dimension itself) with A slots in {2,
+ * ceil(K/TK), all of A}, B slots in {2, all of B} and two C slots, walked row
+ * by row (at most one row of A super-tiles kept) or, when all of A and B are
+ * kept, in growing squares (each shell brings one new row of A super-tiles
+ * and one new column of B super-tiles, which spreads the loads over the run),
+ * is dropped if its device buffers exceed `device_bytes`; the rest are ranked
+ * by a replay of the executor's schedule: the same walk and slot
+ * replacement, an in-order load stream, a store stream and the compute
+ * stream, with a step leaf taking 2*m*n*k at the GEMM rate scaled by how full
+ * it keeps the 256 CUs (ceil(m/256)*ceil(n/256) workgroups in waves of 256)
+ * plus 15 us and its C read and write at 5 TB/s, and a copy taking its bytes
+ * at the link rate plus 10 us, both directions together at most 1.7 times
+ * one direction.  `model` gives the rates (NULL: 140 TFLOP/s, 55 GB/s each
+ * way).  Nothing is run.  Host-only.  Arguments: 1 M, 2 N, 3 K, 4 beta (0: C
+ * is only written), 5 device_bytes, 6 model, 7 out.  SGEMM_ERR_BUDGET if
+ * nothing fits, SGEMM_ERR_TOO_LARGE for a dimension above 2^30; candidates
+ * with more than 2^20 step launches are not considered.
  *
  * sgemm_supertiled_host computes C <- alpha*A*B + beta*C with A, B and C in
  * host memory (row-major, leading dimensions as for sgemm; pinned memory,
  * e.g. hipHostMalloc'ed, gives full link speed) using `plan`.  It allocates
- * the plan's device slots, walks the super-tiles in row-major order: per
- * output super-tile load C (unless beta == 0), run the init leaf and the K
- * step leaves (the same kernels as sgemm_supertiled, so the result is bit for
- * bit that of sgemm_supertiled with the same extents on the same values),
- * store C.  A and B super-tiles are loaded into the least recently used slot
- * of their kind on a load stream of its own, which runs ahead of the compute
- * (`stream`) as far as free slots allow; C stores run on a store stream;
- * events order every load after the last compute or store that used its
- * slot.  Device slot pitches are the tile widths rounded up to 4 floats, each
- * slot starting on a 256-byte boundary; slot counts above the number of
- * distinct tiles of their kind are cut to it: for a plan that sgemm_plan_supertiles
- * returned for the same M, N, K and beta, at most the plan's `device_bytes`
- * are allocated.  Synchronous: returns once C is complete in host memory,
- * after freeing everything it allocated.  Arguments: 1..11 as sgemm (host
- * pointers), 12 plan, 13 stream.  Errors: negative argument index as sgemm
- * (-12: plan NULL or an extent or slot count below 1), SGEMM_ERR_TOO_LARGE,
- * SGEMM_ERR_ALLOC, or a HIP status; after a failure every stream is drained
- * and everything freed, and C may hold finished super-tiles next to
- * unchanged ones.
+ * the plan's device slots and walks the output super-tiles in the plan's
+ * order: per output super-tile load C (unless beta == 0), run the init leaf
+ * and the K step leaves (the same kernels as sgemm_supertiled, so the result
+ * is bit for bit that of sgemm_supertiled with the same extents on the same
+ * values), store C.  A and B super-tiles are loaded into the least recently
+ * used slot of their kind on a load stream of its own, which runs ahead of
+ * the compute (`stream`) as far as free slots allow; C stores run on a store
+ * stream; events order every load after the last compute or store that used
+ * its slot.  Device slot pitches are the tile widths rounded up to 4 floats,
+ * each slot starting on a 256-byte boundary; slot counts above the number of
+ * distinct tiles of their kind are cut to it: for a plan that
+ * sgemm_plan_supertiles returned for the same M, N, K and beta, at most the
+ * plan's `device_bytes` are allocated.  Synchronous: returns once C is
+ * complete in host memory, after freeing everything it allocated.
+ * Arguments: 1..11 as sgemm (host pointers), 12 plan, 13 stream.  Errors:
+ * negative argument index as sgemm (-12: plan NULL, an extent or slot count
+ * below 1, or an unknown walk), SGEMM_ERR_TOO_LARGE, SGEMM_ERR_ALLOC, or a
+ * HIP status; after a failure every stream is drained and everything freed,
+ * and C may hold finished super-tiles next to unchanged ones.
  */
 typedef struct sgemm_plan_model {
     double gemm_tflops;   /* sustained GEMM rate of one step leaf, TFLOP/s */
-    double link_gbs;      /* host<->device copy bandwidth, GB/s */
+    double link_gbs;      /* host<->device copy bandwidth of one direction, GB/s */
 } sgemm_plan_model;
+
+#define SGEMM_WALK_ROWS 0     /* output super-tiles row by row (the pages' order) */
+#define SGEMM_WALK_SHELLS 1   /* growing squares: shell s = tiles with max(pm, pn) == s */
 
 typedef struct sgemm_plan {
     int64_t TM, TN, TK;                /* super-tile extents */
     int32_t a_slots, b_slots, c_slots; /* device tile buffers of each kind */
+    int32_t walk;                      /* SGEMM_WALK_ROWS or SGEMM_WALK_SHELLS */
     int64_t device_bytes;              /* device memory the slots take */
-    double transfer_bytes;             /* modeled host<->device traffic */
+    double transfer_bytes;             /* host<->device bytes of the schedule */
     double modeled_ms;                 /* modeled time of the whole product */
 } sgemm_plan;
 

@@ -48,9 +48,14 @@ def test_plan_is_a_candidate_and_fits_the_budget(M, N, K):
             continue
         assert p.TM in _extents(M) and p.TN in _extents(N) and p.TK in _extents(K)
         gm, gn, nk = _cdiv(M, p.TM), _cdiv(N, p.TN), _cdiv(K, p.TK)
-        assert p.a_slots in (min(2, nk), nk)
+        assert p.a_slots in (min(2, nk), nk, gm * nk)
         assert p.b_slots in (min(2, nk), nk * gn)
         assert p.c_slots == min(2, gm * gn)
+        if p.walk == g.SGEMM_WALK_SHELLS:
+            # growing squares only when every A and B super-tile stays resident
+            assert p.a_slots == gm * nk and p.b_slots == nk * gn and gm > 1 and gn > 1
+        else:
+            assert p.walk == g.SGEMM_WALK_ROWS and p.a_slots <= nk
         # the slot bytes the executor allocates, within the budget
         assert p.device_bytes == _device_bytes(p) <= budget
         # host<->device bytes: A once or once per column of super-tiles, B
@@ -82,14 +87,28 @@ def test_plan_when_everything_fits_keeps_operands_resident():
     larger of compute and loads plus the pipeline's fill."""
     M = N = K = 16384
     p = g.sgemm_plan_supertiles(M, N, K, 1.0, 16 << 30)
-    nk, gn = _cdiv(K, p.TK), _cdiv(N, p.TN)
-    assert p.a_slots == nk and p.b_slots == nk * gn
+    gm, gn, nk = _cdiv(M, p.TM), _cdiv(N, p.TN), _cdiv(K, p.TK)
+    assert p.a_slots in (nk, gm * nk) and p.b_slots == nk * gn
     assert p.transfer_bytes == 4.0 * (M * K + K * N + 2 * M * N)
     # super-tiles large enough to fill the 256 CUs with 256x256 workgroup tiles
     assert _cdiv(p.TM, 256) * _cdiv(p.TN, 256) >= 256
     # a faster link moves the plan toward fewer, larger tiles, never slower
     q = g.sgemm_plan_supertiles(M, N, K, 1.0, 16 << 30, link_gbs=1e6)
     assert q.modeled_ms < p.modeled_ms
+
+
+def test_plan_struct_layout_matches_the_header():
+    import ctypes
+    assert ctypes.sizeof(g.sgemm_plan) == 64
+    assert g.sgemm_plan.device_bytes.offset == 40
+    assert g.sgemm_plan.walk.offset == 36
+
+
+def test_planner_prefers_shells_when_b_would_arrive_all_at_once():
+    """Everything resident, square grid: a row-major walk needs all of B during
+    the first row of outputs, growing squares spread the loads."""
+    p = g.sgemm_plan_supertiles(16384, 16384, 16384, 1.0, 16 << 30)
+    assert p.walk == g.SGEMM_WALK_SHELLS
 
 
 def test_plan_streams_when_memory_is_short():
@@ -125,9 +144,9 @@ def test_plan_argument_checks():
     assert (out.TM, out.TN, out.TK) == (4, 4, 4)
 
 
-def _plan(TM=64, TN=64, TK=64, a=2, b=2, c=2):
+def _plan(TM=64, TN=64, TK=64, a=2, b=2, c=2, walk=0):
     p = g.sgemm_plan()
-    p.TM, p.TN, p.TK, p.a_slots, p.b_slots, p.c_slots = TM, TN, TK, a, b, c
+    p.TM, p.TN, p.TK, p.a_slots, p.b_slots, p.c_slots, p.walk = TM, TN, TK, a, b, c, walk
     return p
 
 
@@ -155,7 +174,7 @@ def test_host_executor_argument_checks(args, want):
 
 
 @pytest.mark.parametrize("plan", [None, _plan(TM=0), _plan(TN=-1), _plan(TK=0), _plan(a=0),
-                                  _plan(b=0), _plan(c=0)])
+                                  _plan(b=0), _plan(c=0), _plan(walk=2), _plan(walk=-1)])
 def test_host_executor_plan_checks(plan):
     assert g.sgemm_supertiled_host_raw(4, 4, 4, 1.0, 8, 4, 8, 4, 1.0, 8, 4, plan,
                                        stream=0) == -12

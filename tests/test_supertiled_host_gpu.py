@@ -14,9 +14,9 @@ from tests import gpu_util as gu
 pytestmark = pytest.mark.gpu
 
 
-def _plan(TM, TN, TK, a, b, c):
+def _plan(TM, TN, TK, a, b, c, walk=g.SGEMM_WALK_ROWS):
     p = g.sgemm_plan()
-    p.TM, p.TN, p.TK, p.a_slots, p.b_slots, p.c_slots = TM, TN, TK, a, b, c
+    p.TM, p.TN, p.TK, p.a_slots, p.b_slots, p.c_slots, p.walk = TM, TN, TK, a, b, c, walk
     return p
 
 
@@ -54,26 +54,32 @@ def _check(w, x, plan, **kw):
     return out
 
 
-# (M, N, K), (TM, TN, TK), slots a/b/c, alpha, beta
+ROWS, SHELLS = g.SGEMM_WALK_ROWS, g.SGEMM_WALK_SHELLS
+
+# (M, N, K), (TM, TN, TK), slots a/b/c, walk, alpha, beta
 CASES = [
-    ((300, 270, 200), (128, 128, 64), (2, 2, 2), 1.5, 0.5),     # A and B evicted and re-loaded
-    ((300, 270, 200), (128, 128, 64), (4, 12, 1), 1.0, 1.0),    # resident A row and B; one C slot
-    ((129, 65, 300), (1000, 1000, 64), (2, 2, 2), 1.0, 0.0),    # one super-tile, beta = 0
-    ((100, 90, 70), (48, 40, 7), (1, 1, 1), 1.0, -1.0),         # one slot each; TK % 4 != 0
-    ((64, 70, 40), (64, 64, 1), (2, 3, 2), 2.0, 0.5),           # one k per step: 40 steps
-    ((513, 515, 260), (256, 256, 256), (1, 2, 2), -0.5, 2.0),   # ragged tiles on every axis
+    ((300, 270, 200), (128, 128, 64), (2, 2, 2), ROWS, 1.5, 0.5),    # A, B evicted and re-loaded
+    ((300, 270, 200), (128, 128, 64), (4, 12, 1), ROWS, 1.0, 1.0),   # resident A row and B; 1 C slot
+    ((129, 65, 300), (1000, 1000, 64), (2, 2, 2), ROWS, 1.0, 0.0),   # one super-tile, beta = 0
+    ((100, 90, 70), (48, 40, 7), (1, 1, 1), ROWS, 1.0, -1.0),        # one slot each; TK % 4 != 0
+    ((64, 70, 40), (64, 64, 1), (2, 3, 2), ROWS, 2.0, 0.5),          # one k per step: 40 steps
+    ((513, 515, 260), (256, 256, 256), (1, 2, 2), ROWS, -0.5, 2.0),  # ragged tiles on every axis
+    ((300, 270, 200), (128, 128, 64), (12, 12, 2), SHELLS, 1.5, 0.5),  # 3x3 grid in shells
+    ((500, 200, 130), (96, 64, 64), (18, 12, 2), SHELLS, 1.0, 0.0),    # 6x4 grid: rows past the square
+    ((200, 500, 130), (64, 96, 64), (12, 18, 1), SHELLS, 1.0, 1.0),    # 4x6: columns past the square
+    ((300, 270, 200), (128, 128, 64), (2, 2, 2), SHELLS, 2.0, -1.0),   # shells with evictions
 ]
 
 
-@pytest.mark.parametrize("shape,tiles,slots,alpha,beta", CASES)
-def test_host_executor_matches_device_and_oracle(shape, tiles, slots, alpha, beta):
+@pytest.mark.parametrize("shape,tiles,slots,walk,alpha,beta", CASES)
+def test_host_executor_matches_device_and_oracle(shape, tiles, slots, walk, alpha, beta):
     M, N, K = shape
-    print(f"host executor {shape} tiles {tiles} slots {slots}", flush=True)
+    print(f"host executor {shape} tiles {tiles} slots {slots} walk {walk}", flush=True)
     cdist = "NaN" if beta == 0 else "U"
     w = wl.custom(M, N, K, alpha, beta, ("U", "U", cdist), seed=M + N + K, lda=K + 4,
                   ldb=N + 2, ldc=N + 6)
     x = wl.make_inputs(w)
-    plan = _plan(*tiles, *slots)
+    plan = _plan(*tiles, *slots, walk=walk)
     out = _check(w, x, plan)
     gu.check_full(w, x, out, steps=_steps(K, tiles[2]), relaxed=True)
     wi = w.integer_variant()
@@ -130,7 +136,7 @@ def test_host_executor_planned_small_budget():
     gu.check_full(w, x, out, steps=_steps(w.K, plan.TK), relaxed=True)
 
 
-@pytest.mark.parametrize("budget", [2 << 30, 256 << 20])
+@pytest.mark.parametrize("budget", [16 << 30, 2 << 30, 256 << 20])
 def test_host_executor_16384(budget):
     """The 16384^3 product from host memory with the planner's plan: bit for
     bit the device-resident super-tiled result with the same extents, sampled
