@@ -1,4 +1,5 @@
-"""CPU oracle for C = alpha*A*B + beta*C (test infrastructure only).
+"""CPU oracle for C = alpha*A*B + beta*C (test infrastructure only), and for its
+matrix-core variant with A and B rounded to fp16 or bf16 first.
 
 Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package.  The GPU library and its Python binding
@@ -68,6 +69,12 @@ class Oracle:
         lib.oracle_sgemm_entries.argtypes = [i64, i64, i64, f32, vp, i64, vp, i64, f32,
                                              vp, i64, i64, vp, vp, vp, vp]
         lib.oracle_sgemm_entries.restype = ctypes.c_int
+        lib.oracle_round.argtypes = [ctypes.c_int, i64, vp, vp]
+        lib.oracle_round.restype = ctypes.c_int
+        lib.oracle_sgemm_tc.argtypes = [ctypes.c_int] + lib.oracle_sgemm.argtypes
+        lib.oracle_sgemm_tc.restype = ctypes.c_int
+        lib.oracle_sgemm_tc_entries.argtypes = [ctypes.c_int] + lib.oracle_sgemm_entries.argtypes
+        lib.oracle_sgemm_tc_entries.restype = ctypes.c_int
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = ctypes.c_int
         self.lib = lib
@@ -77,9 +84,21 @@ class Oracle:
         """Number of OpenMP threads the full-matrix routine runs on."""
         return int(self.lib.oracle_max_threads())
 
+    def round(self, fmt, x):
+        """x (float32 values) rounded to format fmt (F16 or BF16), as float32."""
+        a = np.ascontiguousarray(x, dtype=np.float32)
+        out = np.empty_like(a)
+        rc = self.lib.oracle_round(int(fmt), a.size, _ptr(a), _ptr(out))
+        if rc != 0:
+            raise RuntimeError(f"oracle_round failed with code {rc}")
+        return out
+
     def sgemm(self, M, N, K, alpha, A, B, beta, C, lda=None, ldb=None, ldc=None,
-              bound=True):
-        """Reference C_ref (float32, M x N) and bound (float64, M x N, or None)."""
+              bound=True, fmt=None):
+        """Reference C_ref (float32, M x N) and bound (float64, M x N, or None).
+
+        fmt (F16 or BF16): the matrix-core variant, A and B rounded to that
+        format first; None: the fp32 product."""
         lda = _ld_of(A, K) if lda is None else lda
         ldb = _ld_of(B, N) if ldb is None else ldb
         ldc = _ld_of(C, N) if ldc is None else ldc
@@ -88,16 +107,18 @@ class Oracle:
         c = _buf(C, M, N, ldc, "C") if beta != 0 else None
         out = np.empty((M, N), dtype=np.float32)
         bnd = np.empty((M, N), dtype=np.float64) if bound else None
-        rc = self.lib.oracle_sgemm(M, N, K, float(alpha), _ptr(a), lda, _ptr(b), ldb,
-                                   float(beta), _ptr(c), ldc, _ptr(out), max(N, 1),
-                                   _ptr(bnd), max(N, 1))
+        args = (M, N, K, float(alpha), _ptr(a), lda, _ptr(b), ldb, float(beta), _ptr(c), ldc,
+                _ptr(out), max(N, 1), _ptr(bnd), max(N, 1))
+        rc = (self.lib.oracle_sgemm(*args) if fmt is None
+              else self.lib.oracle_sgemm_tc(int(fmt), *args))
         if rc != 0:
             raise RuntimeError(f"oracle_sgemm failed with code {rc}")
         return out, bnd
 
     def sgemm_entries(self, M, N, K, alpha, A, B, beta, C, rows, cols, lda=None,
-                      ldb=None, ldc=None):
-        """Reference values and bounds at the entries (rows[t], cols[t])."""
+                      ldb=None, ldc=None, fmt=None):
+        """Reference values and bounds at the entries (rows[t], cols[t]); fmt as
+        for sgemm."""
         lda = _ld_of(A, K) if lda is None else lda
         ldb = _ld_of(B, N) if ldb is None else ldb
         ldc = _ld_of(C, N) if ldc is None else ldc
@@ -110,13 +131,18 @@ class Oracle:
             raise ValueError("rows and cols differ in length")
         out = np.empty(r.size, dtype=np.float32)
         bnd = np.empty(r.size, dtype=np.float64)
-        rc = self.lib.oracle_sgemm_entries(M, N, K, float(alpha), _ptr(a), lda, _ptr(b),
-                                           ldb, float(beta), _ptr(c), ldc, r.size, _ptr(r),
-                                           _ptr(q), _ptr(out), _ptr(bnd))
+        args = (M, N, K, float(alpha), _ptr(a), lda, _ptr(b), ldb, float(beta), _ptr(c), ldc,
+                r.size, _ptr(r), _ptr(q), _ptr(out), _ptr(bnd))
+        rc = (self.lib.oracle_sgemm_entries(*args) if fmt is None
+              else self.lib.oracle_sgemm_tc_entries(int(fmt), *args))
         if rc != 0:
             raise RuntimeError(f"oracle_sgemm_entries failed with code {rc}")
         return out, bnd
 
+
+# Input formats of the matrix-core variant.
+F16 = 1
+BF16 = 2
 
 _default = None
 
@@ -139,3 +165,7 @@ def sgemm(*args, **kwargs):
 
 def sgemm_entries(*args, **kwargs):
     return default().sgemm_entries(*args, **kwargs)
+
+
+def round_to(fmt, x):
+    return default().round(fmt, x)

@@ -8,7 +8,11 @@ AssertionError when the oracle disagrees with:
     operands, alpha = 0, beta = 0 with a NaN C, A = 0, K = 0, all-ones),
   - exact integer matrix products (numpy int64),
   - an independent fp64 library product (numpy float64 matmul),
-  - the bound's formula evaluated exactly.
+  - the bound's formula evaluated exactly,
+and, for the matrix-core variant (inputs rounded to fp16 or bf16 first):
+  - hand-worked roundings (tests/golden/round16.txt),
+  - numpy's binary16 conversion and the bfloat16 bit rule,
+  - exact rational products of the rounded inputs.
 The definition being pinned is the one the Phobos blog states ("Show HN:
 Phobos", section "Matrix Multiplication": C = alpha*A*B + beta*C in 32-bit
 floats) and the naive SGEMM it quotes (section "Introducing the Phobos
@@ -299,6 +303,119 @@ def check_entries(orc):
     np.testing.assert_allclose(gb, wb, rtol=1e-12, atol=0)
 
 
+# --------------------------------------------------------------------------
+# The matrix-core variant: A and B rounded to fp16 or bf16, then the product.
+F16, BF16 = 1, 2
+
+
+def round16_ref(fmt, x):
+    """Rounding by routes independent of the oracle: numpy's binary16
+    conversion, and for bfloat16 the bit rule on the fp32 encoding (add
+    0x7FFF plus the lowest kept bit, then drop the low 16 bits), which is
+    round to nearest even on the top 16 bits and overflows into the
+    infinity encoding; NaN stays NaN."""
+    x = np.asarray(x, np.float32)
+    if fmt == F16:
+        with np.errstate(over="ignore"):
+            return x.astype(np.float16).astype(np.float32)
+    b = x.view(np.uint32).astype(np.uint64)
+    r = (((b + 0x7FFF + ((b >> 16) & 1)) >> 16) << 16).astype(np.uint32).view(np.float32)
+    return np.where(np.isnan(x), x, r)
+
+
+def _same_bits(a, b):
+    a, b = np.asarray(a, np.float32), np.asarray(b, np.float32)
+    return np.array_equal(np.isnan(a), np.isnan(b)) and np.array_equal(
+        a[~np.isnan(a)].view(np.int32), b[~np.isnan(b)].view(np.int32))
+
+
+def load_round_golden():
+    rows = []
+    with open(os.path.join(GOLDEN, "round16.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if not line:
+                continue
+            fmt, x, want = line.split()[:3]
+            rows.append(({"f16": F16, "bf16": BF16}[fmt], float.fromhex(x), float(want)
+                         if want.lstrip("-") == "inf" else float.fromhex(want)))
+    return rows
+
+
+def check_round_golden(orc):
+    """Hand-worked roundings (ties, carries, subnormals, overflow)."""
+    for fmt, x, want in load_round_golden():
+        got = orc.round(fmt, np.array([x], np.float32))[0]
+        assert _same_bits([got], [want]), (fmt, x.hex(), float(got).hex(), want)
+
+
+def check_round_libraries(orc):
+    """Many values, all binades and random encodings, against round16_ref."""
+    rng = _rng(11)
+    e = rng.uniform(-150, 128, 40000)
+    v = (np.sign(rng.uniform(-1, 1, e.size)) * rng.uniform(1, 2, e.size) * 2.0 ** e)
+    bits = rng.integers(0, 2 ** 32, 40000, dtype=np.uint64).astype(np.uint32)
+    with np.errstate(over="ignore"):
+        v = np.concatenate([v.astype(np.float32), bits.view(np.float32),
+                            rng.uniform(-1, 1, 20000).astype(np.float32)])
+    for fmt in (F16, BF16):
+        assert _same_bits(orc.round(fmt, v), round16_ref(fmt, v)), fmt
+
+
+def check_tc_exact(orc):
+    """The variant on random fp32 inputs: within 1 ulp of RN32 of the exact
+    product of the rounded inputs, almost always equal, and the bound is the
+    fp32 rule on the rounded inputs."""
+    rng = _rng(12)
+    total = equal = 0
+    for fmt in (F16, BF16):
+        for M, N, K in [(3, 4, 5), (5, 3, 19)]:
+            for alpha, beta in [(1.3, -0.7), (0.5, 0.0)]:
+                A = rng.uniform(-1, 1, (M, K)).astype(np.float32)
+                B = rng.standard_normal((K, N)).astype(np.float32)
+                C = rng.uniform(-1, 1, (M, N)).astype(np.float32)
+                got, bnd = orc.sgemm(M, N, K, alpha, A, B, beta, C, fmt=fmt)
+                Ar, Br = round16_ref(fmt, A), round16_ref(fmt, B)
+                ex, absum = exact_product(M, N, K, alpha, Ar, Br, beta, C)
+                want = np.array([[rn32(v) for v in r] for r in ex], dtype=np.float32)
+                d = ulp_diff(got, want)
+                assert d.max() <= 1, (fmt, (M, N, K), d.max())
+                total += d.size
+                equal += int((d == 0).sum())
+                wb = np.array([[exact_bound(K, alpha, beta, absum[i][j], C[i, j])
+                                for j in range(N)] for i in range(M)])
+                np.testing.assert_allclose(bnd, wb, rtol=1e-13, atol=0)
+    assert equal >= 0.97 * total, (equal, total)
+
+
+def check_tc_representable(orc):
+    """Inputs that both formats hold exactly (integers -3..3): the variant is
+    the fp32 product, bit for bit, and equals the exact integer result."""
+    rng = _rng(13)
+    M, N, K = 20, 17, 300
+    A = rng.integers(-3, 4, (M, K)).astype(np.float32)
+    B = rng.integers(-3, 4, (K, N)).astype(np.float32)
+    C = rng.integers(-3, 4, (M, N)).astype(np.float32)
+    want = (A.astype(np.int64) @ B.astype(np.int64) * 2 + C.astype(np.int64)).astype(np.float32)
+    for fmt in (F16, BF16):
+        got, _ = orc.sgemm(M, N, K, 2.0, A, B, 1.0, C, fmt=fmt)
+        assert np.array_equal(got, want), fmt
+
+
+def check_tc_entries(orc):
+    """The variant's per-entry routine equals its full routine."""
+    w = wl.custom(90, 70, 700, -1.5, 0.5, seed=14, lda=703, ldb=71, ldc=75)
+    x = wl.make_inputs(w)
+    r, c = wl.sample_entries(w, 300)
+    for fmt in (F16, BF16):
+        full, fb = orc.sgemm(w.M, w.N, w.K, w.alpha, x.A, x.B, w.beta, x.C,
+                             lda=w.lda, ldb=w.ldb, ldc=w.ldc, fmt=fmt)
+        got, gb = orc.sgemm_entries(w.M, w.N, w.K, w.alpha, x.A, x.B, w.beta, x.C, r, c,
+                                    lda=w.lda, ldb=w.ldb, ldc=w.ldc, fmt=fmt)
+        assert np.array_equal(got, full[r, c]) and np.array_equal(gb, fb[r, c]), fmt
+
+
 ALL_CHECKS = [check_golden, check_exact_dyadic, check_exact_general,
               check_bound_covers_fp32_loop, check_closed_forms, check_integer_exact,
-              check_numpy_fp64, check_entries]
+              check_numpy_fp64, check_entries, check_round_golden, check_round_libraries,
+              check_tc_exact, check_tc_representable, check_tc_entries]

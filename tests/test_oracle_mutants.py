@@ -47,8 +47,25 @@ MUTANTS = [
      "const double a = (double)A[i * K + k];"),
     ("alpha_scales_by_beta", "double t = (double)alpha * sum;", "double t = (double)beta * sum;"),
     ("entries_transposed_B", "(double)B[k * ldb + j];", "(double)B[j * ldb + k];"),
-    ("entries_drop_beta", "        out[t] = finish(alpha, beta, s, c);",
-     "        out[t] = finish(alpha, 0.0f, s, c);"),
+    ("entries_drop_beta", "        out[t] = finish(alpha, beta, s, c);\n        if (bnd) bnd[t] = bound_of(K, alpha, beta, sa, c);\n    }\n    return 0;\n}\n\n/*\n * Matrix-core",
+     "        out[t] = finish(alpha, 0.0f, s, c);\n        if (bnd) bnd[t] = bound_of(K, alpha, beta, sa, c);\n    }\n    return 0;\n}\n\n/*\n * Matrix-core"),
+    # the matrix-core variant
+    ("round_ties_away", "nearbyint((double)x / q)", "round((double)x / q)"),
+    ("round_truncates", "nearbyint((double)x / q)", "trunc((double)x / q)"),
+    ("f16_one_bit_short", "round_to_format(x, 11, -14, 65504.0)",
+     "round_to_format(x, 10, -14, 65504.0)"),
+    ("no_subnormal_spacing", "if (lead < emin) lead = emin;", ""),
+    ("no_overflow_to_inf", "if (fabs(r) > max) return copysign(INFINITY, (double)x);", ""),
+    ("exponent_off_by_one", "int lead = e - 1; ", "int lead = e; "),
+    ("bf16_rounded_as_f16", "return round_to_format(x, 8, -126, ldexp(255.0, 120));",
+     "return round_to_format(x, 11, -14, 65504.0);"),
+    ("A_not_rounded", "Ar[i * K + k] = (float)round_fmt(fmt, A[i * lda + k]);",
+     "Ar[i * K + k] = A[i * lda + k];"),
+    ("B_not_rounded", "Br[k * N + j] = (float)round_fmt(fmt, B[k * ldb + j]);",
+     "Br[k * N + j] = B[k * ldb + j];"),
+    ("tc_entries_not_rounded",
+     "round_fmt(fmt, A[i * lda + k]) * round_fmt(fmt, B[k * ldb + j])",
+     "(double)A[i * lda + k] * (double)B[k * ldb + j]"),
 ]
 
 RUNNER = r"""
