@@ -28,6 +28,9 @@ SGEMM_WALK_ROWS = 0
 SGEMM_WALK_SHELLS = 1
 SGEMM_KIND_GEMM = 0
 SGEMM_KIND_INIT_LEAF = 1
+SGEMM_KIND_TC = 2
+SGEMM_TC_F16 = 1
+SGEMM_TC_BF16 = 2
 
 
 class SgemmError(RuntimeError):
@@ -83,6 +86,12 @@ _SIGNATURES = {
                               ctypes.c_int),
     "sgemm_tune": ([_i64, _i64, _i64, _i64, _i64, _i64, _i32, _vp,
                     ctypes.POINTER(sgemm_config), ctypes.POINTER(_f32)], ctypes.c_int),
+    "sgemm_tc": ([_i64, _i64, _i64, _f32, _vp, _i64, _vp, _i64, _f32, _vp, _i64, _i32, _vp],
+                 ctypes.c_int),
+    "sgemm_tc_config_count": ([_i32], ctypes.c_int),
+    "sgemm_tc_config_at": ([_i32, _i32, ctypes.POINTER(sgemm_config)], ctypes.c_int),
+    "sgemm_tc_get_config": ([_i32, _i64, _i64, ctypes.POINTER(sgemm_config)], ctypes.c_int),
+    "sgemm_tc_set_config": ([_i32, ctypes.POINTER(sgemm_config)], ctypes.c_int),
     "sgemm_plan_supertiles": ([_i64, _i64, _i64, _f32, _i64, ctypes.POINTER(sgemm_plan_model),
                                ctypes.POINTER(sgemm_plan)], ctypes.c_int),
     "sgemm_supertiled_host": ([_i64, _i64, _i64, _f32, _vp, _i64, _vp, _i64, _f32, _vp, _i64,
@@ -165,6 +174,42 @@ def sgemm_supertiled(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, TM, TN, TK, s
 def sgemm_init_leaf(M, N, beta, C, ldc, stream=None):
     """C <- beta*C (C <- 0 without reading C when beta == 0)."""
     _check(lib().sgemm_init_leaf(M, N, beta, _ptr(C), ldc, _stream(stream)), "sgemm_init_leaf")
+
+
+def sgemm_tc_raw(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, fmt, stream=None):
+    return lib().sgemm_tc(M, N, K, alpha, _ptr(A), lda, _ptr(B), ldb, beta, _ptr(C), ldc, fmt,
+                          _stream(stream))
+
+
+def sgemm_tc(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, fmt=None, stream=None):
+    """C <- alpha*A'*B' + beta*C with A, B rounded to fp16 (fmt SGEMM_TC_F16,
+    the default) or bf16 (SGEMM_TC_BF16) on load, fp32 accumulation."""
+    fmt = SGEMM_TC_F16 if fmt is None else fmt
+    _check(sgemm_tc_raw(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, fmt, stream), "sgemm_tc")
+
+
+def tc_configs(fmt):
+    """The compiled configurations of the matrix-core variant for one format."""
+    out = []
+    for i in range(lib().sgemm_tc_config_count(fmt)):
+        c = sgemm_config()
+        _check(lib().sgemm_tc_config_at(fmt, i, ctypes.byref(c)), "sgemm_tc_config_at")
+        out.append(c)
+    return out
+
+
+def sgemm_tc_get_config(fmt, M, N):
+    c = sgemm_config()
+    _check(lib().sgemm_tc_get_config(fmt, M, N, ctypes.byref(c)), "sgemm_tc_get_config")
+    return c
+
+
+def sgemm_tc_set_config(fmt, cfg):
+    """Force one matrix-core configuration for format fmt (None clears)."""
+    if cfg is not None and not isinstance(cfg, sgemm_config):
+        cfg = sgemm_config(*cfg)
+    _check(lib().sgemm_tc_set_config(fmt, None if cfg is None else ctypes.byref(cfg)),
+           "sgemm_tc_set_config")
 
 
 def configs():

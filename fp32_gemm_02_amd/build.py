@@ -12,6 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libphobos_sgemm.so")
 SOURCES = [os.path.join(HERE, "csrc", "sgemm_kernels.hip"),
+           os.path.join(HERE, "csrc", "sgemm_tc.hip"),
            os.path.join(HERE, "csrc", "sgemm_api.cpp"),
            os.path.join(HERE, "csrc", "sgemm_host.cpp")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -156,11 +156,11 @@ struct TraceScope {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-// One GEMM launch on already-validated arguments (M, N, K > 0, alpha != 0).
-int launch_gemm(int entry, int64_t M, int64_t N, int64_t K, float alpha, const float* A,
-                int64_t lda, const float* B, int64_t ldb, float beta, float* C, int64_t ldc,
-                hipStream_t stream) {
-    const KernelEntry& e = kKernelTable[entry];
+// One launch of kernel entry `e` on already-validated arguments (M, N, K > 0,
+// alpha != 0), traced as `kind`.
+int launch_entry(const KernelEntry& e, int32_t kind, int64_t M, int64_t N, int64_t K,
+                 float alpha, const float* A, int64_t lda, const float* B, int64_t ldb,
+                 float beta, float* C, int64_t ldc, hipStream_t stream) {
     GemmArgs p{};
     p.M = (int32_t)M;
     p.N = (int32_t)N;
@@ -182,9 +182,54 @@ int launch_gemm(int entry, int64_t M, int64_t N, int64_t K, float alpha, const f
     p.xcd_remap = ((tm * tn) % 8 == 0 && env_int("SGEMM_XCD_REMAP", 1) != 0) ? 1 : 0;
     const bool vec = aligned16(A) && aligned16(B) && aligned16(C) && lda % 4 == 0 &&
                      ldb % 4 == 0 && ldc % 4 == 0;
-    TraceScope ts(stream, SGEMM_KIND_GEMM);
+    TraceScope ts(stream, kind);
     const hipError_t err = vec ? e.vec4(p, stream) : e.scalar(p, stream);
     return hip_status(err);
+}
+
+int launch_gemm(int entry, int64_t M, int64_t N, int64_t K, float alpha, const float* A,
+                int64_t lda, const float* B, int64_t ldb, float beta, float* C, int64_t ldc,
+                hipStream_t stream) {
+    return launch_entry(kKernelTable[entry], SGEMM_KIND_GEMM, M, N, K, alpha, A, lda, B, ldb,
+                        beta, C, ldc, stream);
+}
+
+// ---- matrix-core variant: one kernel table per input format ----
+struct TcTable {
+    const KernelEntry* entries[3] = {nullptr, nullptr, nullptr};
+    int count[3] = {0, 0, 0};
+    TcTable() {
+        for (int f : {SGEMM_TC_F16, SGEMM_TC_BF16}) entries[f] = phobos::tc_kernel_table(f, &count[f]);
+    }
+};
+const TcTable& tc_table() {
+    static const TcTable t;
+    return t;
+}
+bool tc_fmt_ok(int32_t fmt) { return fmt == SGEMM_TC_F16 || fmt == SGEMM_TC_BF16; }
+int g_tc_forced[3] = {-1, -1, -1};   // per format: index into its table, or -1 (g_mu)
+
+int tc_find(int32_t fmt, const sgemm_config& c) {
+    const TcTable& t = tc_table();
+    for (int i = 0; i < t.count[fmt]; ++i)
+        if (same_cfg(t.entries[fmt][i].cfg, c)) return i;
+    return -1;
+}
+
+// Forced, else the largest tile that still gives every CU work (the same
+// rule as the fp32 default), else small tiles.
+int tc_choose(int32_t fmt, int64_t M, int64_t N) {
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        if (g_tc_forced[fmt] >= 0) return g_tc_forced[fmt];
+    }
+    static const int order[][4] = {{256, 256, 2, 2}, {256, 128, 2, 2}, {128, 128, 2, 2},
+                                   {128, 64, 2, 1}};
+    for (const auto& o : order) {
+        const int64_t tiles = ((M + o[0] - 1) / o[0]) * ((N + o[1] - 1) / o[1]);
+        if (tiles >= 256) return tc_find(fmt, sgemm_config{o[0], o[1], 32, o[2], o[3]});
+    }
+    return tc_find(fmt, sgemm_config{64, 64, 32, 1, 1});
 }
 
 int launch_init(int64_t M, int64_t N, float beta, float* C, int64_t ldc, hipStream_t stream) {
@@ -287,6 +332,55 @@ int sgemm_init_leaf(int64_t M, int64_t N, float beta, float* C, int64_t ldc, voi
     if (M == 0 || N == 0) return SGEMM_OK;
     if (C == nullptr) return -4;
     return launch_init(M, N, beta, C, ldc, reinterpret_cast<hipStream_t>(stream));
+}
+
+int sgemm_tc(int64_t M, int64_t N, int64_t K, float alpha, const float* A, int64_t lda,
+             const float* B, int64_t ldb, float beta, float* C, int64_t ldc, int32_t fmt,
+             void* stream) {
+    const int st = check_gemm_args(M, N, K, alpha, A, lda, B, ldb, C, ldc);
+    if (st != SGEMM_OK) return st;
+    if (!tc_fmt_ok(fmt)) return -12;
+    if (M == 0 || N == 0) return SGEMM_OK;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (K == 0 || alpha == 0.0f) return launch_init(M, N, beta, C, ldc, s);
+    const int e = tc_choose(fmt, M, N);
+    if (e < 0) return SGEMM_ERR_NO_CONFIG;
+    return launch_entry(tc_table().entries[fmt][e], SGEMM_KIND_TC, M, N, K, alpha, A, lda, B,
+                        ldb, beta, C, ldc, s);
+}
+
+int sgemm_tc_config_count(int32_t fmt) { return tc_fmt_ok(fmt) ? tc_table().count[fmt] : -1; }
+
+int sgemm_tc_config_at(int32_t fmt, int32_t index, sgemm_config* out) {
+    if (!tc_fmt_ok(fmt)) return -1;
+    if (index < 0 || index >= tc_table().count[fmt]) return -2;
+    if (out == nullptr) return -3;
+    *out = tc_table().entries[fmt][index].cfg;
+    return SGEMM_OK;
+}
+
+int sgemm_tc_get_config(int32_t fmt, int64_t M, int64_t N, sgemm_config* out) {
+    if (!tc_fmt_ok(fmt)) return -1;
+    if (M < 0) return -2;
+    if (N < 0) return -3;
+    if (out == nullptr) return -4;
+    const int e = tc_choose(fmt, M, N);
+    if (e < 0) return SGEMM_ERR_NO_CONFIG;
+    *out = tc_table().entries[fmt][e].cfg;
+    return SGEMM_OK;
+}
+
+int sgemm_tc_set_config(int32_t fmt, const sgemm_config* cfg) {
+    if (!tc_fmt_ok(fmt)) return -1;
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (cfg == nullptr) {
+        g_tc_forced[fmt] = -1;
+        return SGEMM_OK;
+    }
+    const int e = tc_find(fmt, *cfg);
+    if (e < 0) return SGEMM_ERR_NO_CONFIG;
+    g_tc_forced[fmt] = e;
+    return SGEMM_OK;
 }
 
 int sgemm_config_count(void) { return kKernelCount; }

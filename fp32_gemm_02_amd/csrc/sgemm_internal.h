@@ -38,6 +38,10 @@ struct KernelEntry {
 // The compiled configurations (count written to *count).
 const KernelEntry* kernel_table(int* count);
 
+// The compiled configurations of the matrix-core variant for input format
+// fmt (SGEMM_TC_F16 or SGEMM_TC_BF16); nullptr and *count = 0 otherwise.
+const KernelEntry* tc_kernel_table(int fmt, int* count);
+
 // C <- beta*C over an M x N view (beta == 0: C <- 0 without reading C).
 hipError_t launch_init_leaf(int64_t M, int64_t N, float beta, float* C, int64_t ldc,
                             hipStream_t stream);

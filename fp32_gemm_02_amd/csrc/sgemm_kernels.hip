@@ -42,6 +42,7 @@
 
 #include <type_traits>
 
+#include "sgemm_device.h"
 #include "sgemm_internal.h"
 
 // The direct global-to-LDS loads of a stage are issued spread over its first
@@ -59,9 +60,6 @@
 
 namespace phobos {
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // NB consecutive floats of B read with one LDS instruction, and element n of it.
 template <int NB> struct BVec;
@@ -98,18 +96,6 @@ template <int N>
 constexpr int kWaitVm = (N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8);
 static_assert(kWaitVm<0> == 0x70 && kWaitVm<4> == 0x74, "s_waitcnt encoding");
 
-// XOR swizzle of the 16-byte pieces of one A-tile row in LDS (QA pieces per
-// row): piece q of row r is stored at position q ^ swz(r).  It depends on
-// r mod 16 only.  For the MFMA reads (32 rows, one piece each) any 8
-// consecutive lanes then touch 8 different 16-byte bank groups of a 128-byte
-// line, and any 16 consecutive lanes 16 different groups of a 256-byte line,
-// so the reads are conflict free whether the LDS serves 8 or 16 lanes of a
-// 128-bit read per cycle.
-template <int QA>
-__device__ __forceinline__ int swz(int r) {
-    if constexpr (QA == 8) return (r & 7) ^ ((r >> 3) & 1);
-    else return ((r >> 1) & 3) ^ ((r >> 3) & 1);
-}
 
 template <int BM, int BN, int BK, int WM, int WN>
 struct TileShape {
@@ -141,42 +127,6 @@ struct TileShape {
                   "whole direct loads per wave");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS of one CU");
 };
-
-// Map the workgroup to its output tile.  Workgroups are handed to the 8 XCDs
-// of the chip round robin (id % 8); with xcd_remap the ids an XCD receives
-// become one contiguous run of the raster order, so tiles that share rows of
-// A and columns of B sit in the same L2.  The raster walks group_m tile rows
-// at a time, column by column, to keep the A panels of a group hot.
-__device__ __forceinline__ void tile_of(const GemmArgs& p, int& tm, int& tn) {
-    int bid = blockIdx.x;
-    if (p.xcd_remap) {
-        const int per = (p.tiles_m * p.tiles_n) >> 3;
-        bid = (bid & 7) * per + (bid >> 3);
-    }
-    const int group = p.group_m * p.tiles_n;
-    const int g = bid / group;
-    const int first = g * p.group_m;
-    const int gsz = min(p.tiles_m - first, p.group_m);
-    const int r = bid - g * group;
-    tm = first + r % gsz;
-    tn = r / gsz;
-}
-
-// Load 4 consecutive floats src[0..3] whose positions are valid while
-// e < nvalid (nvalid <= 0: all zero).  VEC: src is 16-byte aligned.
-template <bool VEC>
-__device__ __forceinline__ f32x4 load4(const float* src, int nvalid) {
-    f32x4 v;
-    if (VEC && nvalid >= 4) {
-        v = *reinterpret_cast<const f32x4*>(src);
-    } else {
-        v[0] = nvalid > 0 ? src[0] : 0.0f;
-        v[1] = nvalid > 1 ? src[1] : 0.0f;
-        v[2] = nvalid > 2 ? src[2] : 0.0f;
-        v[3] = nvalid > 3 ? src[3] : 0.0f;
-    }
-    return v;
-}
 
 template <int BM, int BN, int BK, int WM, int WN, bool VEC>
 __global__ __launch_bounds__(64 * WM * WN) void sgemm_mfma_kernel(GemmArgs p) {

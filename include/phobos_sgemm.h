@@ -161,6 +161,45 @@ int sgemm_tune(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_
                int32_t reps, void* stream, sgemm_config* winner, float* winner_ms);
 
 /*
+ * Matrix-core variant ("Show HN: Phobos", section "Are we cuBLAS yet?", the
+ * side-quest that casts the fp32 data to fp16 before the tensor cores and
+ * keeps an fp32 accumulator).  sgemm_tc computes
+ *     C <- alpha * A' * B' + beta * C
+ * where A' and B' are A and B with every element rounded to the 16-bit
+ * format `fmt` as it is loaded: SGEMM_TC_F16 (IEEE binary16) or
+ * SGEMM_TC_BF16 (bfloat16), round to nearest even, values past the format's
+ * range becoming infinities.  The products of the rounded values are exact
+ * and are accumulated in fp32 by the 16-bit matrix instructions
+ * (v_mfma_f32_32x32x16_f16 / _bf16); alpha, beta, C and the epilogue are
+ * fp32.  A, B and C stay fp32 in memory.
+ *
+ * Accuracy: within 2*K*2^-24 * (|alpha| sum_k |A'[i][k]| |B'[k][j]| +
+ * |beta C[i][j]|) of the exact value of the expression above.  Against the
+ * fp32 product the input rounding adds at most |alpha| sum_k (|a| d(b) +
+ * |b| d(a) + d(a) d(b)), with d(x) = max(2^-11 |x|, 2^-25) for binary16 and
+ * |x| <= 65504, and d(x) = max(2^-8 |x|, 2^-134) for bfloat16.
+ *
+ * Arguments 1..11, quick returns (M or N = 0: nothing; K = 0 or alpha = 0:
+ * C <- beta*C, A and B not read), streams and errors as sgemm; 12 fmt (-12
+ * if unknown), 13 stream.  Tile configurations: sgemm_tc_config_count and
+ * sgemm_tc_config_at list those compiled for a format (bk = 32 always),
+ * sgemm_tc_get_config reports the one an M x N call would launch, and
+ * sgemm_tc_set_config forces one for every later call with that format
+ * (NULL: back to the built-in choice; process-wide, not thread-safe against
+ * concurrent calls).
+ */
+#define SGEMM_TC_F16 1
+#define SGEMM_TC_BF16 2
+
+int sgemm_tc(int64_t M, int64_t N, int64_t K, float alpha, const float* A, int64_t lda,
+             const float* B, int64_t ldb, float beta, float* C, int64_t ldc, int32_t fmt,
+             void* stream);
+int sgemm_tc_config_count(int32_t fmt);
+int sgemm_tc_config_at(int32_t fmt, int32_t index, sgemm_config* out);
+int sgemm_tc_get_config(int32_t fmt, int64_t M, int64_t N, sgemm_config* out);
+int sgemm_tc_set_config(int32_t fmt, const sgemm_config* cfg);
+
+/*
  * Host-resident super-tiled SGEMM, the single-GPU form of the pages' cluster
  * runtime ("@cluster" page, "What runs today": per node, allocate tile
  * buffers, load super-tiles, compute the init and step leaves as their inputs
@@ -250,6 +289,7 @@ int sgemm_supertiled_host(int64_t M, int64_t N, int64_t K, float alpha,
  */
 #define SGEMM_KIND_GEMM 0
 #define SGEMM_KIND_INIT_LEAF 1
+#define SGEMM_KIND_TC 2
 int sgemm_trace_begin(int64_t capacity);
 int sgemm_trace_end(float* ms_out, int32_t* kind_out, int64_t cap, int64_t* n_out);
 

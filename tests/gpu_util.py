@@ -19,11 +19,14 @@ def to_dev(buf):
     return torch.from_numpy(np.ascontiguousarray(buf)).to(device())
 
 
-def run(w, x, entry=None, tiles=None, offset_c=0):
-    """Run the HIP path on the inputs x; returns the flat C buffer after the call."""
+def run(w, x, entry=None, tiles=None, offset_c=0, fmt=None):
+    """Run the HIP path on the inputs x; returns the flat C buffer after the call.
+    fmt: the matrix-core variant (sgemm_tc) with that input format."""
     entry = entry or w.entry
     dA, dB, dC = to_dev(x.A), to_dev(x.B), to_dev(x.C)
-    if entry == "sgemm":
+    if fmt is not None or entry == "sgemm_tc":
+        g.sgemm_tc(w.M, w.N, w.K, w.alpha, dA, w.lda, dB, w.ldb, w.beta, dC, w.ldc, fmt=fmt)
+    elif entry == "sgemm":
         g.sgemm(w.M, w.N, w.K, w.alpha, dA, w.lda, dB, w.ldb, w.beta, dC, w.ldc)
     else:
         TM, TN, TK = tiles or (w.TM, w.TN, w.TK)
@@ -37,10 +40,11 @@ def logical_c(w, flat):
     return flat[: w.M * w.ldc].reshape(w.M, w.ldc)[:, : w.N]
 
 
-def check_full(w, x, out, steps=1, exact=False, relaxed=False):
-    """Every element against the full oracle; pads and guard row untouched."""
+def check_full(w, x, out, steps=1, exact=False, relaxed=False, fmt=None):
+    """Every element against the full oracle; pads and guard row untouched.
+    fmt: against the oracle of the matrix-core variant with that input format."""
     ref, bnd = oracle.sgemm(w.M, w.N, w.K, w.alpha, x.A, x.B, w.beta, x.C,
-                            lda=w.lda, ldb=w.ldb, ldc=w.ldc)
+                            lda=w.lda, ldb=w.ldb, ldc=w.ldc, fmt=fmt)
     got = logical_c(w, out)
     assert not np.isnan(got).any(), f"{w.name}: NaN in C"
     if exact:
@@ -71,11 +75,12 @@ def check_pads(w, x, out):
     assert same.all(), f"{w.name}: {int((~same).sum())} pad/guard elements of C changed"
 
 
-def check_sampled(w, x, out, count=4000, exact=False, seed=7):
-    """Sampled entries against the oracle's per-entry routine."""
+def check_sampled(w, x, out, count=4000, exact=False, seed=7, fmt=None):
+    """Sampled entries against the oracle's per-entry routine (fmt: the
+    matrix-core variant's)."""
     rows, cols = wl.sample_entries(w, count, seed=seed)
     ref, bnd = oracle.sgemm_entries(w.M, w.N, w.K, w.alpha, x.A, x.B, w.beta, x.C, rows, cols,
-                                    lda=w.lda, ldb=w.ldb, ldc=w.ldc)
+                                    lda=w.lda, ldb=w.ldb, ldc=w.ldc, fmt=fmt)
     got = logical_c(w, out)[rows, cols]
     assert not np.isnan(got).any(), f"{w.name}: NaN at sampled entries"
     if exact:
@@ -87,7 +92,7 @@ def check_sampled(w, x, out, count=4000, exact=False, seed=7):
     return float((np.abs(got.astype(np.float64) - ref) / bnd).max())
 
 
-def check_freivalds(w, x, out, seed=3, chunk=2048):
+def check_freivalds(w, x, out, seed=3, chunk=2048, fmt=None):
     """A property that holds at any size: C_out @ v against alpha*A@(B@v) + beta*C0@v.
 
     For every row i, |sum_j (C_out - C_exact)_ij v_j| <= sum_j |v_j| Bnd_ij, and
@@ -99,6 +104,10 @@ def check_freivalds(w, x, out, seed=3, chunk=2048):
     v = rng.choice([-1.0, 1.0], size=w.N)
     A = x.logical("A")
     B = x.logical("B")
+    if fmt is not None:
+        # the matrix-core variant multiplies the inputs as rounded by the oracle
+        A = oracle.round_to(fmt, A)
+        B = oracle.round_to(fmt, B)
     C0 = x.logical("C")
     Cout = logical_c(w, out)
 

@@ -168,3 +168,36 @@ def test_trace_argument_checks():
     assert lib.sgemm_trace_end(None, None, 0, ctypes.byref(n)) == 0
     assert n.value == 0
     assert lib.sgemm_trace_end(None, None, -1, None) == -3
+
+
+@pytest.mark.parametrize("args,want", [
+    ((-1, 4, 4, 1.0, 8, 4, 8, 4, 0.0, 8, 4, 1), -1),
+    ((4, 4, 5, 1.0, 8, 4, 8, 4, 0.0, 8, 4, 1), -6),      # lda < K
+    ((4, 4, 4, 1.0, NULL, 4, 8, 4, 0.0, 8, 4, 1), -5),   # A read but NULL
+    ((4, 4, 4, 1.0, 8, 4, 8, 4, 0.0, 8, 4, 0), -12),     # unknown format
+    ((4, 4, 4, 1.0, 8, 4, 8, 4, 0.0, 8, 4, 3), -12),
+    ((0, 4, 4, 1.0, NULL, 4, NULL, 4, 0.0, NULL, 4, 2), 0),   # M == 0: no-op
+    ((1 << 31, 4, 4, 1.0, 8, 4, 8, 4, 0.0, 8, 4, 2), g.SGEMM_ERR_TOO_LARGE),
+])
+def test_tc_argument_checks(args, want):
+    assert g.sgemm_tc_raw(*args, stream=0) == want
+
+
+def test_tc_configs():
+    for fmt in (g.SGEMM_TC_F16, g.SGEMM_TC_BF16):
+        cfgs = g.tc_configs(fmt)
+        assert len(cfgs) >= 5
+        assert all(c.bk == 32 and c.bm % (32 * c.wm) == 0 and c.bn % (32 * c.wn) == 0
+                   for c in cfgs)
+        # large problems take the 256 x 256 tile, small ones a small tile
+        assert g.sgemm_tc_get_config(fmt, 16384, 16384).as_tuple()[:2] == (256, 256)
+        assert g.sgemm_tc_get_config(fmt, 64, 64).as_tuple()[:2] == (64, 64)
+        g.sgemm_tc_set_config(fmt, cfgs[-1])
+        assert g.sgemm_tc_get_config(fmt, 16384, 16384).as_tuple() == cfgs[-1].as_tuple()
+        g.sgemm_tc_set_config(fmt, None)
+        with pytest.raises(RuntimeError):
+            g.sgemm_tc_set_config(fmt, (48, 48, 32, 1, 1))
+    lib = g.lib()
+    assert lib.sgemm_tc_config_count(0) == -1
+    assert lib.sgemm_tc_config_at(1, 999, None) == -2
+    assert lib.sgemm_tc_get_config(7, 4, 4, None) == -1
