@@ -29,6 +29,7 @@ SGEMM_WALK_SHELLS = 1
 SGEMM_KIND_GEMM = 0
 SGEMM_KIND_INIT_LEAF = 1
 SGEMM_KIND_TC = 2
+SGEMM_KIND_TC_CAST = 3
 SGEMM_TC_F16 = 1
 SGEMM_TC_BF16 = 2
 
@@ -48,6 +49,17 @@ class sgemm_config(ctypes.Structure):
 
     def __repr__(self):
         return "sgemm_config(bm=%d, bn=%d, bk=%d, wm=%d, wn=%d)" % self.as_tuple()
+
+
+class sgemm_tc_config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("bm", "bn", "bk", "wm", "wn", "staged")]
+
+    def as_tuple(self):
+        return (self.bm, self.bn, self.bk, self.wm, self.wn, self.staged)
+
+    def __repr__(self):
+        return ("sgemm_tc_config(bm=%d, bn=%d, bk=%d, wm=%d, wn=%d, staged=%d)"
+                % self.as_tuple())
 
 
 class sgemm_plan_model(ctypes.Structure):
@@ -89,9 +101,10 @@ _SIGNATURES = {
     "sgemm_tc": ([_i64, _i64, _i64, _f32, _vp, _i64, _vp, _i64, _f32, _vp, _i64, _i32, _vp],
                  ctypes.c_int),
     "sgemm_tc_config_count": ([_i32], ctypes.c_int),
-    "sgemm_tc_config_at": ([_i32, _i32, ctypes.POINTER(sgemm_config)], ctypes.c_int),
-    "sgemm_tc_get_config": ([_i32, _i64, _i64, ctypes.POINTER(sgemm_config)], ctypes.c_int),
-    "sgemm_tc_set_config": ([_i32, ctypes.POINTER(sgemm_config)], ctypes.c_int),
+    "sgemm_tc_config_at": ([_i32, _i32, ctypes.POINTER(sgemm_tc_config)], ctypes.c_int),
+    "sgemm_tc_get_config": ([_i32, _i64, _i64, _i64, ctypes.POINTER(sgemm_tc_config)],
+                            ctypes.c_int),
+    "sgemm_tc_set_config": ([_i32, ctypes.POINTER(sgemm_tc_config)], ctypes.c_int),
     "sgemm_plan_supertiles": ([_i64, _i64, _i64, _f32, _i64, ctypes.POINTER(sgemm_plan_model),
                                ctypes.POINTER(sgemm_plan)], ctypes.c_int),
     "sgemm_supertiled_host": ([_i64, _i64, _i64, _f32, _vp, _i64, _vp, _i64, _f32, _vp, _i64,
@@ -189,25 +202,26 @@ def sgemm_tc(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, fmt=None, stream=None
 
 
 def tc_configs(fmt):
-    """The compiled configurations of the matrix-core variant for one format."""
+    """The compiled configurations of the matrix-core variant for one format
+    (fused ones first, then staged ones)."""
     out = []
     for i in range(lib().sgemm_tc_config_count(fmt)):
-        c = sgemm_config()
+        c = sgemm_tc_config()
         _check(lib().sgemm_tc_config_at(fmt, i, ctypes.byref(c)), "sgemm_tc_config_at")
         out.append(c)
     return out
 
 
-def sgemm_tc_get_config(fmt, M, N):
-    c = sgemm_config()
-    _check(lib().sgemm_tc_get_config(fmt, M, N, ctypes.byref(c)), "sgemm_tc_get_config")
+def sgemm_tc_get_config(fmt, M, N, K):
+    c = sgemm_tc_config()
+    _check(lib().sgemm_tc_get_config(fmt, M, N, K, ctypes.byref(c)), "sgemm_tc_get_config")
     return c
 
 
 def sgemm_tc_set_config(fmt, cfg):
     """Force one matrix-core configuration for format fmt (None clears)."""
-    if cfg is not None and not isinstance(cfg, sgemm_config):
-        cfg = sgemm_config(*cfg)
+    if cfg is not None and not isinstance(cfg, sgemm_tc_config):
+        cfg = sgemm_tc_config(*cfg)
     _check(lib().sgemm_tc_set_config(fmt, None if cfg is None else ctypes.byref(cfg)),
            "sgemm_tc_set_config")
 

@@ -194,12 +194,24 @@ int launch_gemm(int entry, int64_t M, int64_t N, int64_t K, float alpha, const f
                         beta, C, ldc, stream);
 }
 
-// ---- matrix-core variant: one kernel table per input format ----
+// ---- matrix-core variant: per input format, a fused table (rounding on
+// load) and a staged table (cast pass into a workspace, then the 16-bit GEMM)
 struct TcTable {
-    const KernelEntry* entries[3] = {nullptr, nullptr, nullptr};
-    int count[3] = {0, 0, 0};
+    const KernelEntry* fused[3] = {nullptr, nullptr, nullptr};
+    const phobos::Tc16Entry* staged[3] = {nullptr, nullptr, nullptr};
+    int nfused[3] = {0, 0, 0}, nstaged[3] = {0, 0, 0};
     TcTable() {
-        for (int f : {SGEMM_TC_F16, SGEMM_TC_BF16}) entries[f] = phobos::tc_kernel_table(f, &count[f]);
+        for (int f : {SGEMM_TC_F16, SGEMM_TC_BF16}) {
+            fused[f] = phobos::tc_kernel_table(f, &nfused[f]);
+            staged[f] = phobos::tc16_kernel_table(f, &nstaged[f]);
+        }
+    }
+    int count(int f) const { return nfused[f] + nstaged[f]; }
+    // entries 0 .. nfused-1 are fused, the rest staged
+    sgemm_tc_config at(int f, int i) const {
+        const bool st = i >= nfused[f];
+        const sgemm_config& c = st ? staged[f][i - nfused[f]].cfg : fused[f][i].cfg;
+        return sgemm_tc_config{c.bm, c.bn, c.bk, c.wm, c.wn, st ? 1 : 0};
     }
 };
 const TcTable& tc_table() {
@@ -207,29 +219,118 @@ const TcTable& tc_table() {
     return t;
 }
 bool tc_fmt_ok(int32_t fmt) { return fmt == SGEMM_TC_F16 || fmt == SGEMM_TC_BF16; }
-int g_tc_forced[3] = {-1, -1, -1};   // per format: index into its table, or -1 (g_mu)
+int g_tc_forced[3] = {-1, -1, -1};   // per format: index into its combined list, or -1 (g_mu)
 
-int tc_find(int32_t fmt, const sgemm_config& c) {
+int tc_find(int32_t fmt, const sgemm_tc_config& c) {
     const TcTable& t = tc_table();
-    for (int i = 0; i < t.count[fmt]; ++i)
-        if (same_cfg(t.entries[fmt][i].cfg, c)) return i;
+    for (int i = 0; i < t.count(fmt); ++i) {
+        const sgemm_tc_config e = t.at(fmt, i);
+        if (e.bm == c.bm && e.bn == c.bn && e.bk == c.bk && e.wm == c.wm && e.wn == c.wn &&
+            e.staged == c.staged)
+            return i;
+    }
     return -1;
 }
 
-// Forced, else the largest tile that still gives every CU work (the same
-// rule as the fp32 default), else small tiles.
-int tc_choose(int32_t fmt, int64_t M, int64_t N) {
+// Forced, else: the staged form for products large enough that the cast pass
+// (one read of A and B, a write of half their size) is small against the
+// GEMM, else the fused form with the largest tile that still gives every CU
+// work (the fp32 rule), else small fused tiles.
+int tc_choose(int32_t fmt, int64_t M, int64_t N, int64_t K) {
     {
         std::lock_guard<std::mutex> lk(g_mu);
         if (g_tc_forced[fmt] >= 0) return g_tc_forced[fmt];
     }
+    if (M >= 2048 && N >= 2048 && K >= 1024)
+        return tc_find(fmt, sgemm_tc_config{256, 256, 64, 4, 2, 1});
     static const int order[][4] = {{256, 256, 2, 2}, {256, 128, 2, 2}, {128, 128, 2, 2},
                                    {128, 64, 2, 1}};
     for (const auto& o : order) {
         const int64_t tiles = ((M + o[0] - 1) / o[0]) * ((N + o[1] - 1) / o[1]);
-        if (tiles >= 256) return tc_find(fmt, sgemm_config{o[0], o[1], 32, o[2], o[3]});
+        if (tiles >= 256) return tc_find(fmt, sgemm_tc_config{o[0], o[1], 32, o[2], o[3], 0});
     }
-    return tc_find(fmt, sgemm_config{64, 64, 32, 1, 1});
+    return tc_find(fmt, sgemm_tc_config{64, 64, 32, 1, 1, 0});
+}
+
+// Stream-ordered workspace of the staged form, from a memory pool of the
+// library's own per device that keeps freed memory for the next call.
+std::mutex g_pool_mu;
+std::map<int, hipMemPool_t> g_pools;
+hipMemPool_t tc_pool(int dev) {
+    std::lock_guard<std::mutex> lk(g_pool_mu);
+    auto it = g_pools.find(dev);
+    if (it != g_pools.end()) return it->second;
+    hipMemPoolProps props{};
+    props.allocType = hipMemAllocationTypePinned;
+    props.location.type = hipMemLocationTypeDevice;
+    props.location.id = dev;
+    hipMemPool_t pool = nullptr;
+    if (hipMemPoolCreate(&pool, &props) != hipSuccess) {
+        (void)hipGetLastError();
+        pool = nullptr;
+    } else {
+        uint64_t keep = UINT64_MAX;
+        (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+    }
+    g_pools[dev] = pool;
+    return pool;
+}
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// The staged form: cast pass into a workspace, 16-bit GEMM, workspace freed
+// on the stream.  Returns 1 (no launch) when the workspace cannot be had.
+int launch_tc_staged(int32_t fmt, const phobos::Tc16Entry& e, int64_t M, int64_t N, int64_t K,
+                     float alpha, const float* A, int64_t lda, const float* B, int64_t ldb,
+                     float beta, float* C, int64_t ldc, hipStream_t stream) {
+    const int64_t Mp = round_up(M, phobos::kTcPadMN), Np = round_up(N, phobos::kTcPadMN),
+                  Kp = round_up(K, phobos::kTcPadK);
+    const int64_t tm = (M + e.cfg.bm - 1) / e.cfg.bm, tn = (N + e.cfg.bn - 1) / e.cfg.bn;
+    if (tm * tn * e.threads > kMaxGridItems || Mp * Kp >= (int64_t(1) << 40))
+        return SGEMM_ERR_TOO_LARGE;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return hip_status(hipGetLastError());
+    hipMemPool_t pool = tc_pool(dev);
+    if (pool == nullptr) return 1;
+    void* ws = nullptr;
+    const size_t bytes = (size_t)((Mp + Np) * Kp) * sizeof(uint16_t);
+    if (hipMallocFromPoolAsync(&ws, bytes, pool, stream) != hipSuccess || ws == nullptr) {
+        (void)hipGetLastError();
+        return 1;
+    }
+    uint16_t* A16 = static_cast<uint16_t*>(ws);
+    uint16_t* B16 = A16 + Mp * Kp;
+    int st;
+    {
+        TraceScope ts(stream, SGEMM_KIND_TC_CAST);
+        const bool va = aligned16(A) && lda % 4 == 0, vb = aligned16(B) && ldb % 4 == 0;
+        st = hip_status(phobos::launch_tc_cast(fmt, A, lda, va, B, ldb, vb, (int)M, (int)N,
+                                               (int)K, A16, B16, (int)Mp, (int)Np, (int)Kp,
+                                               stream));
+    }
+    if (st == SGEMM_OK) {
+        phobos::Tc16Args p{};
+        p.A = A16;
+        p.B = B16;
+        p.ld = Kp;
+        p.M = (int32_t)M;
+        p.N = (int32_t)N;
+        p.K = (int32_t)Kp;
+        p.alpha = alpha;
+        p.beta = beta;
+        p.C = C;
+        p.ldc = ldc;
+        p.vec_c = aligned16(C) && ldc % 4 == 0;
+        p.tiles_m = (int32_t)tm;
+        p.tiles_n = (int32_t)tn;
+        p.group_m = std::max(1, env_int("SGEMM_GROUP_M", 4));
+        p.xcd_remap = ((tm * tn) % 8 == 0 && env_int("SGEMM_XCD_REMAP", 1) != 0) ? 1 : 0;
+        TraceScope ts(stream, SGEMM_KIND_TC);
+        st = hip_status(e.launch(p, stream));
+    }
+    const hipError_t fe = hipFreeAsync(ws, stream);
+    if (st == SGEMM_OK) st = hip_status(fe);
+    return st;
 }
 
 int launch_init(int64_t M, int64_t N, float beta, float* C, int64_t ldc, hipStream_t stream) {
@@ -343,34 +444,46 @@ int sgemm_tc(int64_t M, int64_t N, int64_t K, float alpha, const float* A, int64
     if (M == 0 || N == 0) return SGEMM_OK;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (K == 0 || alpha == 0.0f) return launch_init(M, N, beta, C, ldc, s);
-    const int e = tc_choose(fmt, M, N);
+    const TcTable& t = tc_table();
+    const int e = tc_choose(fmt, M, N, K);
     if (e < 0) return SGEMM_ERR_NO_CONFIG;
-    return launch_entry(tc_table().entries[fmt][e], SGEMM_KIND_TC, M, N, K, alpha, A, lda, B,
-                        ldb, beta, C, ldc, s);
+    if (e >= t.nfused[fmt]) {
+        const int r = launch_tc_staged(fmt, t.staged[fmt][e - t.nfused[fmt]], M, N, K, alpha, A,
+                                       lda, B, ldb, beta, C, ldc, s);
+        if (r != 1) return r;
+        // no workspace: the fused form with the same tile shape, else the default
+        int f = tc_find(fmt, sgemm_tc_config{256, 256, 32, 4, 2, 0});
+        if (f < 0) return SGEMM_ERR_NO_CONFIG;
+        return launch_entry(t.fused[fmt][f], SGEMM_KIND_TC, M, N, K, alpha, A, lda, B, ldb, beta,
+                            C, ldc, s);
+    }
+    return launch_entry(t.fused[fmt][e], SGEMM_KIND_TC, M, N, K, alpha, A, lda, B, ldb, beta, C,
+                        ldc, s);
 }
 
-int sgemm_tc_config_count(int32_t fmt) { return tc_fmt_ok(fmt) ? tc_table().count[fmt] : -1; }
+int sgemm_tc_config_count(int32_t fmt) { return tc_fmt_ok(fmt) ? tc_table().count(fmt) : -1; }
 
-int sgemm_tc_config_at(int32_t fmt, int32_t index, sgemm_config* out) {
+int sgemm_tc_config_at(int32_t fmt, int32_t index, sgemm_tc_config* out) {
     if (!tc_fmt_ok(fmt)) return -1;
-    if (index < 0 || index >= tc_table().count[fmt]) return -2;
+    if (index < 0 || index >= tc_table().count(fmt)) return -2;
     if (out == nullptr) return -3;
-    *out = tc_table().entries[fmt][index].cfg;
+    *out = tc_table().at(fmt, index);
     return SGEMM_OK;
 }
 
-int sgemm_tc_get_config(int32_t fmt, int64_t M, int64_t N, sgemm_config* out) {
+int sgemm_tc_get_config(int32_t fmt, int64_t M, int64_t N, int64_t K, sgemm_tc_config* out) {
     if (!tc_fmt_ok(fmt)) return -1;
     if (M < 0) return -2;
     if (N < 0) return -3;
-    if (out == nullptr) return -4;
-    const int e = tc_choose(fmt, M, N);
+    if (K < 0) return -4;
+    if (out == nullptr) return -5;
+    const int e = tc_choose(fmt, M, N, K);
     if (e < 0) return SGEMM_ERR_NO_CONFIG;
-    *out = tc_table().entries[fmt][e].cfg;
+    *out = tc_table().at(fmt, e);
     return SGEMM_OK;
 }
 
-int sgemm_tc_set_config(int32_t fmt, const sgemm_config* cfg) {
+int sgemm_tc_set_config(int32_t fmt, const sgemm_tc_config* cfg) {
     if (!tc_fmt_ok(fmt)) return -1;
     std::lock_guard<std::mutex> lk(g_mu);
     if (cfg == nullptr) {

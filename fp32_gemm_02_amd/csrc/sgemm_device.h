@@ -18,7 +18,8 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 // become one contiguous run of the raster order, so tiles that share rows of
 // A and columns of B sit in the same L2.  The raster walks group_m tile rows
 // at a time, column by column, to keep the A panels of a group hot.
-__device__ __forceinline__ void tile_of(const GemmArgs& p, int& tm, int& tn) {
+template <class Args>
+__device__ __forceinline__ void tile_of(const Args& p, int& tm, int& tn) {
     int bid = blockIdx.x;
     if (p.xcd_remap) {
         const int per = (p.tiles_m * p.tiles_n) >> 3;
@@ -61,5 +62,25 @@ __device__ __forceinline__ int swz(int r) {
     if constexpr (QA == 8) return (r & 7) ^ ((r >> 3) & 1);
     else return ((r >> 1) & 3) ^ ((r >> 3) & 1);
 }
+
+// One direct global-to-LDS load: every lane fetches the 16 bytes at its `src`
+// and the wave writes them to LDS at lds_dst + 16*lane (lds_dst is the same
+// for the whole wave; it goes in M0).  Issued as inline assembly so that the
+// compiler's wait-count analysis does not see an instruction that touches
+// both memory and LDS: that would make it wait for every outstanding LDS read
+// (lgkmcnt(0)) at each use, where one k-step of lookahead is intended.  The
+// kernel therefore waits for these loads itself (vmcnt) before the barrier
+// that publishes a stage.  Vector-memory loads complete in issue order, so
+// loads the compiler does not track can only make its own waits stricter.
+__device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
+    const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds_dst;
+    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0) : "memory");
+}
+
+// s_waitcnt immediate (gfx9 encoding) waiting for at most N outstanding
+// vector-memory loads and for every LDS access; exports are not waited for.
+template <int N>
+constexpr int kWaitVm = (N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8);
+static_assert(kWaitVm<0> == 0x70 && kWaitVm<4> == 0x74, "s_waitcnt encoding");
 
 }  // namespace phobos

@@ -42,6 +42,38 @@ const KernelEntry* kernel_table(int* count);
 // fmt (SGEMM_TC_F16 or SGEMM_TC_BF16); nullptr and *count = 0 otherwise.
 const KernelEntry* tc_kernel_table(int fmt, int* count);
 
+// Staged form of the matrix-core variant: the 16-bit operands prepared by
+// the cast pass (A16: Mp x Kp row-major; B16: B transposed, Np x Kp; both
+// with row pitch Kp, zero past the real M, N, K) and the fp32 output.
+struct Tc16Args {
+    const uint16_t* A;
+    const uint16_t* B;
+    int64_t ld;                 // Kp
+    int32_t M, N, K;            // real M and N; K = Kp
+    float alpha, beta;
+    float* C;
+    int64_t ldc;
+    int32_t vec_c;              // C 16-byte aligned and ldc % 4 == 0
+    int32_t tiles_m, tiles_n;   // ceil(M/bm), ceil(N/bn)
+    int32_t group_m, xcd_remap;
+};
+using Tc16LaunchFn = hipError_t (*)(const Tc16Args&, hipStream_t);
+struct Tc16Entry {
+    sgemm_config cfg;
+    int32_t stages;       // LDS ring depth
+    int32_t threads;
+    int32_t lds_bytes;
+    Tc16LaunchFn launch;
+};
+// Tiles of the staged GEMM divide 256 x 256 and chunks divide 64, so the
+// cast pass pads M and N to multiples of 256 and K to a multiple of 64.
+constexpr int kTcPadMN = 256, kTcPadK = 64;
+const Tc16Entry* tc16_kernel_table(int fmt, int* count);
+// The cast pass: A16 and B16 from A and B (vec_*: 16-byte aligned rows).
+hipError_t launch_tc_cast(int fmt, const float* A, int64_t lda, bool vec_a, const float* B,
+                          int64_t ldb, bool vec_b, int M, int N, int K, uint16_t* A16,
+                          uint16_t* B16, int Mp, int Np, int Kp, hipStream_t stream);
+
 // C <- beta*C over an M x N view (beta == 0: C <- 0 without reading C).
 hipError_t launch_init_leaf(int64_t M, int64_t N, float beta, float* C, int64_t ldc,
                             hipStream_t stream);

@@ -6,9 +6,10 @@
 // Phobos", section "Are we cuBLAS yet?", the side-quest that casts to fp16
 // before the tensor cores and keeps an fp32 accumulator).
 //
-// One workgroup owns a BM x BN tile of C and walks K in chunks of 32:
+// One workgroup owns a BM x BN tile of C and walks K in chunks of BK (32 or
+// 64, i.e. 2 or 4 MFMA k-steps):
 //   - global -> registers: 128-bit fp32 loads (bounds-checked, zero fill at
-//     the edges), issued one chunk ahead so they overlap the MFMAs;
+//     the edges), issued a whole chunk ahead so they overlap the MFMAs;
 //   - registers -> LDS: converted with gfx950's packed converts
 //     (v_cvt_pk_f16_f32 / v_cvt_pk_bf16_f32, round to nearest even) and
 //     stored as 16-bit values, halving LDS traffic against fp32.  A is stored
@@ -17,7 +18,9 @@
 //     4) rows of k for 4 columns and writes each column's k run at once;
 //   - each 64-lane wave owns a TWM x TWN sub-tile of MB x NB blocks of
 //     32 x 32, accumulated by v_mfma_f32_32x32x16_{f16,bf16};
-//   - two LDS stages, one barrier per chunk.
+//   - two LDS stages, one barrier per chunk, placed before the last k-step's
+//     MFMAs so that those overlap the barrier and the next chunk's first
+//     operand reads; operands are read one k-step ahead of their MFMAs.
 //
 // MFMA 32x32x16 16-bit operand layout (checked on the GPU with an in-bounds
 // probe; l = lane, h = l / 32):
@@ -25,14 +28,17 @@
 //   src B: lane l holds B'[8h + e][l % 32], e = 0..7  (one 16-byte LDS read of
 //          the transposed tile)
 //   acc  : lane l, register r holds D[8*(r/4) + 4h + r%4][l % 32]
-// LDS rows are 32 halves = 64 bytes = 4 pieces of 16 bytes, XOR-swizzled by
-// row (swz<4>) so the 32-row operand reads are free of bank conflicts.  As in
+// LDS rows are BK halves = 4 or 8 pieces of 16 bytes, XOR-swizzled by row
+// (swz<4> / swz<8>) so the 32-row operand reads are free of bank conflicts.  As in
 // the fp32 kernel, block nb of a wave holds the columns NB*j + nb (j =
 // 0..31): the B tile's LDS rows are written in that interleaved order, and
 // the epilogue stores NB consecutive columns of C at once.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <algorithm>
+#include <type_traits>
 
 #include "sgemm_device.h"
 #include "sgemm_internal.h"
@@ -71,32 +77,37 @@ template <> struct TcFmt<SGEMM_TC_BF16> {
     }
 };
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int BK_, int WM, int WN>
 struct TcShape {
     static constexpr int NT = 64 * WM * WN;      // threads
-    static constexpr int BK = 32;                // k per chunk: two MFMA k-steps
+    static constexpr int BK = BK_;               // k per chunk: BK/16 MFMA k-steps
+    static constexpr int KS = BK / 16;
     static constexpr int TWM = BM / WM, TWN = BN / WN;
     static constexpr int MB = TWM / 32, NB = TWN / 32;
     static constexpr int ROWB = BK * 2;          // bytes of one LDS row (16-bit values)
-    static constexpr int UA = BM * 4 / NT;       // A units (8 k of one row) per thread
-    static constexpr int KB = (BN % NT == 0) ? 8 : 4;   // k rows of one B unit
+    static constexpr int PR = ROWB / 16;         // 16-byte pieces per LDS row
+    static constexpr int OA = BK / 8;            // A units (8 k of one row) per row
+    static constexpr int UA = BM * OA / NT;      // A units per thread
     static constexpr int QB = BN / 4;            // column quads of the tile
-    static constexpr int UB = QB * (BK / KB) / NT;      // B units per thread
+    static constexpr int KB = (QB * (BK / 8)) % NT == 0 ? 8 : 4;   // k rows of one B unit
+    static constexpr int UB = QB * (BK / KB) / NT;                 // B units per thread
     static constexpr int STAGE = (BM + BN) * ROWB;
     static constexpr int LDS_BYTES = 2 * STAGE;
+    static_assert(BK == 32 || BK == 64, "4 or 8 pieces per LDS row");
     static_assert(TWM % 32 == 0 && TWN % 32 == 0, "whole 32 x 32 blocks per wave");
     static_assert(NB == 1 || NB == 2 || NB == 4, "NB-wide epilogue stores");
-    static_assert(UA >= 1 && UA * NT == BM * 4, "whole A units per thread");
+    static_assert(UA >= 1 && UA * NT == BM * OA, "whole A units per thread");
     static_assert(UB >= 1 && UB * NT == QB * (BK / KB), "whole B units per thread");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS of one CU");
 };
 
-template <int FMT, int BM, int BN, int WM, int WN, bool VEC>
+template <int FMT, int BM, int BN, int BK_, int WM, int WN, int PF, bool VEC>
 __global__ __launch_bounds__(64 * WM * WN) void sgemm_tc_kernel(GemmArgs p) {
     using F = TcFmt<FMT>;
-    using T = TcShape<BM, BN, WM, WN>;
-    constexpr int NT = T::NT, BK = T::BK, ROWB = T::ROWB, UA = T::UA, UB = T::UB, KB = T::KB,
-                  QB = T::QB, MB = T::MB, NB = T::NB, TWM = T::TWM, TWN = T::TWN;
+    using T = TcShape<BM, BN, BK_, WM, WN>;
+    constexpr int NT = T::NT, BK = T::BK, KS = T::KS, ROWB = T::ROWB, PR = T::PR, OA = T::OA,
+                  UA = T::UA, UB = T::UB, KB = T::KB, QB = T::QB, MB = T::MB, NB = T::NB,
+                  TWM = T::TWM, TWN = T::TWN;
     __shared__ __attribute__((aligned(16))) char lds[T::LDS_BYTES];
 
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -107,21 +118,55 @@ __global__ __launch_bounds__(64 * WM * WN) void sgemm_tc_kernel(GemmArgs p) {
     const int m0 = tm * BM, n0 = tn * BN;
     const int nk = (p.K + BK - 1) / BK;
 
-    f32x4 ra[UA][2];    // A: 8 consecutive k of one row per unit
-    f32x4 rb[UB][KB];   // B: KB rows of k, 4 consecutive columns per unit
+    // PF sets of staging registers: chunk j >= 1 is loaded into set (j-1) % PF
+    f32x4 ra[PF][UA][2];    // A: 8 consecutive k of one row per unit
+    f32x4 rb[PF][UB][KB];   // B: KB rows of k, 4 consecutive columns per unit
 
-    auto load = [&](int k0) {
+    // Interior chunks (the whole tile inside M and N, the chunk inside K,
+    // 16-byte aligned operands) load without bounds checks through pointers
+    // set up once; the checked path below serves the edges.  The test is
+    // uniform over the workgroup, so the choice is a scalar branch.
+    const bool tile_inside = VEC && m0 + BM <= p.M && n0 + BN <= p.N;
+    const float* pa[UA];
+    const float* pb[UB];
+#pragma unroll
+    for (int i = 0; i < UA; ++i) {
+        const int u = t + i * NT;
+        pa[i] = p.A + (int64_t)(m0 + u / OA) * p.lda + 8 * (u % OA);
+    }
+#pragma unroll
+    for (int i = 0; i < UB; ++i) {
+        const int u = t + i * NT;
+        pb[i] = p.B + (int64_t)(KB * (u / QB)) * p.ldb + n0 + 4 * (u % QB);
+    }
+
+    auto load = [&](int k0, auto set) {
+        if (tile_inside && k0 + BK <= p.K) {
+#pragma unroll
+            for (int i = 0; i < UA; ++i) {
+                ra[set][i][0] = *reinterpret_cast<const f32x4*>(pa[i] + k0);
+                ra[set][i][1] = *reinterpret_cast<const f32x4*>(pa[i] + k0 + 4);
+            }
+#pragma unroll
+            for (int i = 0; i < UB; ++i) {
+                const float* src = pb[i] + (int64_t)k0 * p.ldb;
+#pragma unroll
+                for (int r = 0; r < KB; ++r)
+                    rb[set][i][r] = *reinterpret_cast<const f32x4*>(src + (int64_t)r * p.ldb);
+            }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < UA; ++i) {
-            const int u = t + i * NT, row = u >> 2, oct = u & 3;
+            const int u = t + i * NT, row = u / OA, oct = u % OA;
             const int gr = m0 + row, gk = k0 + 8 * oct;
             if (gr < p.M) {
                 const float* src = p.A + (int64_t)gr * p.lda + gk;
-                ra[i][0] = load4<VEC>(src, p.K - gk);
-                ra[i][1] = load4<VEC>(src + 4, p.K - gk - 4);
+                ra[set][i][0] = load4<VEC>(src, p.K - gk);
+                ra[set][i][1] = load4<VEC>(src + 4, p.K - gk - 4);
             } else {
-                ra[i][0] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-                ra[i][1] = ra[i][0];
+                ra[set][i][0] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                ra[set][i][1] = ra[set][i][0];
             }
         }
 #pragma unroll
@@ -132,21 +177,22 @@ __global__ __launch_bounds__(64 * WM * WN) void sgemm_tc_kernel(GemmArgs p) {
 #pragma unroll
             for (int r = 0; r < KB; ++r) {
                 const int k = gk + r;
-                rb[i][r] = (k < p.K) ? load4<VEC>(p.B + (int64_t)k * p.ldb + gc, ncols)
-                                     : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                rb[set][i][r] = (k < p.K) ? load4<VEC>(p.B + (int64_t)k * p.ldb + gc, ncols)
+                                          : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
             }
         }
     };
 
-    auto store = [&](int stage) {
+    auto store = [&](int stage, auto set) {
         char* sa = lds + stage * T::STAGE;
         char* sb = sa + BM * ROWB;
 #pragma unroll
         for (int i = 0; i < UA; ++i) {
-            const int u = t + i * NT, row = u >> 2, oct = u & 3;
-            const u32x4 v = {F::pack(ra[i][0][0], ra[i][0][1]), F::pack(ra[i][0][2], ra[i][0][3]),
-                             F::pack(ra[i][1][0], ra[i][1][1]), F::pack(ra[i][1][2], ra[i][1][3])};
-            *reinterpret_cast<u32x4*>(sa + row * ROWB + 16 * (oct ^ swz<4>(row))) = v;
+            const int u = t + i * NT, row = u / OA, oct = u % OA;
+            const f32x4 a0 = ra[set][i][0], a1 = ra[set][i][1];
+            const u32x4 v = {F::pack(a0[0], a0[1]), F::pack(a0[2], a0[3]), F::pack(a1[0], a1[1]),
+                             F::pack(a1[2], a1[3])};
+            *reinterpret_cast<u32x4*>(sa + row * ROWB + 16 * (oct ^ swz<PR>(row))) = v;
         }
 #pragma unroll
         for (int i = 0; i < UB; ++i) {
@@ -157,13 +203,14 @@ __global__ __launch_bounds__(64 * WM * WN) void sgemm_tc_kernel(GemmArgs p) {
                 const int col = 4 * q + c, wcol = col % TWN;
                 const int lrow = (col - wcol) + (wcol % NB) * 32 + wcol / NB;
                 char* rowp = sb + lrow * ROWB;
+                const auto& b = rb[set][i];
                 if constexpr (KB == 8) {
-                    const u32x4 v = {F::pack(rb[i][0][c], rb[i][1][c]), F::pack(rb[i][2][c], rb[i][3][c]),
-                                     F::pack(rb[i][4][c], rb[i][5][c]), F::pack(rb[i][6][c], rb[i][7][c])};
-                    *reinterpret_cast<u32x4*>(rowp + 16 * (grp ^ swz<4>(lrow))) = v;
+                    const u32x4 v = {F::pack(b[0][c], b[1][c]), F::pack(b[2][c], b[3][c]),
+                                     F::pack(b[4][c], b[5][c]), F::pack(b[6][c], b[7][c])};
+                    *reinterpret_cast<u32x4*>(rowp + 16 * (grp ^ swz<PR>(lrow))) = v;
                 } else {
-                    const u32x2 v = {F::pack(rb[i][0][c], rb[i][1][c]), F::pack(rb[i][2][c], rb[i][3][c])};
-                    *reinterpret_cast<u32x2*>(rowp + 16 * ((grp >> 1) ^ swz<4>(lrow)) + 8 * (grp & 1)) = v;
+                    const u32x2 v = {F::pack(b[0][c], b[1][c]), F::pack(b[2][c], b[3][c])};
+                    *reinterpret_cast<u32x2*>(rowp + 16 * ((grp >> 1) ^ swz<PR>(lrow)) + 8 * (grp & 1)) = v;
                 }
             }
         }
@@ -172,7 +219,16 @@ __global__ __launch_bounds__(64 * WM * WN) void sgemm_tc_kernel(GemmArgs p) {
     // lane l's operand of block row `row` (A) or interleaved row `row` (B) at
     // MFMA k-step s of the chunk: 8 values at k = 16s + 8h
     auto frag = [&](const char* base, int row, int s) -> u32x4 {
-        return *reinterpret_cast<const u32x4*>(base + row * ROWB + 16 * ((2 * s + h) ^ swz<4>(row)));
+        return *reinterpret_cast<const u32x4*>(base + row * ROWB + 16 * ((2 * s + h) ^ swz<PR>(row)));
+    };
+    u32x4 fa[2][MB], fb[2][NB];
+    auto read_step = [&](int stage, int s, int buf) {
+        const char* sa = lds + stage * T::STAGE;
+        const char* sb = sa + BM * ROWB;
+#pragma unroll
+        for (int i = 0; i < MB; ++i) fa[buf][i] = frag(sa, wm * TWM + i * 32 + l32, s);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) fb[buf][j] = frag(sb, wn * TWN + j * 32 + l32, s);
     };
 
     f32x16 acc[MB][NB];
@@ -183,29 +239,47 @@ __global__ __launch_bounds__(64 * WM * WN) void sgemm_tc_kernel(GemmArgs p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    load(0);
-    store(0);
+    // Pipeline: while chunk c is computed from LDS, the registers hold (or
+    // are receiving) chunks c+1 .. c+PF.  At the last k-step of chunk c the
+    // set holding chunk c+1 goes to the other LDS stage, the barrier follows,
+    // the loads of chunk c+1+PF are issued into the set just emptied and the
+    // first operands of chunk c+1 are read; only then are the last k-step's
+    // MFMAs issued, so they overlap all of that.  Loads thus have PF whole
+    // chunks to land.  The stage written at chunk c was last read during
+    // chunk c-1, before that chunk's barrier.
+    using S0 = std::integral_constant<int, 0>;
+    load(0, S0{});
+    store(0, S0{});
+    if (nk > 1) load(BK, S0{});
+    if constexpr (PF == 2) {
+        if (nk > 2) load(2 * BK, std::integral_constant<int, 1>{});
+    }
     __syncthreads();
-    for (int c = 0; c < nk; ++c) {
-        const bool more = c + 1 < nk;
-        if (more) load((c + 1) * BK);   // in flight during this chunk's MFMAs
-        const char* sa = lds + (c & 1) * T::STAGE;
-        const char* sb = sa + BM * ROWB;
+    read_step(0, 0, 0);
+    auto chunk = [&](int c, auto set) {
 #pragma unroll
-        for (int s = 0; s < BK / 16; ++s) {
-            u32x4 fa[MB], fb[NB];
-#pragma unroll
-            for (int i = 0; i < MB; ++i) fa[i] = frag(sa, wm * TWM + i * 32 + l32, s);
-#pragma unroll
-            for (int j = 0; j < NB; ++j) fb[j] = frag(sb, wn * TWN + j * 32 + l32, s);
+        for (int s = 0; s < KS; ++s) {
+            if (s + 1 < KS) {
+                read_step(c & 1, s + 1, (s + 1) & 1);
+            } else if (c + 1 < nk) {
+                store((c + 1) & 1, set);
+                __syncthreads();
+                if (c + 1 + PF < nk) load((c + 1 + PF) * BK, set);
+                read_step((c + 1) & 1, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < MB; ++i)
 #pragma unroll
-                for (int j = 0; j < NB; ++j) acc[i][j] = F::mma(fa[i], fb[j], acc[i][j]);
+                for (int j = 0; j < NB; ++j) acc[i][j] = F::mma(fa[s & 1][i], fb[s & 1][j], acc[i][j]);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        // the other stage was last read before the previous barrier
-        if (more) store((c + 1) & 1);
-        __syncthreads();
+    };
+    for (int c = 0; c < nk; c += PF) {
+        chunk(c, S0{});
+        if constexpr (PF == 2) {
+            if (c + 1 < nk) chunk(c + 1, std::integral_constant<int, 1>{});
+        }
     }
 
     // ---- epilogue: C <- alpha*acc + beta*C (beta == 0: C not read) ----
@@ -254,30 +328,326 @@ __global__ __launch_bounds__(64 * WM * WN) void sgemm_tc_kernel(GemmArgs p) {
     }
 }
 
-template <int FMT, int BM, int BN, int WM, int WN, bool VEC>
+template <int FMT, int BM, int BN, int BK, int WM, int WN, int PF, bool VEC>
 hipError_t launch_tc(const GemmArgs& p, hipStream_t stream) {
     const dim3 grid((unsigned)(p.tiles_m * p.tiles_n));
     const dim3 block(64 * WM * WN);
-    hipLaunchKernelGGL((sgemm_tc_kernel<FMT, BM, BN, WM, WN, VEC>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((sgemm_tc_kernel<FMT, BM, BN, BK, WM, WN, PF, VEC>), grid, block, 0,
+                       stream, p);
     return hipGetLastError();
 }
 
-#define PHOBOS_TC_CFG(FMT, BM, BN, WM, WN)                                              \
-    KernelEntry{sgemm_config{BM, BN, 32, WM, WN}, 64 * WM * WN,                        \
-                TcShape<BM, BN, WM, WN>::LDS_BYTES,                                     \
-                &launch_tc<FMT, BM, BN, WM, WN, true>,                                  \
-                &launch_tc<FMT, BM, BN, WM, WN, false>}
+#ifndef PHOBOS_TC_PF
+#define PHOBOS_TC_PF 1
+#endif
+
+#define PHOBOS_TC_CFG(FMT, BM, BN, BK, WM, WN)                                          \
+    KernelEntry{sgemm_config{BM, BN, BK, WM, WN}, 64 * WM * WN,                        \
+                TcShape<BM, BN, BK, WM, WN>::LDS_BYTES,                                 \
+                &launch_tc<FMT, BM, BN, BK, WM, WN, PHOBOS_TC_PF, true>,                \
+                &launch_tc<FMT, BM, BN, BK, WM, WN, PHOBOS_TC_PF, false>}
 
 #define PHOBOS_TC_TABLE(FMT)                                                            \
     {                                                                                   \
-        PHOBOS_TC_CFG(FMT, 256, 256, 2, 2), PHOBOS_TC_CFG(FMT, 256, 256, 4, 2),         \
-            PHOBOS_TC_CFG(FMT, 256, 128, 2, 2), PHOBOS_TC_CFG(FMT, 128, 256, 2, 2),     \
-            PHOBOS_TC_CFG(FMT, 128, 128, 2, 2), PHOBOS_TC_CFG(FMT, 128, 64, 2, 1),      \
-            PHOBOS_TC_CFG(FMT, 64, 64, 1, 1),                                           \
+        PHOBOS_TC_CFG(FMT, 256, 256, 32, 2, 2), PHOBOS_TC_CFG(FMT, 256, 256, 32, 4, 2), \
+            PHOBOS_TC_CFG(FMT, 256, 128, 32, 2, 2), PHOBOS_TC_CFG(FMT, 128, 256, 32, 2, 2), \
+            PHOBOS_TC_CFG(FMT, 128, 128, 32, 2, 2), PHOBOS_TC_CFG(FMT, 128, 128, 64, 2, 2), \
+            PHOBOS_TC_CFG(FMT, 128, 64, 32, 2, 1), PHOBOS_TC_CFG(FMT, 64, 64, 32, 1, 1),  \
     }
 
-// The compiled configurations of the matrix-core variant, per input format
-// (bk is always 32); nullptr for an unknown format.
+// ---------------------------------------------------------------------------
+// Staged form of the variant: the rounding is done once, by a cast pass, into
+// a 16-bit workspace laid out for the GEMM (A row-major, B transposed, both k
+// contiguous, zero-padded to whole tiles and whole K chunks); the GEMM then
+// streams 16-bit operands straight into LDS with direct loads.  Each element
+// is rounded by the same conversion as in the fused form, so the products
+// and their order are the same.
+
+// A16[i][k] = round(A[i][k]) for i < M, k < K, 0 elsewhere in Mp x Kp.  One
+// thread per 8 consecutive k of a row (two 16-byte loads, one 16-byte store).
+template <int FMT, bool VEC>
+__global__ __launch_bounds__(256) void tc_cast_rows_kernel(const float* A, int64_t lda, int M,
+                                                           int K, uint16_t* out, int Mp, int Kp) {
+    using F = TcFmt<FMT>;
+    const int64_t per_row = Kp / 8, total = (int64_t)Mp * per_row;
+    for (int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x; u < total;
+         u += (int64_t)gridDim.x * 256) {
+        const int i = (int)(u / per_row), k = 8 * (int)(u % per_row);
+        f32x4 a0 = f32x4{0.0f, 0.0f, 0.0f, 0.0f}, a1 = a0;
+        if (i < M) {
+            const float* src = A + (int64_t)i * lda + k;
+            a0 = load4<VEC>(src, K - k);
+            a1 = load4<VEC>(src + 4, K - k - 4);
+        }
+        const u32x4 v = {F::pack(a0[0], a0[1]), F::pack(a0[2], a0[3]), F::pack(a1[0], a1[1]),
+                         F::pack(a1[2], a1[3])};
+        *reinterpret_cast<u32x4*>(out + (int64_t)i * Kp + k) = v;
+    }
+}
+
+// B16[n][k] = round(B[k][n]) for k < K, n < N, 0 elsewhere in Np x Kp: a
+// 64 x 64 transpose through LDS per workgroup step (reads along n, writes
+// along k, both 16 bytes per lane).
+template <int FMT, bool VEC>
+__global__ __launch_bounds__(256) void tc_cast_cols_kernel(const float* B, int64_t ldb, int K,
+                                                           int N, uint16_t* out, int Np, int Kp) {
+    using F = TcFmt<FMT>;
+    __shared__ float t[64][65];
+    const int tn = Np / 64, tk = Kp / 64;
+    const int64_t tiles = (int64_t)tn * tk;
+    for (int64_t b = blockIdx.x; b < tiles; b += gridDim.x) {
+        const int n0 = (int)(b % tn) * 64, k0 = (int)(b / tn) * 64;
+#pragma unroll
+        for (int pass = 0; pass < 4; ++pass) {
+            const int kr = 16 * pass + (int)threadIdx.x / 16, c = 4 * ((int)threadIdx.x % 16);
+            const int k = k0 + kr, n = n0 + c;
+            const f32x4 v = (k < K) ? load4<VEC>(B + (int64_t)k * ldb + n, N - n)
+                                    : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            t[kr][c] = v[0];
+            t[kr][c + 1] = v[1];
+            t[kr][c + 2] = v[2];
+            t[kr][c + 3] = v[3];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int u = (int)threadIdx.x + 256 * j, n = u / 8, o = 8 * (u % 8);
+            const u32x4 v = {F::pack(t[o][n], t[o + 1][n]), F::pack(t[o + 2][n], t[o + 3][n]),
+                             F::pack(t[o + 4][n], t[o + 5][n]), F::pack(t[o + 6][n], t[o + 7][n])};
+            *reinterpret_cast<u32x4*>(out + (int64_t)(n0 + n) * Kp + k0 + o) = v;
+        }
+        __syncthreads();
+    }
+}
+
+template <int BM, int BN, int BK, int NS, int WM, int WN>
+struct Tc16Shape {
+    static constexpr int NW = WM * WN, NT = 64 * NW;
+    static constexpr int KS = BK / 16;           // MFMA k-steps per chunk
+    static constexpr int TWM = BM / WM, TWN = BN / WN;
+    static constexpr int MB = TWM / 32, NB = TWN / 32;
+    static constexpr int ROWB = BK * 2, PR = ROWB / 16;
+    static constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB, STAGE = A_BYTES + B_BYTES;
+    static constexpr int LDS_BYTES = NS * STAGE;
+    static constexpr int DA = A_BYTES / 1024 / NW, DB = B_BYTES / 1024 / NW;   // per wave
+    static constexpr int D = DA + DB;
+    static_assert(BK == 32 || BK == 64, "4 or 8 pieces per LDS row");
+    static_assert(KS % 2 == 0, "operand double buffer returns to slot 0 each chunk");
+    static_assert(NS >= 2 && NS <= 4, "ring depth");
+    static_assert(DA * 1024 * NW == A_BYTES && DB * 1024 * NW == B_BYTES, "whole loads per wave");
+    static_assert(TWM % 32 == 0 && TWN % 32 == 0 && (NB == 1 || NB == 2 || NB == 4), "wave tile");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS of one CU");
+    static_assert((NS - 2) * D <= 63, "s_waitcnt vmcnt range");
+};
+
+// s_waitcnt for at most n outstanding direct loads (n a multiple of d, at
+// most 2d) and every LDS access, then the workgroup barrier.  The barrier is
+// issued as assembly with a memory clobber: the compiler's own barrier would
+// first wait for every outstanding load, draining the ring.
+template <int D>
+__device__ __forceinline__ void wait_loads_and_barrier(int later) {
+    if (later <= 0)
+        __builtin_amdgcn_s_waitcnt(kWaitVm<0>);
+    else if (later == 1)
+        __builtin_amdgcn_s_waitcnt(kWaitVm<D>);
+    else
+        __builtin_amdgcn_s_waitcnt(kWaitVm<2 * D>);
+    asm volatile("s_barrier" ::: "memory");
+}
+
+template <int FMT, int BM, int BN, int BK, int NS, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN) void tc16_kernel(Tc16Args p) {
+    using F = TcFmt<FMT>;
+    using T = Tc16Shape<BM, BN, BK, NS, WM, WN>;
+    constexpr int NW = T::NW, KS = T::KS, ROWB = T::ROWB, PR = T::PR, MB = T::MB, NB = T::NB,
+                  TWM = T::TWM, TWN = T::TWN, DA = T::DA, DB = T::DB;
+    __shared__ __attribute__((aligned(1024))) char lds[T::LDS_BYTES];
+
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    const int l32 = lane & 31, h = lane >> 5;
+    int tm, tn;
+    tile_of(p, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int nk = p.K / BK;   // K is padded to whole chunks
+
+    // Direct load j of this wave fills the 64 consecutive 16-byte slots
+    // (j*NW + wave)*64 .. +63 of the tile; slot g holds row g / PR, stored
+    // piece g % PR, i.e. logical piece (g % PR) ^ swz(row) (8 k values).  B's
+    // LDS rows are in the interleaved column order of the epilogue.
+    int64_t da[DA], db[DB];
+#pragma unroll
+    for (int j = 0; j < DA; ++j) {
+        const int g = (j * NW + wave) * 64 + lane, row = g / PR;
+        da[j] = (int64_t)(m0 + row) * p.ld + 8 * ((g % PR) ^ swz<PR>(row));
+    }
+#pragma unroll
+    for (int j = 0; j < DB; ++j) {
+        const int g = (j * NW + wave) * 64 + lane, lr = g / PR;
+        const int u = lr % TWN, n = n0 + (lr - u) + NB * (u % 32) + u / 32;
+        db[j] = (int64_t)n * p.ld + 8 * ((g % PR) ^ swz<PR>(lr));
+    }
+    auto issue = [&](int kc, int buf) {
+        char* As = lds + buf * T::STAGE;
+        char* Bs = As + T::A_BYTES;
+        const int64_t k0 = (int64_t)kc * BK;
+#pragma unroll
+        for (int j = 0; j < DA; ++j) dma16(p.A + k0 + da[j], As + (j * NW + wave) * 1024);
+#pragma unroll
+        for (int j = 0; j < DB; ++j) dma16(p.B + k0 + db[j], Bs + (j * NW + wave) * 1024);
+    };
+
+    u32x4 fa[2][MB], fb[2][NB];
+    auto frag = [&](const char* base, int row, int s) -> u32x4 {
+        return *reinterpret_cast<const u32x4*>(base + row * ROWB + 16 * ((2 * s + h) ^ swz<PR>(row)));
+    };
+    auto read_step = [&](int buf, int s, int slot) {
+        const char* As = lds + buf * T::STAGE;
+        const char* Bs = As + T::A_BYTES;
+#pragma unroll
+        for (int i = 0; i < MB; ++i) fa[slot][i] = frag(As, wm * TWM + i * 32 + l32, s);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) fb[slot][j] = frag(Bs, wn * TWN + j * 32 + l32, s);
+    };
+
+    f32x16 acc[MB][NB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    // Ring of NS buffers; chunk c lives in buffer c % NS.  Chunk c+NS-1 is
+    // issued at the first k-step of chunk c into the buffer chunk c-1 used
+    // (every wave finished reading it before the barrier that ended chunk
+    // c-1).  The barrier that ends chunk c comes before its last k-step's
+    // MFMAs, once chunk c+1 has landed: loads complete in issue order, so it
+    // is enough that at most the loads of the chunks issued after c+1 are
+    // still outstanding.
+#pragma unroll
+    for (int c = 0; c < NS - 1; ++c)
+        if (c < nk) issue(c, c);
+    wait_loads_and_barrier<T::D>(min(NS - 2, nk - 1));
+    read_step(0, 0, 0);
+    int cur = 0;
+    for (int kt = 0; kt < nk; ++kt) {
+        const int nxt = (cur + 1 == NS) ? 0 : cur + 1;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            if (s == 0 && kt + NS - 1 < nk) issue(kt + NS - 1, (cur == 0) ? NS - 1 : cur - 1);
+            if (s + 1 < KS) {
+                read_step(cur, s + 1, (s + 1) & 1);
+            } else if (kt + 1 < nk) {
+                wait_loads_and_barrier<T::D>(min(NS - 2, nk - 2 - kt));
+                read_step(nxt, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+#pragma unroll
+                for (int j = 0; j < NB; ++j) acc[i][j] = F::mma(fa[s & 1][i], fb[s & 1][j], acc[i][j]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        cur = nxt;
+    }
+
+    // ---- epilogue: C <- alpha*acc + beta*C (beta == 0: C not read) ----
+    const float alpha = p.alpha, beta = p.beta;
+    const int col = n0 + wn * TWN + NB * l32;
+    const int ncols = p.N - col;
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = m0 + wm * TWM + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+            if (row >= p.M || ncols <= 0) continue;
+            float* dst = p.C + (int64_t)row * p.ldc + col;
+            float v[NB];
+#pragma unroll
+            for (int n = 0; n < NB; ++n) v[n] = alpha * acc[i][n][r];
+            if (p.vec_c && ncols >= NB && NB == 4) {
+                if (beta != 0.0f) {
+                    const f32x4 cv = *reinterpret_cast<const f32x4*>(dst);
+                    v[0] += beta * cv[0]; v[1] += beta * cv[1];
+                    v[2] += beta * cv[2]; v[3] += beta * cv[3];
+                }
+                *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
+            } else {
+#pragma unroll
+                for (int n = 0; n < NB; ++n) {
+                    if (n < ncols) {
+                        float o = v[n];
+                        if (beta != 0.0f) o += beta * dst[n];
+                        dst[n] = o;
+                    }
+                }
+            }
+        }
+    }
+}
+
+template <int FMT, int BM, int BN, int BK, int NS, int WM, int WN>
+hipError_t launch_tc16(const Tc16Args& p, hipStream_t stream) {
+    hipLaunchKernelGGL((tc16_kernel<FMT, BM, BN, BK, NS, WM, WN>),
+                       dim3((unsigned)(p.tiles_m * p.tiles_n)), dim3(64 * WM * WN), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_tc_cast(int fmt, const float* A, int64_t lda, bool vec_a, const float* B,
+                          int64_t ldb, bool vec_b, int M, int N, int K, uint16_t* A16,
+                          uint16_t* B16, int Mp, int Np, int Kp, hipStream_t stream) {
+    const int64_t units = (int64_t)Mp * (Kp / 8);
+    const unsigned ga = (unsigned)std::min<int64_t>((units + 255) / 256, 1 << 20);
+    const int64_t tiles = (int64_t)(Np / 64) * (Kp / 64);
+    const unsigned gb = (unsigned)std::min<int64_t>(tiles, 1 << 20);
+#define PHOBOS_CAST(F)                                                                         \
+    do {                                                                                       \
+        if (vec_a)                                                                             \
+            hipLaunchKernelGGL((tc_cast_rows_kernel<F, true>), dim3(ga), dim3(256), 0, stream, \
+                               A, lda, M, K, A16, Mp, Kp);                                     \
+        else                                                                                   \
+            hipLaunchKernelGGL((tc_cast_rows_kernel<F, false>), dim3(ga), dim3(256), 0, stream,\
+                               A, lda, M, K, A16, Mp, Kp);                                     \
+        if (vec_b)                                                                             \
+            hipLaunchKernelGGL((tc_cast_cols_kernel<F, true>), dim3(gb), dim3(256), 0, stream, \
+                               B, ldb, K, N, B16, Np, Kp);                                     \
+        else                                                                                   \
+            hipLaunchKernelGGL((tc_cast_cols_kernel<F, false>), dim3(gb), dim3(256), 0, stream,\
+                               B, ldb, K, N, B16, Np, Kp);                                     \
+    } while (0)
+    if (fmt == SGEMM_TC_F16)
+        PHOBOS_CAST(SGEMM_TC_F16);
+    else
+        PHOBOS_CAST(SGEMM_TC_BF16);
+#undef PHOBOS_CAST
+    return hipGetLastError();
+}
+
+#define PHOBOS_TC16_CFG(FMT, BM, BN, BK, NS, WM, WN)                                        \
+    Tc16Entry{sgemm_config{BM, BN, BK, WM, WN}, NS, 64 * WM * WN,                          \
+              Tc16Shape<BM, BN, BK, NS, WM, WN>::LDS_BYTES,                                 \
+              &launch_tc16<FMT, BM, BN, BK, NS, WM, WN>}
+
+#define PHOBOS_TC16_TABLE(FMT)                                                              \
+    {                                                                                       \
+        PHOBOS_TC16_CFG(FMT, 256, 256, 32, 4, 2, 2), PHOBOS_TC16_CFG(FMT, 256, 256, 32, 4, 4, 2), \
+            PHOBOS_TC16_CFG(FMT, 256, 256, 64, 2, 2, 2), PHOBOS_TC16_CFG(FMT, 256, 256, 64, 2, 4, 2), \
+            PHOBOS_TC16_CFG(FMT, 256, 128, 32, 4, 2, 2), PHOBOS_TC16_CFG(FMT, 128, 128, 64, 2, 2, 2), \
+    }
+
+const Tc16Entry* tc16_kernel_table(int fmt, int* count) {
+    static const Tc16Entry f16[] = PHOBOS_TC16_TABLE(SGEMM_TC_F16);
+    static const Tc16Entry bf16[] = PHOBOS_TC16_TABLE(SGEMM_TC_BF16);
+    *count = (int)(sizeof(f16) / sizeof(f16[0]));
+    if (fmt == SGEMM_TC_F16) return f16;
+    if (fmt == SGEMM_TC_BF16) return bf16;
+    *count = 0;
+    return nullptr;
+}
+
+// The compiled configurations of the matrix-core variant, per input format;
+// nullptr for an unknown format.
 const KernelEntry* tc_kernel_table(int fmt, int* count) {
     static const KernelEntry f16[] = PHOBOS_TC_TABLE(SGEMM_TC_F16);
     static const KernelEntry bf16[] = PHOBOS_TC_TABLE(SGEMM_TC_BF16);

@@ -166,12 +166,24 @@ int sgemm_tune(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_
  * keeps an fp32 accumulator).  sgemm_tc computes
  *     C <- alpha * A' * B' + beta * C
  * where A' and B' are A and B with every element rounded to the 16-bit
- * format `fmt` as it is loaded: SGEMM_TC_F16 (IEEE binary16) or
- * SGEMM_TC_BF16 (bfloat16), round to nearest even, values past the format's
- * range becoming infinities.  The products of the rounded values are exact
- * and are accumulated in fp32 by the 16-bit matrix instructions
+ * format `fmt`: SGEMM_TC_F16 (IEEE binary16) or SGEMM_TC_BF16 (bfloat16),
+ * round to nearest even, values past the format's range becoming
+ * infinities.  The products of the rounded values are exact and are
+ * accumulated in fp32 by the 16-bit matrix instructions
  * (v_mfma_f32_32x32x16_f16 / _bf16); alpha, beta, C and the epilogue are
  * fp32.  A, B and C stay fp32 in memory.
+ *
+ * Two forms compute it.  Fused: the GEMM rounds each element as it loads it
+ * (rounding on load, as on the pages).  Staged: a cast pass first rounds A
+ * and B once into a 16-bit workspace laid out for the GEMM (A row-major, B
+ * transposed, zero-padded to multiples of 256 rows and 64 columns of k),
+ * then the 16-bit GEMM streams it into LDS.  Both round with the same
+ * conversion.  The workspace, (ceil256(M) + ceil256(N)) * ceil64(K) * 2
+ * bytes, comes from a stream-ordered memory pool of the library's own on
+ * the current device (allocated and freed on `stream`; the pool keeps freed
+ * memory for later calls); when it cannot be allocated the fused form runs
+ * instead.  Large products (M, N >= 2048 and K >= 1024) take the staged form
+ * by default.
  *
  * Accuracy: within 2*K*2^-24 * (|alpha| sum_k |A'[i][k]| |B'[k][j]| +
  * |beta C[i][j]|) of the exact value of the expression above.  Against the
@@ -181,23 +193,28 @@ int sgemm_tune(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_
  *
  * Arguments 1..11, quick returns (M or N = 0: nothing; K = 0 or alpha = 0:
  * C <- beta*C, A and B not read), streams and errors as sgemm; 12 fmt (-12
- * if unknown), 13 stream.  Tile configurations: sgemm_tc_config_count and
- * sgemm_tc_config_at list those compiled for a format (bk = 32 always),
- * sgemm_tc_get_config reports the one an M x N call would launch, and
- * sgemm_tc_set_config forces one for every later call with that format
- * (NULL: back to the built-in choice; process-wide, not thread-safe against
- * concurrent calls).
+ * if unknown), 13 stream.  Tile configurations (sgemm_tc_config: the tile,
+ * and `staged` 1 for the staged form): sgemm_tc_config_count and
+ * sgemm_tc_config_at list those compiled for a format, sgemm_tc_get_config
+ * reports the one an M x N x K call would use, and sgemm_tc_set_config
+ * forces one for every later call with that format (NULL: back to the
+ * built-in choice; process-wide, not thread-safe against concurrent calls).
  */
 #define SGEMM_TC_F16 1
 #define SGEMM_TC_BF16 2
+
+typedef struct sgemm_tc_config {
+    int32_t bm, bn, bk, wm, wn;
+    int32_t staged;   /* 0: rounding on load; 1: cast pass + 16-bit GEMM */
+} sgemm_tc_config;
 
 int sgemm_tc(int64_t M, int64_t N, int64_t K, float alpha, const float* A, int64_t lda,
              const float* B, int64_t ldb, float beta, float* C, int64_t ldc, int32_t fmt,
              void* stream);
 int sgemm_tc_config_count(int32_t fmt);
-int sgemm_tc_config_at(int32_t fmt, int32_t index, sgemm_config* out);
-int sgemm_tc_get_config(int32_t fmt, int64_t M, int64_t N, sgemm_config* out);
-int sgemm_tc_set_config(int32_t fmt, const sgemm_config* cfg);
+int sgemm_tc_config_at(int32_t fmt, int32_t index, sgemm_tc_config* out);
+int sgemm_tc_get_config(int32_t fmt, int64_t M, int64_t N, int64_t K, sgemm_tc_config* out);
+int sgemm_tc_set_config(int32_t fmt, const sgemm_tc_config* cfg);
 
 /*
  * Host-resident super-tiled SGEMM, the single-GPU form of the pages' cluster
@@ -289,7 +306,8 @@ int sgemm_supertiled_host(int64_t M, int64_t N, int64_t K, float alpha,
  */
 #define SGEMM_KIND_GEMM 0
 #define SGEMM_KIND_INIT_LEAF 1
-#define SGEMM_KIND_TC 2
+#define SGEMM_KIND_TC 2          /* the matrix-core GEMM (either form) */
+#define SGEMM_KIND_TC_CAST 3     /* the cast pass of its staged form */
 int sgemm_trace_begin(int64_t capacity);
 int sgemm_trace_end(float* ms_out, int32_t* kind_out, int64_t cap, int64_t* n_out);
 

@@ -186,18 +186,24 @@ def test_tc_argument_checks(args, want):
 def test_tc_configs():
     for fmt in (g.SGEMM_TC_F16, g.SGEMM_TC_BF16):
         cfgs = g.tc_configs(fmt)
-        assert len(cfgs) >= 5
-        assert all(c.bk == 32 and c.bm % (32 * c.wm) == 0 and c.bn % (32 * c.wn) == 0
+        assert len(cfgs) >= 8
+        assert any(c.staged for c in cfgs) and any(not c.staged for c in cfgs)
+        assert all(c.bk in (32, 64) and c.bm % (32 * c.wm) == 0 and c.bn % (32 * c.wn) == 0
                    for c in cfgs)
-        # large problems take the 256 x 256 tile, small ones a small tile
-        assert g.sgemm_tc_get_config(fmt, 16384, 16384).as_tuple()[:2] == (256, 256)
-        assert g.sgemm_tc_get_config(fmt, 64, 64).as_tuple()[:2] == (64, 64)
-        g.sgemm_tc_set_config(fmt, cfgs[-1])
-        assert g.sgemm_tc_get_config(fmt, 16384, 16384).as_tuple() == cfgs[-1].as_tuple()
+        # staged tiles divide the 256 x 256 x 64 padding of the workspace
+        assert all(256 % c.bm == 0 and 256 % c.bn == 0 and 64 % c.bk == 0
+                   for c in cfgs if c.staged)
+        # large products take the staged form, small ones a small fused tile
+        big = g.sgemm_tc_get_config(fmt, 16384, 16384, 16384)
+        assert big.staged == 1 and (big.bm, big.bn) == (256, 256)
+        small = g.sgemm_tc_get_config(fmt, 64, 64, 64)
+        assert small.staged == 0 and (small.bm, small.bn) == (64, 64)
+        g.sgemm_tc_set_config(fmt, cfgs[0])
+        assert g.sgemm_tc_get_config(fmt, 16384, 16384, 16384).as_tuple() == cfgs[0].as_tuple()
         g.sgemm_tc_set_config(fmt, None)
         with pytest.raises(RuntimeError):
-            g.sgemm_tc_set_config(fmt, (48, 48, 32, 1, 1))
+            g.sgemm_tc_set_config(fmt, (48, 48, 32, 1, 1, 0))
     lib = g.lib()
     assert lib.sgemm_tc_config_count(0) == -1
     assert lib.sgemm_tc_config_at(1, 999, None) == -2
-    assert lib.sgemm_tc_get_config(7, 4, 4, None) == -1
+    assert lib.sgemm_tc_get_config(7, 4, 4, 4, None) == -1

@@ -29,8 +29,9 @@ def test_oracle_and_library_agree_on_format_ids():
 
 @pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)
 def test_every_config_tile_edges(fmt):
-    """Each compiled tile, forced, on shapes that cut its tiles on every edge,
-    with padded leading dimensions (NaN pads in A and B, sentinel pads in C)."""
+    """Each compiled tile of both forms, forced, on shapes that cut its tiles
+    on every edge, with padded leading dimensions (NaN pads in A and B,
+    sentinel pads in C)."""
     for cfg in g.tc_configs(fmt):
         bm, bn = cfg.bm, cfg.bn
         g.sgemm_tc_set_config(fmt, cfg)
@@ -45,19 +46,29 @@ def test_every_config_tile_edges(fmt):
                 gu.check_full(w, x, out, fmt=fmt)
 
 
+FUSED = (256, 256, 32, 4, 2, 0)
+STAGED = (256, 256, 32, 4, 2, 1)
+FORMS = [None, FUSED, STAGED]
+FORM_IDS = ["default", "fused", "staged"]
+
+
+@pytest.mark.parametrize("form", FORMS, ids=FORM_IDS)
 @pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)
-def test_unaligned_leading_dimensions(fmt):
-    """Odd leading dimensions: the scalar-load kernels."""
+def test_unaligned_leading_dimensions(fmt, form):
+    """Odd leading dimensions: the scalar-load kernels and cast pass."""
+    g.sgemm_tc_set_config(fmt, form)
     w = wl.custom(301, 279, 203, -0.5, 2.0, seed=5, lda=205, ldb=281, ldc=283)
     x = wl.make_inputs(w)
     out = gu.run(w, x, fmt=fmt)
     gu.check_full(w, x, out, fmt=fmt)
 
 
+@pytest.mark.parametrize("form", FORMS, ids=FORM_IDS)
 @pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)
-def test_integer_inputs_are_exact(fmt):
+def test_integer_inputs_are_exact(fmt, form):
     """Integers -3..3 are exact in both formats and every partial sum is below
     2^24: the variant must give the exact product, equal to the fp32 oracle."""
+    g.sgemm_tc_set_config(fmt, form)
     w = wl.custom(513, 300, 700, 1.5, 0.5, ("I7", "I7", "I7"), seed=6, lda=704, ldb=300, ldc=304)
     x = wl.make_inputs(w)
     out = gu.run(w, x, fmt=fmt)
@@ -77,6 +88,24 @@ def test_quick_returns(fmt):
             np.zeros((w.M, w.N), np.float32)
         assert np.array_equal(gu.logical_c(w, out).view(np.int32), want.view(np.int32))
         gu.check_pads(w, x, out)
+
+
+@pytest.mark.parametrize("shape", [(1000, 777, 300), (512, 512, 1024), (300, 1100, 70)])
+@pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)
+def test_staged_equals_fused(fmt, shape):
+    """Same tile, same k order, same conversion: the staged form (cast pass +
+    16-bit GEMM) gives the fused form's values exactly."""
+    M, N, K = shape
+    w = wl.custom(M, N, K, 0.75, -1.25, seed=M + K, lda=K + 3, ldb=N + 1, ldc=N + 5)
+    x = wl.make_inputs(w)
+    g.sgemm_tc_set_config(fmt, FUSED)
+    fused = gu.logical_c(w, gu.run(w, x, fmt=fmt))
+    g.sgemm_tc_set_config(fmt, STAGED)
+    staged_out = gu.run(w, x, fmt=fmt)
+    staged = gu.logical_c(w, staged_out)
+    bad = np.argwhere(fused != staged)
+    assert bad.size == 0, f"{len(bad)} elements differ, first {bad[:5].tolist()}"
+    gu.check_full(w, x, staged_out, fmt=fmt)
 
 
 def test_values_past_the_fp16_range_become_infinite():
@@ -133,6 +162,16 @@ def test_side_stream_and_trace(fmt):
                stream=s)
     ms, kinds, n = g.sgemm_trace_end()
     assert n == 1 and kinds == [g.SGEMM_KIND_TC] and ms[0] > 0
+    s.synchronize()
+    gu.check_full(w, x, dC.cpu().numpy(), fmt=fmt)
+    # the staged form: the cast pass, then the GEMM, on the same stream
+    g.sgemm_tc_set_config(fmt, STAGED)
+    dC = gu.to_dev(x.C)
+    g.sgemm_trace_begin(16)
+    g.sgemm_tc(w.M, w.N, w.K, w.alpha, dA, w.lda, dB, w.ldb, w.beta, dC, w.ldc, fmt=fmt,
+               stream=s)
+    ms, kinds, n = g.sgemm_trace_end()
+    assert n == 2 and kinds == [g.SGEMM_KIND_TC_CAST, g.SGEMM_KIND_TC]
     s.synchronize()
     gu.check_full(w, x, dC.cpu().numpy(), fmt=fmt)
 
