@@ -21,7 +21,11 @@ tuner on the step shape first (untimed) and times the winner;
 --host-resident MIB keeps A, B and C in pinned host memory and times
 sgemm_supertiled_host with the planner's plan for a device budget of MIB MiB
 (a rate that includes every host<->device transfer; the workload's own
-super-tile extents are replaced by the plan's).  For profiling
+super-tile extents are replaced by the plan's); --tc f16|bf16 times the
+matrix-core variant sgemm_tc (A and B rounded to that format, fp32
+accumulation) as one monolithic call per step on the same inputs, its
+cast pass included, with the roofline of its 16-bit GEMM kernel against the
+16-bit matrix peak.  For profiling
 runs: --copy-calibration runs one plain device copy of 1 GiB first (a
 known-size reference for the HBM byte counters); --skip-cpu-baseline leaves
 the oracle leg out.
@@ -39,6 +43,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_FP32_MFMA_TFLOPS = 157.3     # MI355X published dense FP32 matrix peak
 PEAK_HBM_GBS = 8000.0             # MI355X published HBM3E bandwidth
+PEAK_F16_MFMA_TFLOPS = 2500.0     # MI355X published dense fp16 / bf16 matrix peak
 DEFAULT_WORKLOAD = "supertiled_16384_t4096"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sgemm_step_4096_ld16384.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "fp32_gemm_02_amd", "csrc", "sgemm_kernels.hip")]
@@ -70,8 +75,9 @@ def measured_traffic(workload):
     return float(m_bytes.group(1))
 
 
-def cpu_baseline(x, w, target_s=15.0):
-    """The oracle as it stands, on a slab of rows of the same product."""
+def cpu_baseline(x, w, target_s=15.0, fmt=None):
+    """The oracle as it stands, on a slab of rows of the same product (fmt:
+    the oracle of the matrix-core variant)."""
     import oracle
 
     orc = oracle.default()
@@ -80,12 +86,18 @@ def cpu_baseline(x, w, target_s=15.0):
     def run(rows):
         t0 = time.perf_counter()
         orc.sgemm(rows, w.N, w.K, w.alpha, x.A, x.B, w.beta, x.C, lda=w.lda, ldb=w.ldb,
-                  ldc=w.ldc)
+                  ldc=w.ldc, fmt=fmt)
         return time.perf_counter() - t0
 
-    probe_rows = max(8, threads)
-    t = run(probe_rows)
-    rows = int(min(w.M, max(probe_rows, probe_rows * target_s / max(t, 1e-3))))
+    # two probes give the per-row time and any fixed cost (the variant's
+    # oracle rounds all of B first); the sample is sized from both
+    r1 = max(8, threads)
+    t1 = run(r1)
+    r2 = min(w.M, 4 * r1)
+    t2 = run(r2)
+    per_row = max((t2 - t1) / max(r2 - r1, 1), 1e-6)
+    fixed = max(t1 - per_row * r1, 0.0)
+    rows = int(min(w.M, max(r1, (target_s - fixed) / per_row)))
     rows = max(threads, rows - rows % max(1, threads))
     t = run(rows)
     return {
@@ -94,7 +106,8 @@ def cpu_baseline(x, w, target_s=15.0):
         "cores": threads,
         "kind": "oracle",
         "sample": f"rows 0..{rows - 1} of the {w.M}x{w.N}x{w.K} product "
-                  f"({rows}x{w.N}x{w.K}, {t:.1f} s, fp64 accumulation and bound)",
+                  f"({rows}x{w.N}x{w.K}, {t:.1f} s, fp64 accumulation and bound"
+                  + (", inputs rounded to the 16-bit format" if fmt else "") + ")",
     }
 
 
@@ -106,6 +119,7 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--tune", action="store_true")
     ap.add_argument("--host-resident", type=int, default=None, metavar="MIB")
+    ap.add_argument("--tc", choices=("f16", "bf16"), default=None)
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -127,6 +141,12 @@ def main():
     w = wl.BY_NAME[args.workload]
     supertiled = w.entry == "sgemm_supertiled"
     host = args.host_resident is not None
+    tc = {"f16": g.SGEMM_TC_F16, "bf16": g.SGEMM_TC_BF16}.get(args.tc)
+    if tc is not None:
+        if host:
+            print("--tc and --host-resident do not combine", file=sys.stderr)
+            sys.exit(2)
+        supertiled = False   # one monolithic sgemm_tc call per step
     plan = None
     if host:
         if not supertiled:
@@ -159,7 +179,10 @@ def main():
     stream.synchronize()
 
     def step():
-        if host:
+        if tc is not None:
+            g.sgemm_tc(w.M, w.N, w.K, w.alpha, dA, w.lda, dB, w.ldb, w.beta, dC, w.ldc, fmt=tc,
+                       stream=stream)
+        elif host:
             g.sgemm_supertiled_host(w.M, w.N, w.K, w.alpha, dA, w.lda, dB, w.ldb, w.beta, dC,
                                     w.ldc, plan, stream=stream)
         elif supertiled:
@@ -170,7 +193,7 @@ def main():
                     stream=stream)
 
     tuned = None
-    if args.tune:
+    if args.tune and tc is None:
         tuned, _ = g.sgemm_tune(*step_shape, w.lda, w.ldb, w.ldc, reps=10, stream=stream)
 
     for _ in range(args.warmup):
@@ -179,6 +202,8 @@ def main():
 
     if supertiled:
         launches_per_step = (-(-w.M // tiles[0])) * (-(-w.N // tiles[1])) * (-(-w.K // tiles[2]))
+    elif tc is not None:
+        launches_per_step = 1 + g.sgemm_tc_get_config(tc, w.M, w.N, w.K).staged   # cast pass
     else:
         launches_per_step = 1
     g.sgemm_trace_begin(args.steps * launches_per_step * 2 + 16)
@@ -198,11 +223,14 @@ def main():
     ms_per_step = ms_total / args.steps
     value = gflops(w.M, w.N, w.K, ms_per_step)
 
-    step_ms = [t for t, k in zip(ms_kern, kinds) if k == g.SGEMM_KIND_GEMM]
+    dominant = g.SGEMM_KIND_TC if tc is not None else g.SGEMM_KIND_GEMM
+    step_ms = [t for t, k in zip(ms_kern, kinds) if k == dominant]
+    cast_ms = [t for t, k in zip(ms_kern, kinds) if k == g.SGEMM_KIND_TC_CAST]
     avg_launch_ms = float(np.mean(step_ms))
     step_flops = 2.0 * step_shape[0] * step_shape[1] * step_shape[2]
     achieved_tflops = step_flops / (avg_launch_ms * 1e-3) / 1e12
-    traffic = None if host else measured_traffic(args.workload)
+    traffic = None if (host or tc is not None) else measured_traffic(args.workload)
+    peak = PEAK_FP32_MFMA_TFLOPS if tc is None else PEAK_F16_MFMA_TFLOPS
 
     out = {
         "metric": "SGEMM GFLOP/s and % of MI355X FP32 matrix peak at 16384^3, 1 GPU",
@@ -217,8 +245,10 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": w.name + ("_host_resident" if host else ""),
-                   "entry": "sgemm_supertiled_host" if host else w.entry,
+        "config": {"workload": (f"tc_{args.tc}_{w.M}" if tc is not None else
+                                w.name + ("_host_resident" if host else "")),
+                   "entry": ("sgemm_tc" if tc is not None else
+                             "sgemm_supertiled_host" if host else w.entry),
                    "M": w.M, "N": w.N, "K": w.K,
                    "lda": w.lda, "ldb": w.ldb, "ldc": w.ldc,
                    **(dict(zip(("TM", "TN", "TK"), tiles)) if supertiled else {}),
@@ -230,18 +260,30 @@ def main():
                       if host else {}),
                    "alpha": w.alpha, "beta": w.beta,
                    "inputs": "A/B/C %s/%s/%s, seed %d" % (*w.dists, w.seed),
-                   "leaf_config": "bm=%d bn=%d bk=%d wm=%d wn=%d" %
-                   g.sgemm_get_config(*step_shape, w.lda, w.ldb, w.ldc).as_tuple(),
+                   "leaf_config": (
+                       "bm=%d bn=%d bk=%d wm=%d wn=%d staged=%d" %
+                       g.sgemm_tc_get_config(tc, w.M, w.N, w.K).as_tuple() if tc is not None else
+                       "bm=%d bn=%d bk=%d wm=%d wn=%d" %
+                       g.sgemm_get_config(*step_shape, w.lda, w.ldb, w.ldc).as_tuple()),
                    "tuned": tuned is not None,
                    "launches_per_step": launches_per_step,
-                   "pct_of_fp32_matrix_peak": round(100.0 * value / 1e3 / PEAK_FP32_MFMA_TFLOPS, 2)},
+                   **({"cast_pass_ms": round(float(np.mean(cast_ms)), 4) if cast_ms else 0.0,
+                       "gemm_ms": round(avg_launch_ms, 4),
+                       "inputs_rounded_to": args.tc,
+                       "pct_of_f16_matrix_peak": round(100.0 * value / 1e3 / PEAK_F16_MFMA_TFLOPS, 2)}
+                      if tc is not None else
+                      {"pct_of_fp32_matrix_peak": round(100.0 * value / 1e3 / PEAK_FP32_MFMA_TFLOPS, 2)})},
         "roofline": {"bound": "mfma", "achieved": round(achieved_tflops, 2),
-                     "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved_tflops / PEAK_FP32_MFMA_TFLOPS, 4),
+                     "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved_tflops / peak, 4),
                      "traffic": traffic},
     }
+    if tc is not None:
+        out["metric"] = ("SGEMM GFLOP/s of the matrix-core variant (inputs rounded to %s, fp32 "
+                         "accumulation) at %d^3, 1 GPU" % (args.tc, w.M))
+        out["dtype"] = args.tc
     if not args.skip_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(x, w)
+        out["cpu_baseline"] = cpu_baseline(x, w, fmt=tc)
     if tuned is not None:
         g.sgemm_set_config(None)
     print(f"# timed {args.steps} steps: {ms_total:.2f} ms on the stream ({wall * 1e3:.2f} ms "
