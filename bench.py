@@ -46,7 +46,8 @@ PEAK_HBM_GBS = 8000.0             # MI355X published HBM3E bandwidth
 PEAK_F16_MFMA_TFLOPS = 2500.0     # MI355X published dense fp16 / bf16 matrix peak
 DEFAULT_WORKLOAD = "supertiled_16384_t4096"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sgemm_step_4096_ld16384.txt")
-KERNEL_SOURCES = [os.path.join(ROOT, "fp32_gemm_02_amd", "csrc", "sgemm_kernels.hip")]
+KERNEL_SOURCES = [os.path.join(ROOT, "fp32_gemm_02_amd", "csrc", f)
+                  for f in ("sgemm_kernels.hip", "sgemm_device.h")]
 
 
 def gflops(M, N, K, ms):
