@@ -1,5 +1,6 @@
-"""CPU oracle for C = alpha*A*B + beta*C (test infrastructure only), and for its
-matrix-core variant with A and B rounded to fp16 or bf16 first.
+"""CPU oracle for C = alpha*A*B + beta*C (test infrastructure only), for its
+matrix-core variant with A and B rounded to fp16 or bf16 first, and for the
+pages' second example, attention O = softmax(scale*Q K^T) V.
 
 Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package.  The GPU library and its Python binding
@@ -21,15 +22,16 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "sgemm_oracle.c")
+_SRC_ATT = os.path.join(_HERE, "attention_oracle.c")
 LIB_PATH = os.path.join(_HERE, "libsgemm_oracle.so")
 
-def build(force=True, src=_SRC, out=LIB_PATH):
+def build(force=True, src=_SRC, out=LIB_PATH, src_att=_SRC_ATT):
     """Compile the oracle with gcc (no fast-math, no FMA contraction)."""
     if not force and os.path.exists(out):
         return out
     tmp = out + ".tmp"
     cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
-           "-std=c11", "-shared", "-fPIC", src, "-o", tmp, "-lm"]
+           "-std=c11", "-shared", "-fPIC", src, src_att, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
     return out
@@ -75,6 +77,9 @@ class Oracle:
         lib.oracle_sgemm_tc.restype = ctypes.c_int
         lib.oracle_sgemm_tc_entries.argtypes = [ctypes.c_int] + lib.oracle_sgemm_entries.argtypes
         lib.oracle_sgemm_tc_entries.restype = ctypes.c_int
+        lib.oracle_attention_rows.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, f32,
+                                              i64, vp, vp, i64, vp, i64]
+        lib.oracle_attention_rows.restype = ctypes.c_int
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = ctypes.c_int
         self.lib = lib
@@ -140,6 +145,28 @@ class Oracle:
         return out, bnd
 
 
+    def attention(self, Nq, Nk, D, Q, K, V, scale, rows=None, ldq=None, ldk=None, ldv=None,
+                  bound=True):
+        """Rows of O = softmax(scale*Q K^T) V (all rows when rows is None), as a
+        float32 (len(rows) x D) array, and their bound (float64) or None."""
+        ldq = _ld_of(Q, D) if ldq is None else ldq
+        ldk = _ld_of(K, D) if ldk is None else ldk
+        ldv = _ld_of(V, D) if ldv is None else ldv
+        q = _buf(Q, Nq, D, ldq, "Q")
+        k = _buf(K, Nk, D, ldk, "K")
+        v = _buf(V, Nk, D, ldv, "V")
+        r = np.arange(Nq, dtype=np.int64) if rows is None else \
+            np.ascontiguousarray(rows, dtype=np.int64).reshape(-1)
+        out = np.empty((r.size, D), dtype=np.float32)
+        bnd = np.empty((r.size, D), dtype=np.float64) if bound else None
+        rc = self.lib.oracle_attention_rows(Nq, Nk, D, _ptr(q), ldq, _ptr(k), ldk, _ptr(v), ldv,
+                                            float(scale), r.size, _ptr(r), _ptr(out), D,
+                                            _ptr(bnd), D)
+        if rc != 0:
+            raise RuntimeError(f"oracle_attention_rows failed with code {rc}")
+        return out, bnd
+
+
 # Input formats of the matrix-core variant.
 F16 = 1
 BF16 = 2
@@ -169,3 +196,7 @@ def sgemm_entries(*args, **kwargs):
 
 def round_to(fmt, x):
     return default().round(fmt, x)
+
+
+def attention(*args, **kwargs):
+    return default().attention(*args, **kwargs)

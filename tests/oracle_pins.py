@@ -415,7 +415,155 @@ def check_tc_entries(orc):
         assert np.array_equal(got, full[r, c]) and np.array_equal(gb, fb[r, c]), fmt
 
 
+# --------------------------------------------------------------------------
+# Attention, O = softmax(scale * Q K^T) V over the keys (the pages' second
+# @cluster example; the body is the FlashAttention paper's exact attention).
+def _att_inputs(rng, Nq, Nk, D, dist="n"):
+    f = (lambda s: rng.standard_normal(s)) if dist == "n" else (lambda s: rng.uniform(-1, 1, s))
+    return (f((Nq, D)).astype(np.float32), f((Nk, D)).astype(np.float32),
+            f((Nk, D)).astype(np.float32))
+
+
+def _att_fp64(Q, K, V, scale):
+    """numpy/scipy in fp64: scipy's softmax over the keys, then the product."""
+    from scipy.special import softmax
+    S = np.float64(np.float32(scale)) * (Q.astype(np.float64) @ K.astype(np.float64).T)
+    return softmax(S, axis=1) @ V.astype(np.float64)
+
+
+def check_att_library(orc):
+    """Against scipy's softmax in fp64, rounded once: within half an ulp plus
+    fp64 noise, on shapes with Nk != D and scales of both signs."""
+    rng = _rng(31)
+    for Nq, Nk, D, scale in [(9, 50, 64, 0.125), (5, 3, 64, 1.0), (17, 200, 16, -0.3),
+                             (4, 129, 64, 0.7)]:
+        Q, K, V = _att_inputs(rng, Nq, Nk, D)
+        got, _ = orc.attention(Nq, Nk, D, Q, K, V, scale)
+        ref = _att_fp64(Q, K, V, scale)
+        assert np.all(np.abs(got - ref) <= 2.0 ** -24 * np.abs(ref) + 1e-12), (Nq, Nk, D)
+
+
+def check_att_closed_forms(orc):
+    rng = _rng(32)
+    D = 64
+    Q, K, V = _att_inputs(rng, 6, 40, D)
+    # one key: every weight is 1, the output is that key's value row, exactly
+    got, _ = orc.attention(6, 1, D, Q, K[:1], V[:1], 0.125)
+    assert np.array_equal(got, np.repeat(V[:1], 6, axis=0))
+    # scale 0, or identical keys: uniform weights, the mean of the value rows
+    want = V.astype(np.float64).mean(axis=0).astype(np.float32)
+    got, _ = orc.attention(6, 40, D, Q, K, V, 0.0)
+    assert np.all(ulp_diff(got, np.repeat(want[None], 6, axis=0)) <= 1)
+    Ks = np.repeat(K[:1], 40, axis=0)
+    got, _ = orc.attention(6, 40, D, Q, Ks, V, 0.9)
+    assert np.all(ulp_diff(got, np.repeat(want[None], 6, axis=0)) <= 1)
+    # one dominant key (score gap above 745: the others' weights are 0 in fp64)
+    Qd = np.zeros((3, D), np.float32)
+    Qd[:, 0] = 1.0
+    Kd = np.zeros((40, D), np.float32)
+    Kd[17, 0] = 1000.0
+    got, _ = orc.attention(3, 40, D, Qd, Kd, V, 1.0)
+    assert np.array_equal(got, np.repeat(V[17:18], 3, axis=0))
+
+
+def check_att_invariances(orc):
+    """A shift of all of a row's scores (through a coordinate every key shares)
+    and a permutation of the keys leave the output unchanged."""
+    rng = _rng(33)
+    Nq, Nk, D = 8, 90, 64
+    Q, K, V = _att_inputs(rng, Nq, Nk, D)
+    Q[:, 5] = 0.0
+    K[:, 5] = 1.0
+    base, _ = orc.attention(Nq, Nk, D, Q, K, V, 0.125)
+    Qs = Q.copy()
+    Qs[:, 5] = np.linspace(1e4, 3e4, Nq, dtype=np.float32)   # scores shifted by 1250..3750
+    shifted, _ = orc.attention(Nq, Nk, D, Qs, K, V, 0.125)
+    assert np.all(np.isfinite(shifted)) and np.all(ulp_diff(shifted, base) <= 4)
+    perm = rng.permutation(Nk)
+    permuted, _ = orc.attention(Nq, Nk, D, Q, K[perm], V[perm], 0.125)
+    assert np.all(ulp_diff(permuted, base) <= 2)
+
+
+def check_att_bound_covers_fp32(orc):
+    """A plain fp32 attention (numpy float32: scores, running maximum, exp, sums)
+    lies within the oracle's bound, and the bound is not vacuous."""
+    rng = _rng(34)
+    for Nq, Nk, D, scale, dist in [(16, 300, 64, 0.125, "n"), (8, 1000, 64, 1.0, "u"),
+                                   (8, 64, 16, 2.0, "n")]:
+        Q, K, V = _att_inputs(rng, Nq, Nk, D, dist)
+        got, bnd = orc.attention(Nq, Nk, D, Q, K, V, scale)
+        S = (Q @ K.T) * np.float32(scale)
+        P = np.exp(S - S.max(axis=1, keepdims=True))
+        O32 = (P @ V) / P.sum(axis=1, keepdims=True, dtype=np.float32)
+        ref = _att_fp64(Q, K, V, scale)
+        assert np.all(np.abs(O32.astype(np.float64) - ref) <= bnd), (Nq, Nk, D)
+        assert np.all(np.abs(got.astype(np.float64) - ref) <= bnd)
+        # not vacuous: far below the scale of the values themselves
+        assert bnd.max() < 1e-2 * np.abs(V).max()
+
+
+def _att_fp32_sequential(Q, K, V, scale):
+    """Attention in fp32 with sequential (left to right) sums: dot products,
+    weight sum and weighted sum accumulated one term at a time."""
+    Q, K, V = (np.asarray(a, np.float32) for a in (Q, K, V))
+    prod = Q[:, None, :] * K[None, :, :]                       # exact-ish fp32 products
+    S = np.cumsum(prod, axis=2, dtype=np.float32)[:, :, -1] * np.float32(scale)
+    P = np.exp(S - S.max(axis=1, keepdims=True)).astype(np.float32)
+    l = np.cumsum(P, axis=1, dtype=np.float32)[:, -1:]
+    out = np.empty((Q.shape[0], V.shape[1]), np.float32)
+    for i in range(Q.shape[0]):
+        out[i] = np.cumsum(P[i][:, None] * V, axis=0, dtype=np.float32)[-1] / l[i]
+    return out
+
+
+def check_att_bound_needs_every_term(orc):
+    """Sequential fp32 sums stay within the bound where each of its terms is
+    needed: long key ranges (the output and weight sums drift by many ulps)
+    and scores with a large common part (the dot products' rounding changes
+    the weights)."""
+    rng = _rng(36)
+    # 50k keys, uniform weights, values near 1: the running fp32 sum drifts
+    Nq, Nk, D = 2, 50000, 8
+    Q = np.zeros((Nq, D), np.float32)
+    K = np.zeros((Nk, D), np.float32)
+    V = rng.uniform(0.5, 1.5, (Nk, D)).astype(np.float32)
+    _, bnd = orc.attention(Nq, Nk, D, Q, K, V, 1.0)
+    ref = _att_fp64(Q, K, V, 1.0)
+    got = _att_fp32_sequential(Q, K, V, 1.0)
+    err = np.abs(got.astype(np.float64) - ref)
+    assert np.all(err <= bnd) and err.max() > 64 * 2.0 ** -24 * np.abs(ref).max()
+    # every score = 2^20 + 63 terms below 1.5: each fp32 addition onto 2^20
+    # loses up to 1/16, so the scores, and with them the weights, differ from
+    # the exact ones far more than the scores' own rounding (u*|S|) would
+    # allow; only the dot products' error term (2*D*u*sum|q*k|) covers it
+    rng = _rng(36)
+    Nq, Nk, D = 16, 64, 64
+    Q = np.ones((Nq, D), np.float32)
+    Q[:, 0] = 2.0 ** 20
+    Q[:, 1:] = rng.uniform(0.5, 1.5, (Nq, D - 1)).astype(np.float32)
+    K = rng.uniform(0, 1, (Nk, D)).astype(np.float32)
+    K[:, 0] = 1.0
+    V = rng.standard_normal((Nk, D)).astype(np.float32)
+    _, bnd = orc.attention(Nq, Nk, D, Q, K, V, 1.0)
+    ref = _att_fp64(Q, K, V, 1.0)
+    got = _att_fp32_sequential(Q, K, V, 1.0)
+    err = np.abs(got.astype(np.float64) - ref)
+    assert np.all(err <= bnd) and err.max() > 0.1
+
+
+def check_att_rows(orc):
+    """Selected rows equal the same rows of the full output."""
+    rng = _rng(35)
+    Q, K, V = _att_inputs(rng, 40, 77, 64)
+    full, fb = orc.attention(40, 77, 64, Q, K, V, 0.2)
+    rows = np.array([39, 0, 17, 17, 5])
+    got, gb = orc.attention(40, 77, 64, Q, K, V, 0.2, rows=rows)
+    assert np.array_equal(got, full[rows]) and np.array_equal(gb, fb[rows])
+
+
 ALL_CHECKS = [check_golden, check_exact_dyadic, check_exact_general,
               check_bound_covers_fp32_loop, check_closed_forms, check_integer_exact,
               check_numpy_fp64, check_entries, check_round_golden, check_round_libraries,
-              check_tc_exact, check_tc_representable, check_tc_entries]
+              check_tc_exact, check_tc_representable, check_tc_entries, check_att_library,
+              check_att_closed_forms, check_att_invariances, check_att_bound_covers_fp32,
+              check_att_bound_needs_every_term, check_att_rows]

@@ -1,6 +1,7 @@
 """Each pin set must catch plausible mistakes planted in a copy of the oracle.
 
-Every mutant is a one-line textual change to ``oracle/sgemm_oracle.c``
+Every mutant is a one-line textual change to ``oracle/sgemm_oracle.c`` or
+``oracle/attention_oracle.c``
 (a dropped term, a wrong sign or index, a transposed operand, a lost factor
 in the bound, ...), compiled to a temporary library.  The pins of
 tests/oracle_pins.py then run against it in a child process (a mutant may
@@ -18,6 +19,7 @@ import oracle
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "sgemm_oracle.c")
+SRC_ATT = os.path.join(ROOT, "oracle", "attention_oracle.c")
 
 # (name, text in the oracle, replacement)
 MUTANTS = [
@@ -68,6 +70,24 @@ MUTANTS = [
      "(double)A[i * lda + k] * (double)B[k * ldb + j]"),
 ]
 
+# mutants of the attention oracle
+ATT_MUTANTS = [
+    ("att_no_max_subtraction", "w[j] = exp((double)scale * s0[j] - smax);",
+     "w[j] = exp((double)scale * s0[j]);"),
+    ("att_scale_dropped", "w[j] = exp((double)scale * s0[j] - smax);",
+     "w[j] = exp(s0[j] - smax / (double)scale);"),
+    ("att_not_normalised", "        o /= l;\n", ""),
+    ("att_sum_skips_first_key", "        l += w[j];", "        if (j > 0) l += w[j];"),
+    ("att_dot_drops_last_d", "        for (int64_t d = 0; d < D; ++d) {\n            const double p",
+     "        for (int64_t d = 0; d + 1 < D; ++d) {\n            const double p"),
+    ("att_value_column_of_key", "o += w[j] * (double)V[j * ldv + d];",
+     "o += w[j] * (double)V[j * ldv + (d + j) % D];"),
+    ("att_query_row_ignored", "const float* q = Q + i * ldq;", "const float* q = Q;"),
+    ("att_bound_drops_accumulation", "(5.0 * (double)Nk + 8.0) * ATT_U * mag", "0.0 * mag"),
+    ("att_bound_drops_score_error", "(2.0 * (double)D * ATT_U * delta[j] +",
+     "(0.0 * delta[j] +"),
+]
+
 RUNNER = r"""
 import sys
 sys.path.insert(0, {root!r})
@@ -84,14 +104,21 @@ print("FAILED_PINS", ",".join(failed))
 """
 
 
-@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
-def test_mutant_is_caught(tmp_path, name, old, new):
-    text = open(SRC).read()
+CASES = [(m, SRC) for m in MUTANTS] + [(m, SRC_ATT) for m in ATT_MUTANTS]
+
+
+@pytest.mark.parametrize("mutant,path", CASES, ids=[c[0][0] for c in CASES])
+def test_mutant_is_caught(tmp_path, mutant, path):
+    name, old, new = mutant
+    text = open(path).read()
     assert text.count(old) == 1, f"mutation site for {name} not unique or missing"
     src = tmp_path / f"{name}.c"
     src.write_text(text.replace(old, new))
     lib = str(tmp_path / f"lib_{name}.so")
-    oracle.build(src=str(src), out=lib)
+    if path == SRC:
+        oracle.build(src=str(src), out=lib)
+    else:
+        oracle.build(src_att=str(src), out=lib)
     env = dict(os.environ, OMP_NUM_THREADS="2")
     proc = subprocess.run([sys.executable, "-c", RUNNER.format(root=ROOT, lib=lib)],
                           capture_output=True, text=True, timeout=300, env=env)
