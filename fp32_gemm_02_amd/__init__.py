@@ -30,6 +30,7 @@ SGEMM_KIND_GEMM = 0
 SGEMM_KIND_INIT_LEAF = 1
 SGEMM_KIND_TC = 2
 SGEMM_KIND_TC_CAST = 3
+SGEMM_KIND_ATTENTION = 4
 SGEMM_TC_F16 = 1
 SGEMM_TC_BF16 = 2
 
@@ -105,6 +106,10 @@ _SIGNATURES = {
     "sgemm_tc_get_config": ([_i32, _i64, _i64, _i64, ctypes.POINTER(sgemm_tc_config)],
                             ctypes.c_int),
     "sgemm_tc_set_config": ([_i32, ctypes.POINTER(sgemm_tc_config)], ctypes.c_int),
+    "flash_attention": ([_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _f32,
+                         _vp], ctypes.c_int),
+    "flash_attention_supertiled": ([_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp,
+                                    _i64, _f32, _i64, _vp], ctypes.c_int),
     "sgemm_plan_supertiles": ([_i64, _i64, _i64, _f32, _i64, ctypes.POINTER(sgemm_plan_model),
                                ctypes.POINTER(sgemm_plan)], ctypes.c_int),
     "sgemm_supertiled_host": ([_i64, _i64, _i64, _f32, _vp, _i64, _vp, _i64, _f32, _vp, _i64,
@@ -224,6 +229,30 @@ def sgemm_tc_set_config(fmt, cfg):
         cfg = sgemm_tc_config(*cfg)
     _check(lib().sgemm_tc_set_config(fmt, None if cfg is None else ctypes.byref(cfg)),
            "sgemm_tc_set_config")
+
+
+def flash_attention_raw(Nq, Nk, D, Q, ldq, K, ldk, V, ldv, O, ldo, scale, stream=None):
+    return lib().flash_attention(Nq, Nk, D, _ptr(Q), ldq, _ptr(K), ldk, _ptr(V), ldv, _ptr(O),
+                                 ldo, scale, _stream(stream))
+
+
+def flash_attention(Nq, Nk, D, Q, ldq, K, ldk, V, ldv, O, ldo, scale, stream=None):
+    """O <- softmax(scale * Q K^T) V (row-major device buffers, D = 64)."""
+    _check(flash_attention_raw(Nq, Nk, D, Q, ldq, K, ldk, V, ldv, O, ldo, scale, stream),
+           "flash_attention")
+
+
+def flash_attention_supertiled_raw(Nq, Nk, D, Q, ldq, K, ldk, V, ldv, O, ldo, scale, BR,
+                                   stream=None):
+    return lib().flash_attention_supertiled(Nq, Nk, D, _ptr(Q), ldq, _ptr(K), ldk, _ptr(V),
+                                            ldv, _ptr(O), ldo, scale, BR, _stream(stream))
+
+
+def flash_attention_supertiled(Nq, Nk, D, Q, ldq, K, ldk, V, ldv, O, ldo, scale, BR,
+                               stream=None):
+    """The same through super-tiles of BR query rows (one leaf launch each)."""
+    _check(flash_attention_supertiled_raw(Nq, Nk, D, Q, ldq, K, ldk, V, ldv, O, ldo, scale, BR,
+                                          stream), "flash_attention_supertiled")
 
 
 def configs():

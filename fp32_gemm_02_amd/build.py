@@ -13,6 +13,7 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libphobos_sgemm.so")
 SOURCES = [os.path.join(HERE, "csrc", "sgemm_kernels.hip"),
            os.path.join(HERE, "csrc", "sgemm_tc.hip"),
+           os.path.join(HERE, "csrc", "attention.hip"),
            os.path.join(HERE, "csrc", "sgemm_api.cpp"),
            os.path.join(HERE, "csrc", "sgemm_host.cpp")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -333,6 +333,52 @@ int launch_tc_staged(int32_t fmt, const phobos::Tc16Entry& e, int64_t M, int64_t
     return st;
 }
 
+// ---- attention ----
+constexpr int kAttnD = 64;     // the one head dimension compiled
+
+int check_attention_args(int64_t Nq, int64_t Nk, int64_t D, const float* Q, int64_t ldq,
+                         const float* K, int64_t ldk, const float* V, int64_t ldv,
+                         const float* O, int64_t ldo) {
+    if (Nq < 0) return -1;
+    if (Nk < 1) return -2;
+    if (D != kAttnD) return -3;
+    if (ldq < D) return -5;
+    if (ldk < D) return -7;
+    if (ldv < D) return -9;
+    if (ldo < D) return -11;
+    if (Nq == 0) return SGEMM_OK;
+    if (Q == nullptr) return -4;
+    if (K == nullptr) return -6;
+    if (V == nullptr) return -8;
+    if (O == nullptr) return -10;
+    if (Nq > kMaxDim || Nk > kMaxDim) return SGEMM_ERR_TOO_LARGE;
+    return SGEMM_OK;
+}
+
+int launch_attn(int64_t Nq, int64_t Nk, const float* Q, int64_t ldq, const float* K,
+                int64_t ldk, const float* V, int64_t ldv, float* O, int64_t ldo, float scale,
+                int64_t br, hipStream_t stream) {
+    phobos::AttnArgs p{};
+    p.Nq = (int32_t)Nq;
+    p.Nk = (int32_t)Nk;
+    p.Q = Q;
+    p.ldq = ldq;
+    p.K = K;
+    p.ldk = ldk;
+    p.V = V;
+    p.ldv = ldv;
+    p.O = O;
+    p.ldo = ldo;
+    p.scale = scale;
+    p.br = (int32_t)br;
+    p.blocks_per_tile = (int32_t)((br + 63) / 64);
+    if (((Nq + br - 1) / br) * p.blocks_per_tile * 256 > kMaxGridItems) return SGEMM_ERR_TOO_LARGE;
+    const bool vec = aligned16(Q) && aligned16(K) && aligned16(V) && aligned16(O) &&
+                     ldq % 4 == 0 && ldk % 4 == 0 && ldv % 4 == 0 && ldo % 4 == 0;
+    TraceScope ts(stream, SGEMM_KIND_ATTENTION);
+    return hip_status(phobos::launch_attention(p, vec, stream));
+}
+
 int launch_init(int64_t M, int64_t N, float beta, float* C, int64_t ldc, hipStream_t stream) {
     if (beta == 1.0f) return SGEMM_OK;
     TraceScope ts(stream, SGEMM_KIND_INIT_LEAF);
@@ -494,6 +540,26 @@ int sgemm_tc_set_config(int32_t fmt, const sgemm_tc_config* cfg) {
     if (e < 0) return SGEMM_ERR_NO_CONFIG;
     g_tc_forced[fmt] = e;
     return SGEMM_OK;
+}
+
+int flash_attention(int64_t Nq, int64_t Nk, int64_t D, const float* Q, int64_t ldq,
+                    const float* K, int64_t ldk, const float* V, int64_t ldv, float* O,
+                    int64_t ldo, float scale, void* stream) {
+    const int st = check_attention_args(Nq, Nk, D, Q, ldq, K, ldk, V, ldv, O, ldo);
+    if (st != SGEMM_OK || Nq == 0) return st;
+    return launch_attn(Nq, Nk, Q, ldq, K, ldk, V, ldv, O, ldo, scale, Nq,
+                       reinterpret_cast<hipStream_t>(stream));
+}
+
+int flash_attention_supertiled(int64_t Nq, int64_t Nk, int64_t D, const float* Q, int64_t ldq,
+                               const float* K, int64_t ldk, const float* V, int64_t ldv,
+                               float* O, int64_t ldo, float scale, int64_t BR, void* stream) {
+    const int st = check_attention_args(Nq, Nk, D, Q, ldq, K, ldk, V, ldv, O, ldo);
+    if (st != SGEMM_OK) return st;
+    if (BR < 1) return -13;
+    if (Nq == 0) return SGEMM_OK;
+    return launch_attn(Nq, Nk, Q, ldq, K, ldk, V, ldv, O, ldo, scale, std::min(BR, Nq),
+                       reinterpret_cast<hipStream_t>(stream));
 }
 
 int sgemm_config_count(void) { return kKernelCount; }

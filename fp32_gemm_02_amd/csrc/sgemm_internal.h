@@ -74,6 +74,26 @@ hipError_t launch_tc_cast(int fmt, const float* A, int64_t lda, bool vec_a, cons
                           int64_t ldb, bool vec_b, int M, int N, int K, uint16_t* A16,
                           uint16_t* B16, int Mp, int Np, int Kp, hipStream_t stream);
 
+// Attention O = softmax(scale * Q K^T) V over query rows 0 .. Nq-1 of the
+// given pointers, head dimension 64 (attention.hip), as one launch holding
+// the leaves of every super-tile of br rows.
+struct AttnArgs {
+    int32_t Nq, Nk;
+    const float* Q;
+    int64_t ldq;
+    const float* K;
+    int64_t ldk;
+    const float* V;
+    int64_t ldv;
+    float* O;
+    int64_t ldo;
+    float scale;
+    int32_t br;                 // query rows per super-tile (Nq: one super-tile)
+    int32_t blocks_per_tile;    // ceil(br / 64) workgroups per super-tile
+};
+// vec: Q, K, V, O 16-byte aligned with leading dimensions % 4 == 0.
+hipError_t launch_attention(const AttnArgs& p, bool vec, hipStream_t stream);
+
 // C <- beta*C over an M x N view (beta == 0: C <- 0 without reading C).
 hipError_t launch_init_leaf(int64_t M, int64_t N, float beta, float* C, int64_t ldc,
                             hipStream_t stream);

@@ -217,6 +217,40 @@ int sgemm_tc_get_config(int32_t fmt, int64_t M, int64_t N, int64_t K, sgemm_tc_c
 int sgemm_tc_set_config(int32_t fmt, const sgemm_tc_config* cfg);
 
 /*
+ * Attention, the pages' second @cluster example ("@cluster" page, "The same
+ * names at two levels": flash_attention(Q[Nq, D], K[Nk, D], V[Nk, D],
+ * O[Nq, D], scale) with D = 64; its body is not on the pages, which cite the
+ * FlashAttention paper).  Computes exact, unmasked attention with a row
+ * softmax over the keys, in fp32:
+ *     O[i][:] = sum_j P[i][j] V[j][:],
+ *     P[i][j] = exp(scale * Q[i].K[j] - max_j(...)) / sum_j exp(...)
+ * in one pass over the keys per block of query rows (running maximum,
+ * running weight sum, running weighted sum, rescaled as the maximum grows).
+ * The scores and the weighted sum run on the FP32 matrix cores.
+ *
+ * flash_attention computes all Nq rows as one super-tile.  flash_attention_
+ * supertiled follows the pages' cluster form: super-tiles of BR query rows
+ * (the pages' @cluster BR, 1024 to 4096), each worked by its own leaf, which
+ * reads all of K and V.  Super-tiles are independent, so the leaves of all of
+ * them go out as one grouped launch (ceil(BR/64) workgroups of 64 rows per
+ * super-tile) and run side by side; the result is bit for bit that of
+ * flash_attention (every row is computed by the same code either way).
+ *
+ * All matrices are row-major fp32 device buffers with leading dimensions.
+ * Arguments: 1 Nq, 2 Nk (>= 1), 3 D (64 only), 4 Q, 5 ldq, 6 K, 7 ldk, 8 V,
+ * 9 ldv, 10 O, 11 ldo (each >= D), 12 scale, then 13 BR (super-tiled form),
+ * then the stream.  Nq = 0: nothing.  Errors as sgemm (negative argument
+ * index, SGEMM_ERR_TOO_LARGE above 2^30 rows, HIP status).  O must not
+ * overlap Q, K or V.  Asynchronous on `stream`.
+ */
+int flash_attention(int64_t Nq, int64_t Nk, int64_t D, const float* Q, int64_t ldq,
+                    const float* K, int64_t ldk, const float* V, int64_t ldv, float* O,
+                    int64_t ldo, float scale, void* stream);
+int flash_attention_supertiled(int64_t Nq, int64_t Nk, int64_t D, const float* Q, int64_t ldq,
+                               const float* K, int64_t ldk, const float* V, int64_t ldv,
+                               float* O, int64_t ldo, float scale, int64_t BR, void* stream);
+
+/*
  * Host-resident super-tiled SGEMM, the single-GPU form of the pages' cluster
  * runtime ("@cluster" page, "What runs today": per node, allocate tile
  * buffers, load super-tiles, compute the init and step leaves as their inputs
@@ -308,6 +342,7 @@ int sgemm_supertiled_host(int64_t M, int64_t N, int64_t K, float alpha,
 #define SGEMM_KIND_INIT_LEAF 1
 #define SGEMM_KIND_TC 2          /* the matrix-core GEMM (either form) */
 #define SGEMM_KIND_TC_CAST 3     /* the cast pass of its staged form */
+#define SGEMM_KIND_ATTENTION 4   /* one attention leaf */
 int sgemm_trace_begin(int64_t capacity);
 int sgemm_trace_end(float* ms_out, int32_t* kind_out, int64_t cap, int64_t* n_out);
 

@@ -181,3 +181,67 @@ def sample_entries(w: Workload, count, seed=12345, edges=True):
         rows += list(rng.integers(0, w.M, tail))
         cols += list(np.full(tail, w.N - 1))
     return np.asarray(rows, dtype=np.int64), np.asarray(cols, dtype=np.int64)
+
+
+# ---------------------------------------------------------------------------
+# Attention inputs (the pages' flash_attention: Q[Nq, D], K, V[Nk, D], O[Nq, D]).
+# The pages' job reads 16384 x 64 tensors from files of unstated content;
+# seeded synthetic values of that shape stand in for them.
+
+@dataclass
+class AttnWorkload:
+    name: str
+    Nq: int
+    Nk: int
+    D: int
+    scale: float
+    dists: tuple = ("U", "U", "U")    # Q, K, V
+    seed: int = 0
+    ldq: int = 0                      # 0: D
+    ldk: int = 0
+    ldv: int = 0
+    ldo: int = 0
+    BR: int = 0                       # query rows per super-tile (0: monolithic)
+
+    def __post_init__(self):
+        for f in ("ldq", "ldk", "ldv", "ldo"):
+            if getattr(self, f) == 0:
+                setattr(self, f, self.D)
+
+
+@dataclass
+class AttnInputs:
+    w: AttnWorkload
+    Q: np.ndarray       # flat, (Nq + 1) * ldq, NaN pads
+    K: np.ndarray       # flat, (Nk + 1) * ldk, NaN pads
+    V: np.ndarray       # flat, (Nk + 1) * ldv, NaN pads
+    O: np.ndarray       # flat, (Nq + 1) * ldo, every element C_SENTINEL
+
+    def logical(self, name):
+        w = self.w
+        rows, ld = {"Q": (w.Nq, w.ldq), "K": (w.Nk, w.ldk), "V": (w.Nk, w.ldv),
+                    "O": (w.Nq, w.ldo)}[name]
+        return getattr(self, name)[: rows * ld].reshape(rows, ld)[:, : w.D]
+
+
+# The pages' job: Nq = Nk = 16384, D = 64 (scale 1/sqrt(D)), cluster row block 4096.
+ATTN_16384 = AttnWorkload("attention_16384_d64", 16384, 16384, 64, 0.125, seed=5, BR=4096)
+
+
+def make_attn_inputs(w: AttnWorkload) -> AttnInputs:
+    gen = torch.Generator().manual_seed(w.seed)
+    q = _draw(w.dists[0], w.Nq, w.D, gen).numpy()
+    k = _draw(w.dists[1], w.Nk, w.D, gen).numpy()
+    v = _draw(w.dists[2], w.Nk, w.D, gen).numpy()
+    nan = np.float32(np.nan)
+    out = np.full((w.Nq + 1) * w.ldo, C_SENTINEL, dtype=np.float32)
+    return AttnInputs(w, _embed(q, w.Nq, w.D, w.ldq, nan), _embed(k, w.Nk, w.D, w.ldk, nan),
+                      _embed(v, w.Nk, w.D, w.ldv, nan), out)
+
+
+def attn_pad_mask(w: AttnWorkload):
+    """Boolean mask over the flat O buffer: True on pad columns and the guard row."""
+    mask = np.ones((w.Nq + 1) * w.ldo, dtype=bool)
+    if w.Nq > 0:
+        mask[: w.Nq * w.ldo].reshape(w.Nq, w.ldo)[:, : w.D] = False
+    return mask

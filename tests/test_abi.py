@@ -15,13 +15,16 @@ HEADER = os.path.join(ROOT, "include", "phobos_sgemm.h")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w]*\s*\*?\s*(sgemm\w*)\s*\(", text, flags=re.M)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w]*\s*\*?\s*((?:sgemm|flash_attention)\w*)\s*\(",
+                       text, flags=re.M)
     return sorted(set(names))
 
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for want in ("sgemm", "sgemm_supertiled", "sgemm_init_leaf", "sgemm_tune",
+    for want in ("sgemm", "sgemm_supertiled", "sgemm_init_leaf", "sgemm_tune", "sgemm_tc",
+                 "sgemm_supertiled_host", "sgemm_plan_supertiles", "flash_attention",
+                 "flash_attention_supertiled",
                  "sgemm_tune_candidates", "sgemm_set_config", "sgemm_get_config",
                  "sgemm_config_count", "sgemm_config_at", "sgemm_trace_begin",
                  "sgemm_trace_end", "sgemm_status_string", "sgemm_version"):
@@ -207,3 +210,28 @@ def test_tc_configs():
     assert lib.sgemm_tc_config_count(0) == -1
     assert lib.sgemm_tc_config_at(1, 999, None) == -2
     assert lib.sgemm_tc_get_config(7, 4, 4, 4, None) == -1
+
+
+@pytest.mark.parametrize("args,want", [
+    ((-1, 4, 64, 8, 64, 8, 64, 8, 64, 8, 64, 0.1), -1),
+    ((4, 0, 64, 8, 64, 8, 64, 8, 64, 8, 64, 0.1), -2),     # no keys
+    ((4, 4, 32, 8, 64, 8, 64, 8, 64, 8, 64, 0.1), -3),     # only D = 64
+    ((4, 4, 64, 8, 63, 8, 64, 8, 64, 8, 64, 0.1), -5),     # ldq < D
+    ((4, 4, 64, 8, 64, 8, 60, 8, 64, 8, 64, 0.1), -7),
+    ((4, 4, 64, 8, 64, 8, 64, 8, 1, 8, 64, 0.1), -9),
+    ((4, 4, 64, 8, 64, 8, 64, 8, 64, 8, 0, 0.1), -11),
+    ((4, 4, 64, NULL, 64, 8, 64, 8, 64, 8, 64, 0.1), -4),
+    ((4, 4, 64, 8, 64, NULL, 64, 8, 64, 8, 64, 0.1), -6),
+    ((4, 4, 64, 8, 64, 8, 64, NULL, 64, 8, 64, 0.1), -8),
+    ((4, 4, 64, 8, 64, 8, 64, 8, 64, NULL, 64, 0.1), -10),
+    ((0, 4, 64, NULL, 64, NULL, 64, NULL, 64, NULL, 64, 0.1), 0),   # Nq == 0: nothing
+    ((1 << 31, 4, 64, 8, 64, 8, 64, 8, 64, 8, 64, 0.1), g.SGEMM_ERR_TOO_LARGE),
+])
+def test_attention_argument_checks(args, want):
+    assert g.flash_attention_raw(*args, stream=0) == want
+    assert g.flash_attention_supertiled_raw(*args, 1024, stream=0) == want
+
+
+def test_attention_supertile_rows_checked():
+    assert g.flash_attention_supertiled_raw(4, 4, 64, 8, 64, 8, 64, 8, 64, 8, 64, 0.1, 0,
+                                            stream=0) == -13
