@@ -25,7 +25,9 @@ super-tile extents are replaced by the plan's); --tc f16|bf16 times the
 matrix-core variant sgemm_tc (A and B rounded to that format, fp32
 accumulation) as one monolithic call per step on the same inputs, its
 cast pass included, with the roofline of its 16-bit GEMM kernel against the
-16-bit matrix peak.  For profiling
+16-bit matrix peak; --attention times the pages' second example, attention
+over 16384 queries and keys with D = 64 (the pages' job), as one call of its
+cluster form (super-tiles of 4096 query rows) per step.  For profiling
 runs: --copy-calibration runs one plain device copy of 1 GiB first (a
 known-size reference for the HBM byte counters); --skip-cpu-baseline leaves
 the oracle leg out.
@@ -112,6 +114,109 @@ def cpu_baseline(x, w, target_s=15.0, fmt=None):
     }
 
 
+def attention_flops(Nq, Nk, D):
+    """Two products of 2*Nq*Nk*D flops each (the softmax is not counted)."""
+    return 4.0 * Nq * Nk * D
+
+
+def cpu_baseline_attention(x, w, target_s=15.0):
+    """The attention oracle as it stands, on a block of query rows."""
+    import numpy as np
+
+    import oracle
+
+    orc = oracle.default()
+    threads = orc.max_threads()
+
+    def run(rows):
+        t0 = time.perf_counter()
+        orc.attention(w.Nq, w.Nk, w.D, x.Q, x.K, x.V, w.scale, rows=np.arange(rows),
+                      ldq=w.ldq, ldk=w.ldk, ldv=w.ldv)
+        return time.perf_counter() - t0
+
+    r1 = max(8, threads)
+    t1 = run(r1)
+    rows = int(min(w.Nq, max(r1, r1 * target_s / max(t1, 1e-3))))
+    rows = max(threads, rows - rows % max(1, threads))
+    t = run(rows)
+    return {
+        "value": round(attention_flops(rows, w.Nk, w.D) / t / 1e9, 3),
+        "unit": "GFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"query rows 0..{rows - 1} of the {w.Nq}x{w.Nk}, D={w.D} attention "
+                  f"({t:.1f} s, fp64, bound included)",
+    }
+
+
+def main_attention(args):
+    import numpy as np
+    import torch
+
+    import fp32_gemm_02_amd as g
+    import sgemm_workloads as wl
+
+    w = wl.ATTN_16384
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.Stream(device=dev)
+    x = wl.make_attn_inputs(w)
+    with torch.cuda.stream(stream):
+        dQ, dK, dV, dO = (torch.from_numpy(b).to(dev) for b in (x.Q, x.K, x.V, x.O))
+    stream.synchronize()
+
+    def step():
+        g.flash_attention_supertiled(w.Nq, w.Nk, w.D, dQ, w.ldq, dK, w.ldk, dV, w.ldv, dO, w.ldo,
+                                     w.scale, w.BR, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    stream.synchronize()
+    g.sgemm_trace_begin(args.steps + 16)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    stream.synchronize()
+    ms_total = e0.elapsed_time(e1)
+    ms_kern, kinds, n = g.sgemm_trace_end(cap=args.steps + 16)
+    launch_ms = float(np.mean([t for t, k in zip(ms_kern, kinds) if k == g.SGEMM_KIND_ATTENTION]))
+    ms_per_step = ms_total / args.steps
+    flops = attention_flops(w.Nq, w.Nk, w.D)
+    value = flops / (ms_per_step * 1e-3) / 1e9
+    achieved = flops / (launch_ms * 1e-3) / 1e12
+    out = {
+        "metric": "attention GFLOP/s (2 products of 2*Nq*Nk*D) at Nq = Nk = 16384, D = 64, 1 GPU",
+        "value": round(value, 1),
+        "unit": "GFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "entry": "flash_attention_supertiled", "Nq": w.Nq,
+                   "Nk": w.Nk, "D": w.D, "scale": w.scale, "BR": w.BR,
+                   "inputs": "Q/K/V %s/%s/%s, seed %d" % (*w.dists, w.seed),
+                   "launches_per_step": 1,
+                   "pct_of_fp32_matrix_peak": round(100.0 * value / 1e3 / PEAK_FP32_MFMA_TFLOPS, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_FP32_MFMA_TFLOPS, 4), "traffic": None},
+    }
+    if not args.skip_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_attention(x, w)
+    print(f"# timed {args.steps} steps: {ms_total:.2f} ms on the stream; {n} launches traced, "
+          f"mean {launch_ms:.4f} ms", file=sys.stderr, flush=True)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -121,6 +226,7 @@ def main():
     ap.add_argument("--tune", action="store_true")
     ap.add_argument("--host-resident", type=int, default=None, metavar="MIB")
     ap.add_argument("--tc", choices=("f16", "bf16"), default=None)
+    ap.add_argument("--attention", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -128,6 +234,10 @@ def main():
         print("bench.py runs on one GPU only: the super-tile grid of this workload is one "
               "GPU's share, and no multi-GPU path is built (use --gpus 1).", file=sys.stderr)
         sys.exit(2)
+
+    if args.attention:
+        main_attention(args)
+        return
 
     import numpy as np
     import torch
