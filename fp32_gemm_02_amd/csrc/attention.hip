@@ -8,10 +8,11 @@
 //
 // Query rows come in super-tiles of br rows (the pages' @cluster row block;
 // br = Nq for the monolithic form), each worked by ceil(br/64) workgroups of
-// one launch.  One workgroup (4 waves) owns 64 query rows, 16 per wave, of
-// its super-tile, and walks the keys
-// in blocks of 64 staged through LDS (K and V, double-buffered, loaded one
-// block ahead through registers).  Both products run on the FP32 matrix cores
+// one launch.  One workgroup owns 64 query rows of its super-tile, 16 per
+// query group; each group has two waves that take alternate blocks of 64
+// keys (the workgroup stages 128 keys of K and V per step through LDS,
+// double-buffered, loaded one step ahead through registers) and merge their
+// running statistics at the end.  Both products run on the FP32 matrix cores
 // (v_mfma_f32_16x16x4_f32, lane layout checked on the GPU with an in-bounds
 // probe; l = lane, g = l / 16, q = l % 16):
 //   src A: lane l holds A'[q][g]   (16 x 4)
@@ -51,18 +52,28 @@ constexpr float kLog2e = 1.4426950408889634f;
 // groups (and 8 consecutive lanes 8 different ones of a 128-byte line).
 __device__ __forceinline__ int kswz(int row, int piece) { return piece ^ (row & 15); }
 
-template <bool VEC>
-__global__ __launch_bounds__(256) void attention_kernel(AttnArgs p) {
-    __shared__ __attribute__((aligned(16))) char lds[2 * kStage];
+// KSPLIT = 2: two waves per group of 16 queries, each taking every other
+// block of 64 keys (128 keys per step), two waves per SIMD in all; their
+// running (maximum, weight sum, weighted sum) are merged at the end.
+template <bool VEC, int KSPLIT>
+__global__ __launch_bounds__(256 * KSPLIT) void attention_kernel(AttnArgs p) {
+    constexpr int NT = 256 * KSPLIT;           // threads
+    constexpr int KI = kBC * KSPLIT;           // keys per step
+    constexpr int TILE = KI * kRowB;           // bytes of the K (or V) rows of one step
+    constexpr int STAGE = 2 * TILE;
+    constexpr int LD = KI * 16 / NT;           // 16-byte pieces per thread per tensor
+    static_assert(LD * NT == KI * 16, "whole pieces per thread");
+    __shared__ __attribute__((aligned(16))) char lds[2 * STAGE];
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int q = lane & 15, g = lane >> 4;
+    const int wq = wave & 3, half = wave >> 2;   // query group, key half
     // super-tile of this workgroup and its rows; one launch holds the leaves
     // of every super-tile
     const int st = blockIdx.x / p.blocks_per_tile, lb = blockIdx.x - st * p.blocks_per_tile;
     const int row_end = min(p.Nq, (st + 1) * p.br);
-    const int qrow = st * p.br + lb * kBQ + wave * 16 + q;   // this lane's query row
+    const int qrow = st * p.br + lb * kBQ + wq * 16 + q;   // this lane's query row
     const bool qin = qrow < row_end;
-    const int nb = (p.Nk + kBC - 1) / kBC;
+    const int ni = (p.Nk + KI - 1) / KI;
 
     // ---- Q operand, held for the whole key loop: Q[qrow][16g + j] ----
     float qv[16];
@@ -78,13 +89,13 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnArgs p) {
         }
     }
 
-    // ---- K / V tiles: thread t moves 16-byte pieces (t + 256*i) of each ----
-    f32x4 sk[4], sv[4];
-    auto load = [&](int b) {
-        const int k0 = b * kBC;
+    // ---- K / V rows of one step: thread t moves 16-byte pieces t + NT*i ----
+    f32x4 sk[LD], sv[LD];
+    auto load = [&](int it) {
+        const int k0 = it * KI;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int u = t + 256 * i, row = u >> 4, piece = u & 15, key = k0 + row;
+        for (int i = 0; i < LD; ++i) {
+            const int u = t + NT * i, row = u >> 4, piece = u & 15, key = k0 + row;
             const bool in = key < p.Nk;
             sk[i] = in ? load4<VEC>(p.K + (int64_t)key * p.ldk + 4 * piece, 4)
                        : f32x4{0.f, 0.f, 0.f, 0.f};
@@ -93,11 +104,11 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnArgs p) {
         }
     };
     auto store = [&](int buf) {
-        char* ks = lds + buf * kStage;
-        char* vs = ks + kTile;
+        char* ks = lds + buf * STAGE;
+        char* vs = ks + TILE;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int u = t + 256 * i, row = u >> 4, piece = u & 15;
+        for (int i = 0; i < LD; ++i) {
+            const int u = t + NT * i, row = u >> 4, piece = u & 15;
             *reinterpret_cast<f32x4*>(ks + row * kRowB + 16 * kswz(row, piece)) = sk[i];
             *reinterpret_cast<f32x4*>(vs + row * kRowB + 16 * piece) = sv[i];
         }
@@ -113,13 +124,14 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnArgs p) {
     load(0);
     store(0);
     __syncthreads();
-    for (int b = 0; b < nb; ++b) {
-        const bool more = b + 1 < nb;
-        if (more) load(b + 1);
-        const char* ks = lds + (b & 1) * kStage;
-        const char* vs = ks + kTile;
+    for (int it = 0; it < ni; ++it) {
+        const bool more = it + 1 < ni;
+        if (more) load(it + 1);
+        // this wave's 64 keys of the step: rows 64*half .. +63 of the stage
+        const char* ks = lds + (it & 1) * STAGE + half * (kBC * kRowB);
+        const char* vs = lds + (it & 1) * STAGE + TILE + half * (kBC * kRowB);
 
-        // S^T for the 4 sub-blocks of 16 keys: s[kb][r] = S[qrow][64b + 16kb + 4g + r]
+        // S^T for the 4 sub-blocks of 16 keys: s[kb][r] = S[qrow][kbase + 16kb + r]
         f32x4 s[4];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
@@ -128,6 +140,7 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnArgs p) {
             const char* kr = ks + krow * kRowB;
 #pragma unroll
             for (int cc = 0; cc < 4; ++cc) {
+                // the swizzle of row 64*half + krow is that of krow (64 = 0 mod 16)
                 const f32x4 a = *reinterpret_cast<const f32x4*>(kr + 16 * kswz(krow, 4 * g + cc));
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
@@ -136,7 +149,7 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnArgs p) {
         }
 
         // online softmax in base 2; keys past Nk weigh nothing
-        const int kbase = b * kBC + 4 * g;
+        const int kbase = it * KI + half * kBC + 4 * g;
         float bm = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
@@ -150,14 +163,16 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnArgs p) {
         bm = fmaxf(bm, __shfl_xor(bm, 16));
         bm = fmaxf(bm, __shfl_xor(bm, 32));
         const float mn = fmaxf(m, bm);
-        const float alpha = __builtin_amdgcn_exp2f(m - mn);   // 0 on the first block
+        // a key half that has met no key yet keeps weight 0 (not exp2(-inf + inf))
+        const float base = (mn == -INFINITY) ? 0.0f : mn;
+        const float alpha = __builtin_amdgcn_exp2f(m - base);   // 0 until a key is met
         m = mn;
         float bl = 0.0f;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float w = __builtin_amdgcn_exp2f(s[kb][r] - mn);
+                const float w = __builtin_amdgcn_exp2f(s[kb][r] - base);
                 s[kb][r] = w;
                 bl += w;
             }
@@ -177,8 +192,31 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnArgs p) {
         }
 
         // the other buffer was last read before the previous barrier
-        if (more) store((b + 1) & 1);
+        if (more) store((it + 1) & 1);
         __syncthreads();
+    }
+
+    if constexpr (KSPLIT == 2) {
+        // merge the second key half into the first: both hold the same lanes'
+        // queries and output columns; the buffers are free after the last barrier
+        float* x = reinterpret_cast<float*>(lds) + (wq * 64 + lane) * 18;
+        if (half == 1) {
+            x[0] = m;
+            x[1] = l;
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) x[2 + 4 * db + r] = o[db][r];
+        }
+        __syncthreads();
+        if (half == 1) return;
+        const float m2 = x[0], mm = fmaxf(m, m2);
+        const float f1 = __builtin_amdgcn_exp2f(m - mm), f2 = __builtin_amdgcn_exp2f(m2 - mm);
+        l = l * f1 + x[1] * f2;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[db][r] = o[db][r] * f1 + x[2 + 4 * db + r] * f2;
     }
 
     // ---- epilogue: the weight sum over all keys, O = o / l ----
@@ -204,12 +242,15 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnArgs p) {
 }  // namespace
 
 hipError_t launch_attention(const AttnArgs& p, bool vec, hipStream_t stream) {
+    // two waves per query group: at 16384 queries one 16-query wave per SIMD
+    // left latency exposed (87-92 TFLOP/s); two per SIMD reach 103-107
+    constexpr int KS = 2;
     const int64_t tiles = (p.Nq + (int64_t)p.br - 1) / p.br;
-    const dim3 grid((unsigned)(tiles * p.blocks_per_tile)), block(256);
+    const dim3 grid((unsigned)(tiles * p.blocks_per_tile)), block(256 * KS);
     if (vec)
-        hipLaunchKernelGGL(attention_kernel<true>, grid, block, 0, stream, p);
+        hipLaunchKernelGGL((attention_kernel<true, KS>), grid, block, 0, stream, p);
     else
-        hipLaunchKernelGGL(attention_kernel<false>, grid, block, 0, stream, p);
+        hipLaunchKernelGGL((attention_kernel<false, KS>), grid, block, 0, stream, p);
     return hipGetLastError();
 }
 
