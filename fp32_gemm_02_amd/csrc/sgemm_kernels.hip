@@ -295,46 +295,122 @@ __global__ __launch_bounds__(64 * WM * WN) void sgemm_mfma_kernel(GemmArgs p) {
         store_regs(st, buf);
         return false;
     };
-    bool pend = false;
-    issue(0, 0);
-    if (NS == 3 && nk > 1) pend = issue(1, 1);
-    wait_and_barrier(pend);
-    read_a(smem, 0, fa[0]);
-    fb[0] = read_b(smem, 0);
-    int cur = 0;                       // buffer of stage kt
-    for (int kt = 0; kt < nk; ++kt) {
-        const int nxt = (cur + 1 == NS) ? 0 : cur + 1;
-        const int lbuf = (cur == 0) ? NS - 1 : cur - 1;   // buffer of stage kt+NS-1
-        const float* base = smem + cur * T::STAGE;
-        const float* nbase = smem + nxt * T::STAGE;
-        const int lk0 = (kt + NS - 1) * BK;
-        const bool more = kt + 1 < nk;
-        const bool load = kt + NS - 1 < nk;
-        const bool direct = load && direct_ok(lk0);
-        const bool staged = load && !direct;
-        Staged st;   // register path only; dead outside this iteration
+    // ---- interior fast path ----
+    // A tile clear of the N edge, with K a whole number of chunks, loads
+    // every chunk directly.  With a two-stage ring its stage loop then has no
+    // data-dependent branch, and the work between MFMAs is spread out: the
+    // fragment reads for the next k-step, the direct loads and the stage
+    // barrier are each issued right after one MFMA, while it runs, instead of
+    // as one group between k-steps that leaves the matrix core idle until the
+    // group has issued.  The loop body is straight-line code, so the
+    // compiler's LDS waits are exact: before an MFMA it waits only for the
+    // fragments that MFMA reads, not for the next stage's first reads issued
+    // after the barrier.
+    constexpr int MFMAS = T::MB * T::NB;                // MFMAs per k-step
+    constexpr int DMA_AT = (MFMAS >= 10) ? 6 : MFMAS - DMA_PER_STEP;
+    bool done = false;
+    if constexpr (NS == 2 && T::MB + 2 <= MFMAS && DMA_AT >= 0) {
+        if (VEC && n_inside && p.K % BK == 0) {
+            auto read_a_one = [&](const float* base, int c, f32x4* dst, int i) {
+                dst[i] = *reinterpret_cast<const f32x4*>(base + a_row + i * 32 * BK + a_piece[c]);
+            };
+            load_direct(0, 0);
+            __builtin_amdgcn_s_waitcnt(kWaitVm<0>);
+            __syncthreads();
+            read_a(smem, 0, fa[0]);
+            fb[0] = read_b(smem, 0);
+            int cur = 0;
+            // One stage: k-steps of stage kt from buffer cur; with MORE, the
+            // loads of stage kt+1 into the other buffer and, at the last
+            // k-step, the barrier and the first reads of stage kt+1.
+            auto stage = [&](int kt, auto more_tag) {
+                constexpr bool MORE = decltype(more_tag)::value;
+                const float* base = smem + cur * T::STAGE;
+                const int nb = cur ^ 1;
+                const float* nbase = smem + nb * T::STAGE;
+                const int lk0 = (kt + 1) * BK;
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-            if (kk + 1 < KS) {
-                if ((kk + 1) % 4 == 0) read_a(base, (kk + 1) / 4, fa[((kk + 1) / 4) & 1]);
-                fb[(kk + 1) & 1] = read_b(base, kk + 1);
-            } else if (more) {
-                wait_and_barrier(direct);
-                read_a(nbase, 0, fa[0]);
-                fb[0] = read_b(nbase, 0);
-            }
-            if (direct) {
+                for (int kk = 0; kk < KS; ++kk) {
 #pragma unroll
-                for (int j = kk * DMA_PER_STEP; j < (kk + 1) * DMA_PER_STEP; ++j)
-                    if (j < DIRECT_LOADS) load_direct_one(lk0, lbuf, j);
-            }
-            if (kk == 0 && staged) load_regs(st, lk0);
-            if (kk == KS - 4 && staged) store_regs(st, lbuf);
-            __builtin_amdgcn_sched_barrier(0);
-            mfma_step(fa[(kk / 4) & 1], kk % 4, fb[kk & 1]);
-            __builtin_amdgcn_sched_barrier(0);
+                    for (int m = 0; m < MFMAS; ++m) {
+                        const int i = m / T::NB, n = m % T::NB;
+                        acc[i][n] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                            fa[(kk / 4) & 1][i][kk % 4], BVec<T::NB>::get(fb[kk & 1], n), acc[i][n],
+                            0, 0, 0);
+                        __builtin_amdgcn_sched_barrier(0);
+                        if (kk + 1 < KS) {
+                            if (m == 0) fb[(kk + 1) & 1] = read_b(base, kk + 1);
+                            if ((kk + 1) % 4 == 0 && m >= 1 && m <= T::MB)
+                                read_a_one(base, (kk + 1) / 4, fa[((kk + 1) / 4) & 1], m - 1);
+                        } else if (MORE) {
+                            // stage kt+1 has landed everywhere, and every
+                            // wave has read stage kt's buffer for the last
+                            // time (its fragments are in registers)
+                            if (m == 0) {
+                                __builtin_amdgcn_s_waitcnt(kWaitVm<0>);
+                                asm volatile("s_barrier" ::: "memory");
+                            }
+                            if (m == 1) fb[0] = read_b(nbase, 0);
+                            if (m >= 2 && m < 2 + T::MB) read_a_one(nbase, 0, fa[0], m - 2);
+                        }
+                        if (MORE && kk < DMA_STEPS && m >= DMA_AT && m < DMA_AT + DMA_PER_STEP) {
+                            const int j = kk * DMA_PER_STEP + (m - DMA_AT);
+                            if (j < DIRECT_LOADS) load_direct_one(lk0, nb, j);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
+                cur = nb;
+            };
+            for (int kt = 0; kt + 1 < nk; ++kt) stage(kt, std::true_type{});
+            stage(nk - 1, std::false_type{});
+            done = true;
         }
-        cur = nxt;
+    }
+
+    // ---- general path: edge tiles, K tails, three-stage rings ----
+    if (!done) {
+        bool pend = false;
+        issue(0, 0);
+        if (NS == 3 && nk > 1) pend = issue(1, 1);
+        wait_and_barrier(pend);
+        read_a(smem, 0, fa[0]);
+        fb[0] = read_b(smem, 0);
+        int cur = 0;                       // buffer of stage kt
+        for (int kt = 0; kt < nk; ++kt) {
+            const int nxt = (cur + 1 == NS) ? 0 : cur + 1;
+            const int lbuf = (cur == 0) ? NS - 1 : cur - 1;   // buffer of stage kt+NS-1
+            const float* base = smem + cur * T::STAGE;
+            const float* nbase = smem + nxt * T::STAGE;
+            const int lk0 = (kt + NS - 1) * BK;
+            const bool more = kt + 1 < nk;
+            const bool load = kt + NS - 1 < nk;
+            const bool direct = load && direct_ok(lk0);
+            const bool staged = load && !direct;
+            Staged st;   // register path only; dead outside this iteration
+    #pragma unroll
+            for (int kk = 0; kk < KS; ++kk) {
+                if (kk + 1 < KS) {
+                    if ((kk + 1) % 4 == 0) read_a(base, (kk + 1) / 4, fa[((kk + 1) / 4) & 1]);
+                    fb[(kk + 1) & 1] = read_b(base, kk + 1);
+                } else if (more) {
+                    wait_and_barrier(direct);
+                    read_a(nbase, 0, fa[0]);
+                    fb[0] = read_b(nbase, 0);
+                }
+                if (direct) {
+    #pragma unroll
+                    for (int j = kk * DMA_PER_STEP; j < (kk + 1) * DMA_PER_STEP; ++j)
+                        if (j < DIRECT_LOADS) load_direct_one(lk0, lbuf, j);
+                }
+                if (kk == 0 && staged) load_regs(st, lk0);
+                if (kk == KS - 4 && staged) store_regs(st, lbuf);
+                __builtin_amdgcn_sched_barrier(0);
+                mfma_step(fa[(kk / 4) & 1], kk % 4, fb[kk & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            cur = nxt;
+        }
     }
 
     // ---- epilogue: C <- alpha*acc + beta*C (beta == 0: C not read) ----
