@@ -288,6 +288,9 @@ int launch_tc_staged(int32_t fmt, const phobos::Tc16Entry& e, int64_t M, int64_t
     const int64_t tm = (M + e.cfg.bm - 1) / e.cfg.bm, tn = (N + e.cfg.bn - 1) / e.cfg.bn;
     if (tm * tn * e.threads > kMaxGridItems || Mp * Kp >= (int64_t(1) << 40))
         return SGEMM_ERR_TOO_LARGE;
+    // the 16-bit kernel addresses a tile's rows with 32-bit byte offsets
+    const int64_t span = (std::max(e.cfg.bm, e.cfg.bn) - 1) * Kp + e.cfg.bk;
+    if (span * (int64_t)sizeof(uint16_t) > (int64_t)UINT32_MAX) return 1;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return hip_status(hipGetLastError());
     hipMemPool_t pool = tc_pool(dev);
@@ -497,7 +500,7 @@ int sgemm_tc(int64_t M, int64_t N, int64_t K, float alpha, const float* A, int64
         const int r = launch_tc_staged(fmt, t.staged[fmt][e - t.nfused[fmt]], M, N, K, alpha, A,
                                        lda, B, ldb, beta, C, ldc, s);
         if (r != 1) return r;
-        // no workspace: the fused form with the same tile shape, else the default
+        // no workspace, or a K too long for its 32-bit offsets: the fused form
         int f = tc_find(fmt, sgemm_tc_config{256, 256, 32, 4, 2, 0});
         if (f < 0) return SGEMM_ERR_NO_CONFIG;
         return launch_entry(t.fused[fmt][f], SGEMM_KIND_TC, M, N, K, alpha, A, lda, B, ldb, beta,

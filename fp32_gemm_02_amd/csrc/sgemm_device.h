@@ -77,6 +77,17 @@ __device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
     asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0) : "memory");
 }
 
+// The same load with a wave-uniform 64-bit base (held in scalar registers)
+// and a 32-bit per-lane byte offset: lane l fetches the 16 bytes at
+// base + voff.  Interleaved between MFMAs, the form with a 64-bit address per
+// lane cost about 2% of the matrix-core rate in a register-only timing test
+// and this form nothing measurable, so it is the one the GEMM kernels use
+// wherever their offsets fit in 32 bits.
+__device__ __forceinline__ void dma16s(const void* base, uint32_t voff, void* lds_dst) {
+    const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds_dst;
+    asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(m0) : "memory");
+}
+
 // s_waitcnt immediate (gfx9 encoding) waiting for at most N outstanding
 // vector-memory loads and for every LDS access; exports are not waited for.
 template <int N>

@@ -173,7 +173,8 @@ __global__ __launch_bounds__(64 * WM * WN) void sgemm_mfma_kernel(GemmArgs p) {
     // Wave w's j-th load of A fills the 64 consecutive 16-byte slots
     // (j*NW + w)*64 .. +63 of the A tile; slot g holds row g / QA, stored
     // piece g % QA, i.e. logical piece (g % QA) ^ swz(row).  B's slots are
-    // its pieces in row-major order.  Offsets are relative to k0 = 0.
+    // its pieces in row-major order.  Offsets are relative to the chunk's
+    // first row and column inside the tile.
     // Tiles at the M or N edge load too: a row of A past M reads row M-1 and
     // a piece of B wholly past N reads the tile's first piece instead; both
     // only feed rows or columns of C that are never stored.  A piece of B
@@ -181,30 +182,36 @@ __global__ __launch_bounds__(64 * WM * WN) void sgemm_mfma_kernel(GemmArgs p) {
     // (ldb is a multiple of 4 here, so they lie before the next row); for the
     // last row of B that could pass the end of the buffer, so a chunk that
     // holds row K-1 of an N-edge tile takes the register path.
-    int64_t da_off[T::DA], db_off[T::DB];
+    // The loads take a wave-uniform base (A: row m0, column k0; B: row k0,
+    // column n0) and a 32-bit byte offset per lane, so they need
+    // (BM-1)*lda + BK and (BK-1)*ldb + BN floats to fit in 32-bit byte
+    // offsets; beyond that every chunk takes the register path.
+    uint32_t da_off[T::DA], db_off[T::DB];
 #pragma unroll
     for (int j = 0; j < T::DA; ++j) {
         const int g = (j * T::NW + wave) * 64 + lane;
         const int row = g / T::QA;
         const int q = (g % T::QA) ^ swz<T::QA>(row);
         const int grow = min(m0 + row, p.M - 1);
-        da_off[j] = (int64_t)grow * p.lda + 4 * q;
+        da_off[j] = (uint32_t)(((int64_t)(grow - m0) * p.lda + 4 * q) * 4);
     }
 #pragma unroll
     for (int j = 0; j < T::DB; ++j) {
         const int g = (j * T::NW + wave) * 64 + lane;
         const int gn = n0 + 4 * (g % T::QB);
-        db_off[j] = (int64_t)(g / T::QB) * p.ldb + (gn < p.N ? gn : n0);
+        db_off[j] = (uint32_t)(((int64_t)(g / T::QB) * p.ldb + (gn < p.N ? gn - n0 : 0)) * 4);
     }
+    const bool narrow = ((int64_t)(BM - 1) * p.lda + BK) * 4 <= (int64_t)UINT32_MAX &&
+                        ((int64_t)(BK - 1) * p.ldb + BN) * 4 <= (int64_t)UINT32_MAX;
     // Direct load number j (0 .. DA+DB-1) of the chunk at k0 into buffer s.
     auto load_direct_one = [&](int k0, int s, int j) {
         float* As = smem + s * T::STAGE;
         float* Bs = As + T::A_FLOATS;
         if (j < T::DA)
-            dma16(p.A + k0 + da_off[j], As + (j * T::NW + wave) * 256);
+            dma16s(p.A + (int64_t)m0 * p.lda + k0, da_off[j], As + (j * T::NW + wave) * 256);
         else
-            dma16(p.B + (int64_t)k0 * p.ldb + db_off[j - T::DA],
-                  Bs + ((j - T::DA) * T::NW + wave) * 256);
+            dma16s(p.B + (int64_t)k0 * p.ldb + n0, db_off[j - T::DA],
+                   Bs + ((j - T::DA) * T::NW + wave) * 256);
     };
     auto load_direct = [&](int k0, int s) {
 #pragma unroll
@@ -214,7 +221,7 @@ __global__ __launch_bounds__(64 * WM * WN) void sgemm_mfma_kernel(GemmArgs p) {
     // for a tile at the N edge, does not hold the last row of B.
     const bool n_inside = n0 + BN <= p.N;
     auto direct_ok = [&](int k0) {
-        return VEC && (n_inside ? k0 + BK <= p.K : k0 + BK < p.K);
+        return VEC && narrow && (n_inside ? k0 + BK <= p.K : k0 + BK < p.K);
     };
 
     f32x16 acc[T::MB][T::NB];
@@ -310,7 +317,7 @@ __global__ __launch_bounds__(64 * WM * WN) void sgemm_mfma_kernel(GemmArgs p) {
     constexpr int DMA_AT = (MFMAS >= 10) ? 6 : MFMAS - DMA_PER_STEP;
     bool done = false;
     if constexpr (NS == 2 && T::MB + 2 <= MFMAS && DMA_AT >= 0) {
-        if (VEC && n_inside && p.K % BK == 0) {
+        if (VEC && narrow && n_inside && p.K % BK == 0) {
             auto read_a_one = [&](const float* base, int c, f32x4* dst, int i) {
                 dst[i] = *reinterpret_cast<const f32x4*>(base + a_row + i * 32 * BK + a_piece[c]);
             };

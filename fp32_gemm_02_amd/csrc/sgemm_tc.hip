@@ -475,26 +475,31 @@ __global__ __launch_bounds__(64 * WM * WN) void tc16_kernel(Tc16Args p) {
     // (j*NW + wave)*64 .. +63 of the tile; slot g holds row g / PR, stored
     // piece g % PR, i.e. logical piece (g % PR) ^ swz(row) (8 k values).  B's
     // LDS rows are in the interleaved column order of the epilogue.
-    int64_t da[DA], db[DB];
+    // Byte offsets from the chunk's first row (A) or column (B) of the tile;
+    // the host checks that (BM-1)*ld + BK and (BN-1)*ld + BK 16-bit values
+    // fit in 32-bit byte offsets.
+    uint32_t da[DA], db[DB];
 #pragma unroll
     for (int j = 0; j < DA; ++j) {
         const int g = (j * NW + wave) * 64 + lane, row = g / PR;
-        da[j] = (int64_t)(m0 + row) * p.ld + 8 * ((g % PR) ^ swz<PR>(row));
+        da[j] = (uint32_t)(((int64_t)row * p.ld + 8 * ((g % PR) ^ swz<PR>(row))) * 2);
     }
 #pragma unroll
     for (int j = 0; j < DB; ++j) {
         const int g = (j * NW + wave) * 64 + lane, lr = g / PR;
-        const int u = lr % TWN, n = n0 + (lr - u) + NB * (u % 32) + u / 32;
-        db[j] = (int64_t)n * p.ld + 8 * ((g % PR) ^ swz<PR>(lr));
+        const int u = lr % TWN, n = (lr - u) + NB * (u % 32) + u / 32;
+        db[j] = (uint32_t)(((int64_t)n * p.ld + 8 * ((g % PR) ^ swz<PR>(lr))) * 2);
     }
     auto issue = [&](int kc, int buf) {
         char* As = lds + buf * T::STAGE;
         char* Bs = As + T::A_BYTES;
         const int64_t k0 = (int64_t)kc * BK;
+        const uint16_t* a0 = p.A + (int64_t)m0 * p.ld + k0;
+        const uint16_t* b0 = p.B + (int64_t)n0 * p.ld + k0;
 #pragma unroll
-        for (int j = 0; j < DA; ++j) dma16(p.A + k0 + da[j], As + (j * NW + wave) * 1024);
+        for (int j = 0; j < DA; ++j) dma16s(a0, da[j], As + (j * NW + wave) * 1024);
 #pragma unroll
-        for (int j = 0; j < DB; ++j) dma16(p.B + k0 + db[j], Bs + (j * NW + wave) * 1024);
+        for (int j = 0; j < DB; ++j) dma16s(b0, db[j], Bs + (j * NW + wave) * 1024);
     };
 
     u32x4 fa[2][MB], fb[2][NB];
