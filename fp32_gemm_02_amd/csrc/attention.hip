@@ -32,6 +32,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "sgemm_device.h"
 #include "sgemm_internal.h"
 
@@ -46,6 +48,9 @@ constexpr int kRowB = kD * 4;                      // bytes of one K or V row in
 constexpr int kTile = kBC * kRowB;                 // bytes of one K or V tile
 constexpr int kStage = 2 * kTile;                  // K and V
 constexpr float kLog2e = 1.4426950408889634f;
+// Fourth word of a raw buffer descriptor on gfx9-class GPUs: 32-bit data
+// format, no swizzle, no index stride.
+constexpr int kBufferWord3 = 0x00020000;
 
 // K rows are stored with their 16-byte pieces XOR-swizzled by row.  The LDS
 // serves a 128-bit read for 16 lanes per cycle, from a 256-byte bank window,
@@ -61,21 +66,25 @@ __device__ __forceinline__ int kswz(int row, int piece) { return piece ^ (row & 
 // block of 64 keys (128 keys per step), two waves per SIMD in all; their
 // running (maximum, weight sum, weighted sum) are merged at the end.
 //
-// K and V have rings of two stages each: stage it & 1 holds the rows of step
-// it while those of step it+1 are in flight through registers.  (Forming the
-// next step's scores during this step's exponentials, with the K ring one
-// step ahead, measured 4% slower: two waves per SIMD already overlap one
-// wave's vector work with the other's matrix products.)
-template <bool VEC, int KSPLIT>
+// K has a ring of two stages and V one of three: K stage it & 1 and V stage
+// it % 3 hold the rows of step it while those of step it+1 are in flight
+// through registers.  The two waves of a query group share a SIMD (waves w
+// and w+4), and the barrier that ends each step would keep them in the same
+// phase, taking their exponentials at the same time while the matrix core
+// idles.  So the second wave runs half a step behind: in step it it takes
+// the exponentials and output products of step it-1 (whose V rows the third
+// V stage keeps), then the scores of step it, and finishes step ni-1 after
+// the loop.
+template <bool VEC, bool BUF, int KSPLIT>
 __global__ __launch_bounds__(256 * KSPLIT) void attention_kernel(AttnArgs p) {
     constexpr int NT = 256 * KSPLIT;           // threads
     constexpr int KI = kBC * KSPLIT;           // keys per step
     constexpr int TILE = KI * kRowB;           // bytes of the K (or V) rows of one step
     constexpr int LD = KI * 16 / NT;           // 16-byte pieces per thread per tensor
     static_assert(LD * NT == KI * 16, "whole pieces per thread");
-    __shared__ __attribute__((aligned(16))) char lds[4 * TILE];
+    __shared__ __attribute__((aligned(16))) char lds[5 * TILE];
     char* const kring = lds;                   // K stages 0, 1
-    char* const vring = lds + 2 * TILE;        // V stages 0, 1
+    char* const vring = lds + 2 * TILE;        // V stages 0, 1, 2
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int q = lane & 15, g = lane >> 4;
     const int wq = wave & 3, half = wave >> 2;   // query group, key half
@@ -87,29 +96,50 @@ __global__ __launch_bounds__(256 * KSPLIT) void attention_kernel(AttnArgs p) {
     const bool qin = qrow < row_end;
     const int ni = (p.Nk + KI - 1) / KI;
 
-    // ---- Q operand, held for the whole key loop: Q[qrow][16g + j] ----
+    // ---- Q operand, held for the whole key loop: c * Q[qrow][16g + j] ----
+    // The scores come out in base-2 exponent units, scale * log2(e) * S0, so
+    // the softmax needs no multiply per score.
+    const float c = p.scale * kLog2e;
     float qv[16];
     {
         const float* src = p.Q + (int64_t)qrow * p.ldq + 16 * g;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const f32x4 v = qin ? load4<VEC>(src + 4 * c, 4) : f32x4{0.f, 0.f, 0.f, 0.f};
-            qv[4 * c] = v[0];
-            qv[4 * c + 1] = v[1];
-            qv[4 * c + 2] = v[2];
-            qv[4 * c + 3] = v[3];
+        for (int j = 0; j < 4; ++j) {
+            const f32x4 v = qin ? load4<VEC>(src + 4 * j, 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+            qv[4 * j] = v[0] * c;
+            qv[4 * j + 1] = v[1] * c;
+            qv[4 * j + 2] = v[2] * c;
+            qv[4 * j + 3] = v[3] * c;
         }
     }
 
     // ---- K / V rows of one step: thread t moves 16-byte pieces t + NT*i ----
+    // BUF: buffer loads.  A step's rows lie within 4 GiB of its first row, so
+    // each load is that row's buffer descriptor (scalar registers) plus a
+    // 32-bit byte offset per lane, with no per-lane address arithmetic or
+    // branch.  The descriptor's size ends after row Nk-1, and the hardware
+    // returns zeros past it, which is the zero fill of the rows past Nk.
     f32x4 sk[LD], sv[LD];
     auto load_rows = [&](const float* src, int64_t ld, int it, f32x4* dst) {
         const int k0 = it * KI;
+        if constexpr (BUF) {
+            const int64_t bytes = ((int64_t)(p.Nk - k0 - 1) * ld + kD) * 4;
+            const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<float*>(src + (int64_t)k0 * ld), (short)0,
+                (int)(uint32_t)min<int64_t>(bytes, UINT32_MAX), kBufferWord3);
 #pragma unroll
-        for (int i = 0; i < LD; ++i) {
-            const int u = t + NT * i, row = u >> 4, piece = u & 15, key = k0 + row;
-            dst[i] = key < p.Nk ? load4<VEC>(src + (int64_t)key * ld + 4 * piece, 4)
-                                : f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int i = 0; i < LD; ++i) {
+                const int u = t + NT * i, row = u >> 4, piece = u & 15;
+                dst[i] = __builtin_amdgcn_raw_buffer_load_b128(
+                    rsrc, (row * (uint32_t)ld + 4 * piece) * 4, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < LD; ++i) {
+                const int u = t + NT * i, row = u >> 4, piece = u & 15, key = k0 + row;
+                dst[i] = key < p.Nk ? load4<VEC>(src + (int64_t)key * ld + 4 * piece, 4)
+                                    : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
         }
     };
     auto store_k = [&](int buf) {
@@ -130,25 +160,29 @@ __global__ __launch_bounds__(256 * KSPLIT) void attention_kernel(AttnArgs p) {
     };
     // S^T for this wave's 64 keys of a step (rows 64*half .. +63 of the
     // stage), in 4 sub-blocks of 16: s[kb][r] = S[qrow][kbase + 16kb + r]
+    // The four sub-blocks' accumulations are interleaved, so that an MFMA
+    // never waits for the result of the one just before it.
     auto scores = [&](int buf, f32x4* s) {
         const char* ks = kring + buf * TILE + half * (kBC * kRowB);
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const int krow = 16 * kb + q;                 // A' row of this lane
-            const char* kr = ks + krow * kRowB;
+        for (int kb = 0; kb < 4; ++kb) s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int cc = 0; cc < 4; ++cc) {
+        for (int cc = 0; cc < 4; ++cc) {
+            f32x4 a[4];
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const int krow = 16 * kb + q;             // A' row of this lane
                 // the swizzle of row 64*half + krow is that of krow (64 = 0 mod 16)
-                const f32x4 a = *reinterpret_cast<const f32x4*>(kr + 16 * kswz(krow, 4 * g + cc));
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    s[kb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], qv[4 * cc + e], s[kb], 0, 0, 0);
+                a[kb] = *reinterpret_cast<const f32x4*>(ks + krow * kRowB + 16 * kswz(krow, 4 * g + cc));
             }
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+                    s[kb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[kb][e], qv[4 * cc + e], s[kb], 0, 0, 0);
         }
     };
 
-    const float c = p.scale * kLog2e;   // scores in base-2 exponent units
     float m = -INFINITY;                // running maximum (base 2), same in the 4 lanes of q
     float l = 0.0f;                     // this lane's part of the running weight sum
     f32x4 o[4];                         // O^T blocks: o[db][r] = O[qrow][16g + 4r + db]
@@ -157,18 +191,21 @@ __global__ __launch_bounds__(256 * KSPLIT) void attention_kernel(AttnArgs p) {
 
     // softmax of one step's scores s (in place) and the output products
     auto consume = [&](int it, f32x4* s) {
-        // online softmax in base 2; keys past Nk weigh nothing
-        const int kbase = it * KI + half * kBC + 4 * g;
+        // online softmax in base 2; keys past Nk weigh nothing (only the
+        // last step can hold any)
         float bm = -INFINITY;
+        if ((it + 1) * KI > p.Nk) {
+            const int kbase = it * KI + half * kBC + 4 * g;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (kbase + 16 * kb + r >= p.Nk) s[kb][r] = -INFINITY;
+        }
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float x = s[kb][r] * c;
-                if (kbase + 16 * kb + r >= p.Nk) x = -INFINITY;
-                s[kb][r] = x;
-                bm = fmaxf(bm, x);
-            }
+            for (int r = 0; r < 4; ++r) bm = fmaxf(bm, s[kb][r]);
         bm = fmaxf(bm, __shfl_xor(bm, 16));
         bm = fmaxf(bm, __shfl_xor(bm, 32));
         const float mn = fmaxf(m, bm);
@@ -190,7 +227,7 @@ __global__ __launch_bounds__(256 * KSPLIT) void attention_kernel(AttnArgs p) {
         for (int db = 0; db < 4; ++db) o[db] *= alpha;
 
         // O^T += V^T P^T: step ts uses keys 16(ts/4) + 4g + ts%4 (lane group g)
-        const char* vs = vring + (it & 1) * TILE + half * (kBC * kRowB);
+        const char* vs = vring + (it % 3) * TILE + half * (kBC * kRowB);
 #pragma unroll
         for (int ts = 0; ts < 16; ++ts) {
             const int vrow = 16 * (ts >> 2) + 4 * g + (ts & 3);
@@ -207,25 +244,36 @@ __global__ __launch_bounds__(256 * KSPLIT) void attention_kernel(AttnArgs p) {
     store_k(0);
     store_v(0);
     __syncthreads();
+    f32x4 s[4];
     for (int it = 0; it < ni; ++it) {
         const bool more = it + 1 < ni;
         if (more) {
             load_rows(p.K, p.ldk, it + 1, sk);
             load_rows(p.V, p.ldv, it + 1, sv);
         }
-        f32x4 s[4];
-        scores(it & 1, s);
-        consume(it, s);
+        if (KSPLIT == 1 || half == 0) {
+            scores(it & 1, s);
+            consume(it, s);
+        } else {
+            // half a step behind: the previous step's softmax and output
+            // products first, then this step's scores
+            if (it > 0) consume(it - 1, s);
+            scores(it & 1, s);
+        }
+        // K stage (it+1) & 1 held K(it-1) and V stage (it+1) % 3 held
+        // V(it-2): both last read before the previous barrier
         if (more) {
             store_k((it + 1) & 1);
-            store_v((it + 1) & 1);
+            store_v((it + 1) % 3);
         }
         __syncthreads();
     }
+    if (KSPLIT == 2 && half == 1) consume(ni - 1, s);
 
     if constexpr (KSPLIT == 2) {
         // merge the second key half into the first: both hold the same lanes'
-        // queries and output columns; the buffers are free after the last barrier
+        // queries and output columns; the K ring is free after the last
+        // barrier (the second half's last output products read the V ring)
         float* x = reinterpret_cast<float*>(lds) + (wq * 64 + lane) * 18;
         if (half == 1) {
             x[0] = m;
@@ -274,10 +322,15 @@ hipError_t launch_attention(const AttnArgs& p, bool vec, hipStream_t stream) {
     constexpr int KS = 2;
     const int64_t tiles = (p.Nq + (int64_t)p.br - 1) / p.br;
     const dim3 grid((unsigned)(tiles * p.blocks_per_tile)), block(256 * KS);
-    if (vec)
-        hipLaunchKernelGGL((attention_kernel<true, KS>), grid, block, 0, stream, p);
+    // buffer loads when 32-bit byte offsets cover the rows of one step of K
+    // and of V, and the rows are 16-byte aligned
+    const int64_t span = ((int64_t)(kBC * KS - 1) * std::max(p.ldk, p.ldv) + kD) * 4;
+    if (vec && span <= (int64_t)UINT32_MAX)
+        hipLaunchKernelGGL((attention_kernel<true, true, KS>), grid, block, 0, stream, p);
+    else if (vec)
+        hipLaunchKernelGGL((attention_kernel<true, false, KS>), grid, block, 0, stream, p);
     else
-        hipLaunchKernelGGL((attention_kernel<false, KS>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((attention_kernel<false, false, KS>), grid, block, 0, stream, p);
     return hipGetLastError();
 }
 
