@@ -66,14 +66,17 @@ template <int NB> struct BVec;
 template <> struct BVec<1> {
     using type = float;
     static __device__ __forceinline__ float get(float v, int) { return v; }
+    static __device__ __forceinline__ void set(float& v, int, float x) { v = x; }
 };
 template <> struct BVec<2> {
     using type = f32x2;
     static __device__ __forceinline__ float get(f32x2 v, int n) { return v[n]; }
+    static __device__ __forceinline__ void set(f32x2& v, int n, float x) { v[n] = x; }
 };
 template <> struct BVec<4> {
     using type = f32x4;
     static __device__ __forceinline__ float get(f32x4 v, int n) { return v[n]; }
+    static __device__ __forceinline__ void set(f32x4& v, int n, float x) { v[n] = x; }
 };
 
 
@@ -424,6 +427,34 @@ __global__ __launch_bounds__(64 * WM * WN) void sgemm_mfma_kernel(GemmArgs p) {
     const float alpha = p.alpha, beta = p.beta;
     const int col = n0 + wn * T::TWN + T::NB * l32;
     const int ncols = p.N - col;
+    using CV = typename BVec<T::NB>::type;
+    if (VEC && m0 + BM <= p.M && n_inside) {
+        // Whole tile inside C: the 16 rows of a 32-row block are read before
+        // any is written, so a lane waits for one memory round trip per block
+        // rather than one per row.
+#pragma unroll
+        for (int i = 0; i < T::MB; ++i) {
+            float* base = p.C + (int64_t)(m0 + wm * T::TWM + i * 32 + 4 * h) * p.ldc + col;
+            auto row_ptr = [&](int r) { return base + (int64_t)(8 * (r >> 2) + (r & 3)) * p.ldc; };
+            CV cv[16];
+            if (beta != 0.0f) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) cv[r] = *reinterpret_cast<const CV*>(row_ptr(r));
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                CV o;
+#pragma unroll
+                for (int n = 0; n < T::NB; ++n) {
+                    float v = alpha * acc[i][n][r];
+                    if (beta != 0.0f) v += beta * BVec<T::NB>::get(cv[r], n);
+                    BVec<T::NB>::set(o, n, v);
+                }
+                *reinterpret_cast<CV*>(row_ptr(r)) = o;
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < T::MB; ++i) {
 #pragma unroll
