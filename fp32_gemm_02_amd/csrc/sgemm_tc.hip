@@ -614,6 +614,35 @@ __global__ __launch_bounds__(64 * WM * WN) void tc16_kernel(Tc16Args p) {
     const float alpha = p.alpha, beta = p.beta;
     const int col = n0 + wn * TWN + NB * l32;
     const int ncols = p.N - col;
+    if constexpr (NB == 4) {
+        if (p.vec_c && m0 + BM <= p.M && n0 + BN <= p.N) {
+            // Whole tile inside C: the 16 rows of C of a 32-row block are read
+            // before any is written, one memory round trip per block rather
+            // than one per row.
+#pragma unroll
+            for (int i = 0; i < MB; ++i) {
+                float* base = p.C + (int64_t)(m0 + wm * TWM + i * 32 + 4 * h) * p.ldc + col;
+                auto row_ptr = [&](int r) { return base + (int64_t)(8 * (r >> 2) + (r & 3)) * p.ldc; };
+                f32x4 cv[16];
+                if (beta != 0.0f) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) cv[r] = *reinterpret_cast<const f32x4*>(row_ptr(r));
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    f32x4 o;
+#pragma unroll
+                    for (int n = 0; n < 4; ++n) {
+                        float v = alpha * acc[i][n][r];
+                        if (beta != 0.0f) v += beta * cv[r][n];
+                        o[n] = v;
+                    }
+                    *reinterpret_cast<f32x4*>(row_ptr(r)) = o;
+                }
+            }
+            return;
+        }
+    }
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
 #pragma unroll
