@@ -365,6 +365,8 @@ def main():
                    **(dict(zip(("TM", "TN", "TK"), tiles)) if supertiled else {}),
                    **({"device_budget_mib": args.host_resident,
                        "slots_a_b_c": [plan.a_slots, plan.b_slots, plan.c_slots],
+                       "walk": {g.SGEMM_WALK_ROWS: "rows", g.SGEMM_WALK_SHELLS: "shells",
+                                g.SGEMM_WALK_BLOCKS: "blocks"}[plan.walk],
                        "planned_transfer_bytes": plan.transfer_bytes,
                        "modeled_ms": round(plan.modeled_ms, 3),
                        "inputs_in": "pinned host memory (rate includes all transfers)"}

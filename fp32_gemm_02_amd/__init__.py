@@ -26,6 +26,7 @@ SGEMM_ERR_BUDGET = 5
 SGEMM_ERR_HIP_BASE = 1000
 SGEMM_WALK_ROWS = 0
 SGEMM_WALK_SHELLS = 1
+SGEMM_WALK_BLOCKS = 2
 SGEMM_KIND_GEMM = 0
 SGEMM_KIND_INIT_LEAF = 1
 SGEMM_KIND_TC = 2
@@ -78,7 +79,7 @@ class sgemm_plan(ctypes.Structure):
         return ("sgemm_plan(TM=%d, TN=%d, TK=%d, slots a/b/c=%d/%d/%d, walk=%s, "
                 "device_bytes=%d, transfer_bytes=%.4g, modeled_ms=%.4g)" % (
                     self.TM, self.TN, self.TK, self.a_slots, self.b_slots, self.c_slots,
-                    {SGEMM_WALK_ROWS: "rows", SGEMM_WALK_SHELLS: "shells"}.get(self.walk, self.walk),
+                    {SGEMM_WALK_ROWS: "rows", SGEMM_WALK_SHELLS: "shells", SGEMM_WALK_BLOCKS: "blocks"}.get(self.walk, self.walk),
                     self.device_bytes, self.transfer_bytes, self.modeled_ms))
 
 

@@ -39,7 +39,7 @@ int host_launch_init(int64_t M, int64_t N, float beta, float* C, int64_t ldc,
 namespace {
 
 // Default model rates (MI355X, PCIe 5.0 x16 host link, pinned memory).
-constexpr double kDefaultTflops = 140.0;   // sustained step-leaf rate
+constexpr double kDefaultTflops = 146.0;   // sustained step-leaf rate
 constexpr double kDefaultLinkGBs = 55.0;   // one direction
 constexpr double kDuplex = 1.7;            // both directions at once: this many times one
 constexpr double kCopyMs = 0.010;          // fixed cost of one copy call
@@ -86,6 +86,47 @@ std::vector<std::pair<int64_t, int64_t>> walk_order(int64_t gm, int64_t gn, int3
             for (int64_t pm = 0; pm < std::min(s, gm); ++pm) v.emplace_back(pm, s);
         if (s < gm && s < gn) v.emplace_back(s, s);
     }
+    return v;
+}
+
+// Output super-tiles live at once in a BLOCKS walk: blocks of kBlock x kBlock.
+constexpr int64_t kBlock = 2;
+int64_t live_c_tiles(int64_t gm, int64_t gn, int32_t walk) {
+    return walk == SGEMM_WALK_BLOCKS ? std::min(kBlock, gm) * std::min(kBlock, gn) : 1;
+}
+
+// One step of a schedule: step leaf kt of output super-tile (pm, pn) (kt = -1
+// when there is no K chunk: only the init leaf runs); `first` and `last`
+// mark the tile's first and last step (load or clear C before, store after).
+struct Step {
+    int64_t pm, pn, kt;
+    bool first, last;
+};
+
+// The steps in execution order.  ROWS and SHELLS finish each output
+// super-tile, all its K chunks in turn, before the next.  BLOCKS takes the
+// output super-tiles in blocks of kBlock x kBlock (row by row of blocks) and
+// runs the K loop outside inside a block: chunk kt of every tile of the
+// block, then chunk kt+1.  A block's tiles then share each A and B chunk
+// while it is resident, so the first tiles need a block row of A and a block
+// column of B per chunk, rather than a whole row of A and column of B before
+// the first tile can finish.
+std::vector<Step> walk_steps(int64_t gm, int64_t gn, int64_t nk, int32_t walk) {
+    std::vector<Step> v;
+    const int64_t ks = std::max<int64_t>(nk, 1);
+    v.reserve((size_t)(gm * gn * ks));
+    if (walk == SGEMM_WALK_BLOCKS) {
+        for (int64_t m0 = 0; m0 < gm; m0 += kBlock)
+            for (int64_t n0 = 0; n0 < gn; n0 += kBlock)
+                for (int64_t k = 0; k < ks; ++k)
+                    for (int64_t pm = m0; pm < std::min(m0 + kBlock, gm); ++pm)
+                        for (int64_t pn = n0; pn < std::min(n0 + kBlock, gn); ++pn)
+                            v.push_back({pm, pn, nk > 0 ? k : -1, k == 0, k == ks - 1});
+        return v;
+    }
+    for (const auto& t : walk_order(gm, gn, walk))
+        for (int64_t k = 0; k < ks; ++k)
+            v.push_back({t.first, t.second, nk > 0 ? k : -1, k == 0, k == ks - 1});
     return v;
 }
 
@@ -155,23 +196,27 @@ Modeled simulate(int64_t M, int64_t N, int64_t K, float beta, const Candidate& c
     SlotTable ta(c.na), tb(c.nb);
     std::vector<double> a_ready(c.na, 0), a_free(c.na, 0), b_ready(c.nb, 0), b_free(c.nb, 0),
         c_free(c.nc, 0);
+    std::vector<int64_t> tile_slot((size_t)(gm * gn), -1);
     double h2d = 0, d2h = 0, comp = 0, h2d_bytes = 0, d2h_bytes = 0;
     int64_t ci = 0;
-    for (const auto& t : walk_order(gm, gn, c.walk)) {
-        const int64_t pm = t.first, pn = t.second;
+    for (const Step& t : walk_steps(gm, gn, nk, c.walk)) {
+        const int64_t pm = t.pm, pn = t.pn;
         const int64_t rows = std::min(c.TM, M - pm * c.TM), cols = std::min(c.TN, N - pn * c.TN);
-        const int64_t slot = ci++ % c.nc;
         const double cb = 4.0 * rows * cols;
-        if (beta != 0.0f) {
-            h2d = std::max(h2d, c_free[slot]) + copy_ms(cb);
-            h2d_bytes += cb;
-            comp = std::max(comp, h2d);
-        } else {
-            comp = std::max(comp, c_free[slot]);
+        if (t.first) {
+            const int64_t slot = ci++ % c.nc;
+            tile_slot[(size_t)(pm * gn + pn)] = slot;
+            if (beta != 0.0f) {
+                h2d = std::max(h2d, c_free[slot]) + copy_ms(cb);
+                h2d_bytes += cb;
+                comp = std::max(comp, h2d);
+            } else {
+                comp = std::max(comp, c_free[slot]);
+            }
+            if (beta != 1.0f) comp += kLaunchMs + (beta != 0.0f ? 2 : 1) * cb / (kHbmGBs * 1e9) * 1e3;
         }
-        if (beta != 1.0f) comp += kLaunchMs + (beta != 0.0f ? 2 : 1) * cb / (kHbmGBs * 1e9) * 1e3;
-        for (int64_t kt = 0; kt < nk; ++kt) {
-            const int64_t depth = std::min(c.TK, K - kt * c.TK);
+        if (t.kt >= 0) {
+            const int64_t kt = t.kt, depth = std::min(c.TK, K - kt * c.TK);
             bool load;
             const int64_t sa = ta.acquire(pm * nk + kt, &load);
             if (load) {
@@ -188,9 +233,11 @@ Modeled simulate(int64_t M, int64_t N, int64_t K, float beta, const Candidate& c
             comp = std::max({comp, a_ready[sa], b_ready[sb]}) + step_ms(rows, cols, depth);
             a_free[sa] = b_free[sb] = comp;
         }
-        d2h = std::max(d2h, comp) + copy_ms(cb);
-        d2h_bytes += cb;
-        c_free[slot] = d2h;
+        if (t.last) {
+            d2h = std::max(d2h, comp) + copy_ms(cb);
+            d2h_bytes += cb;
+            c_free[tile_slot[(size_t)(pm * gn + pn)]] = d2h;
+        }
     }
     // both directions together move at most kDuplex times one direction's rate
     const double both = (h2d_bytes + d2h_bytes) / (kDuplex * link) * 1e3;
@@ -237,25 +284,39 @@ int sgemm_plan_supertiles(int64_t M, int64_t N, int64_t K, float beta, int64_t d
             for (int64_t TK : extents(K)) {
                 const int64_t gm = cdiv(M, TM), gn = cdiv(N, TN), nk = cdiv(K, TK);
                 if (gm * gn * nk > kMaxLaunches) continue;
-                const int64_t nc = std::min<int64_t>(2, gm * gn);
                 const int64_t a_all = gm * nk, b_all = nk * gn;
-                const int64_t a_opts[3] = {std::min<int64_t>(2, nk), nk, a_all};
-                const int64_t b_opts[2] = {std::min<int64_t>(2, nk), b_all};
-                for (int ia = 0; ia < 3; ++ia)
-                    for (int ib = 0; ib < 2; ++ib) {
+                const double lower = std::max(min_flop_ms + gm * gn * nk * kLaunchMs, min_link_ms);
+                auto add = [&](int64_t na, int64_t nb, int64_t nc, int32_t walk) {
+                    const int64_t bytes = 4 * (na * slot_floats(TM, TK) + nb * slot_floats(TK, TN) +
+                                               nc * slot_floats(TM, TN));
+                    if (bytes <= device_bytes)
+                        cands.push_back({TM, TN, TK, na, nb, nc, walk, bytes, lower});
+                };
+                const int64_t a_opts[4] = {std::min<int64_t>(2, nk), nk,
+                                           std::min<int64_t>(kBlock * nk, a_all), a_all};
+                const int64_t b_opts[3] = {std::min<int64_t>(2, nk),
+                                           std::min<int64_t>(kBlock * nk, b_all), b_all};
+                for (int ia = 0; ia < 4; ++ia)
+                    for (int ib = 0; ib < 3; ++ib) {
                         const int64_t na = a_opts[ia], nb = b_opts[ib];
-                        if ((ia > 0 && na == a_opts[ia - 1]) || (ib > 0 && nb == b_opts[0])) continue;
-                        const int64_t bytes = 4 * (na * slot_floats(TM, TK) +
-                                                   nb * slot_floats(TK, TN) + nc * slot_floats(TM, TN));
-                        if (bytes > device_bytes) continue;
-                        const double lower =
-                            std::max(min_flop_ms + gm * gn * nk * kLaunchMs, min_link_ms);
+                        bool dup = false;
+                        for (int j = 0; j < ia; ++j) dup |= a_opts[j] == na;
+                        for (int j = 0; j < ib; ++j) dup |= b_opts[j] == nb;
+                        if (dup) continue;
+                        const int64_t nc = std::min<int64_t>(2, gm * gn);
                         // row-major walks keep one row of A resident at most;
                         // shells need all of A and B resident
-                        if (na <= nk)
-                            cands.push_back({TM, TN, TK, na, nb, nc, SGEMM_WALK_ROWS, bytes, lower});
+                        if (na <= nk && (nb == b_opts[0] || nb == b_all)) add(na, nb, nc, SGEMM_WALK_ROWS);
                         if (na == a_all && nb == b_all && gm > 1 && gn > 1)
-                            cands.push_back({TM, TN, TK, na, nb, nc, SGEMM_WALK_SHELLS, bytes, lower});
+                            add(na, nb, nc, SGEMM_WALK_SHELLS);
+                        // blocks: one block's C tiles, or two blocks' (the next
+                        // one's loads overlap this one's steps)
+                        const int64_t live = live_c_tiles(gm, gn, SGEMM_WALK_BLOCKS);
+                        if (live > 1 && na >= std::min<int64_t>(2, nk))
+                            for (int64_t ncb : {live, std::min<int64_t>(2 * live, gm * gn)}) {
+                                add(na, nb, ncb, SGEMM_WALK_BLOCKS);
+                                if (ncb == gm * gn) break;
+                            }
                     }
             }
     if (cands.empty()) return SGEMM_ERR_BUDGET;
@@ -290,7 +351,8 @@ int sgemm_supertiled_host(int64_t M, int64_t N, int64_t K, float alpha, const fl
     if (ldc < std::max<int64_t>(1, N)) return -11;
     if (plan == nullptr || plan->TM < 1 || plan->TN < 1 || plan->TK < 1 || plan->a_slots < 1 ||
         plan->b_slots < 1 || plan->c_slots < 1 ||
-        (plan->walk != SGEMM_WALK_ROWS && plan->walk != SGEMM_WALK_SHELLS))
+        (plan->walk != SGEMM_WALK_ROWS && plan->walk != SGEMM_WALK_SHELLS &&
+         plan->walk != SGEMM_WALK_BLOCKS))
         return -12;
     if (M == 0 || N == 0) return SGEMM_OK;
     const bool steps = K > 0 && alpha != 0.0f;
@@ -312,6 +374,8 @@ int sgemm_supertiled_host(int64_t M, int64_t N, int64_t K, float alpha, const fl
     const int64_t na = steps ? std::min<int64_t>(plan->a_slots, gm * nk) : 0;
     const int64_t nb = steps ? std::min<int64_t>(plan->b_slots, nk * gn) : 0;
     const int64_t nc = std::min<int64_t>(plan->c_slots, gm * gn);
+    // every output super-tile that is live at once needs a C slot of its own
+    if (nc < live_c_tiles(gm, gn, plan->walk)) return -12;
     const int64_t total = na * a_tile + nb * b_tile + nc * c_tile;
 
     float* pool = nullptr;
@@ -369,30 +433,37 @@ int sgemm_supertiled_host(int64_t M, int64_t N, int64_t K, float alpha, const fl
     };
 
     SlotTable ta(std::max<int64_t>(na, 1)), tb(std::max<int64_t>(nb, 1));
+    std::vector<int64_t> tile_slot((size_t)(gm * gn), -1);
     int64_t ci = 0;
-    for (const auto& t : walk_order(gm, gn, plan->walk)) {
+    for (const Step& t : walk_steps(gm, gn, nk, plan->walk)) {
         if (st != SGEMM_OK) break;
-        const int64_t pm = t.first, pn = t.second;
+        const int64_t pm = t.pm, pn = t.pn;
         const int64_t r0 = pm * TM, rows = std::min(TM, M - r0);
         const int64_t c0 = pn * TN, cols = std::min(TN, N - c0);
-        const int64_t slot = ci++ % nc;
-        Slot& cs = sc[slot];
-        // cs.free is recorded after the store of the slot's previous tile (or
-        // at the start): nothing overwrites the slot before that
-        if (beta != 0.0f) {
-            PHOBOS_CHK(hipStreamWaitEvent(h2d, cs.free, 0));
-            PHOBOS_CHK(hipMemcpy2DAsync(cs.dev, ldc_t * sizeof(float), C + r0 * ldc + c0,
-                                        ldc * sizeof(float), cols * sizeof(float), rows,
-                                        hipMemcpyHostToDevice, h2d));
-            PHOBOS_CHK(hipEventRecord(cs.ready, h2d));
-            PHOBOS_CHK(hipStreamWaitEvent(comp, cs.ready, 0));
-        } else {
-            PHOBOS_CHK(hipStreamWaitEvent(comp, cs.free, 0));
+        if (t.first) {
+            // C slots go round-robin over the output super-tiles in the order
+            // they start; a walk never has more tiles live than slots
+            const int64_t slot = ci++ % nc;
+            tile_slot[(size_t)(pm * gn + pn)] = slot;
+            Slot& cs = sc[slot];
+            // cs.free is recorded after the store of the slot's previous tile
+            // (or at the start): nothing overwrites the slot before that
+            if (beta != 0.0f) {
+                PHOBOS_CHK(hipStreamWaitEvent(h2d, cs.free, 0));
+                PHOBOS_CHK(hipMemcpy2DAsync(cs.dev, ldc_t * sizeof(float), C + r0 * ldc + c0,
+                                            ldc * sizeof(float), cols * sizeof(float), rows,
+                                            hipMemcpyHostToDevice, h2d));
+                PHOBOS_CHK(hipEventRecord(cs.ready, h2d));
+                PHOBOS_CHK(hipStreamWaitEvent(comp, cs.ready, 0));
+            } else {
+                PHOBOS_CHK(hipStreamWaitEvent(comp, cs.free, 0));
+            }
+            if (st == SGEMM_OK) st = phobos::host_launch_init(rows, cols, beta, cs.dev, ldc_t, comp);
         }
-        // init leaf, then one step leaf per K chunk
-        if (st == SGEMM_OK) st = phobos::host_launch_init(rows, cols, beta, cs.dev, ldc_t, comp);
-        for (int64_t kt = 0; kt < nk && st == SGEMM_OK; ++kt) {
-            const int64_t k0 = kt * TK, depth = std::min(TK, K - k0);
+        const int64_t slot = tile_slot[(size_t)(pm * gn + pn)];
+        Slot& cs = sc[slot];
+        if (t.kt >= 0 && st == SGEMM_OK) {
+            const int64_t kt = t.kt, k0 = kt * TK, depth = std::min(TK, K - k0);
             Slot* a = acquire(ta, sa, pm * nk + kt, A, lda, r0, k0, rows, depth, lda_t);
             Slot* b = acquire(tb, sb, kt * gn + pn, B, ldb, k0, c0, depth, cols, ldb_t);
             PHOBOS_CHK(hipStreamWaitEvent(comp, a->ready, 0));
@@ -403,13 +474,15 @@ int sgemm_supertiled_host(int64_t M, int64_t N, int64_t K, float alpha, const fl
             PHOBOS_CHK(hipEventRecord(a->free, comp));
             PHOBOS_CHK(hipEventRecord(b->free, comp));
         }
-        // store the finished super-tile on the store stream
-        PHOBOS_CHK(hipEventRecord(c_done[slot], comp));
-        PHOBOS_CHK(hipStreamWaitEvent(d2h, c_done[slot], 0));
-        PHOBOS_CHK(hipMemcpy2DAsync(C + r0 * ldc + c0, ldc * sizeof(float), cs.dev,
-                                    ldc_t * sizeof(float), cols * sizeof(float), rows,
-                                    hipMemcpyDeviceToHost, d2h));
-        PHOBOS_CHK(hipEventRecord(cs.free, d2h));
+        if (t.last) {
+            // store the finished super-tile on the store stream
+            PHOBOS_CHK(hipEventRecord(c_done[slot], comp));
+            PHOBOS_CHK(hipStreamWaitEvent(d2h, c_done[slot], 0));
+            PHOBOS_CHK(hipMemcpy2DAsync(C + r0 * ldc + c0, ldc * sizeof(float), cs.dev,
+                                        ldc_t * sizeof(float), cols * sizeof(float), rows,
+                                        hipMemcpyDeviceToHost, d2h));
+            PHOBOS_CHK(hipEventRecord(cs.free, d2h));
+        }
     }
 #undef PHOBOS_CHK
     // the call returns with C complete in host memory; every stream is

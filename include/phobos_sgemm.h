@@ -274,7 +274,7 @@ int flash_attention_supertiled(int64_t Nq, int64_t Nk, int64_t D, const float* Q
  * it keeps the 256 CUs (ceil(m/256)*ceil(n/256) workgroups in waves of 256)
  * plus 15 us and its C read and write at 5 TB/s, and a copy taking its bytes
  * at the link rate plus 10 us, both directions together at most 1.7 times
- * one direction.  `model` gives the rates (NULL: 140 TFLOP/s, 55 GB/s each
+ * one direction.  `model` gives the rates (NULL: 146 TFLOP/s, 55 GB/s each
  * way).  Nothing is run.  Host-only.  Arguments: 1 M, 2 N, 3 K, 4 beta (0: C
  * is only written), 5 device_bytes, 6 model, 7 out.  SGEMM_ERR_BUDGET if
  * nothing fits, SGEMM_ERR_TOO_LARGE for a dimension above 2^30; candidates
@@ -310,11 +310,14 @@ typedef struct sgemm_plan_model {
 
 #define SGEMM_WALK_ROWS 0     /* output super-tiles row by row (the pages' order) */
 #define SGEMM_WALK_SHELLS 1   /* growing squares: shell s = tiles with max(pm, pn) == s */
+#define SGEMM_WALK_BLOCKS 2   /* 2 x 2 blocks of output super-tiles, row by row of blocks, the
+                                 K loop outside inside a block: c_slots must cover the tiles of
+                                 one block (up to 4), else -12 */
 
 typedef struct sgemm_plan {
     int64_t TM, TN, TK;                /* super-tile extents */
     int32_t a_slots, b_slots, c_slots; /* device tile buffers of each kind */
-    int32_t walk;                      /* SGEMM_WALK_ROWS or SGEMM_WALK_SHELLS */
+    int32_t walk;                      /* SGEMM_WALK_ROWS, _SHELLS or _BLOCKS */
     int64_t device_bytes;              /* device memory the slots take */
     double transfer_bytes;             /* host<->device bytes of the schedule */
     double modeled_ms;                 /* modeled time of the whole product */

@@ -38,6 +38,47 @@ SHAPES = [(16384, 16384, 16384), (5003, 3001, 2047), (65536, 512, 4096), (300, 2
 BUDGETS = [1 << 34, 2 << 30, 1 << 30, 256 << 20, 64 << 20, 8 << 20]
 
 
+def _steps(gm, gn, nk, walk):
+    """(pm, pn, kt) of a walk in execution order (kt over range(nk))."""
+    if walk == g.SGEMM_WALK_BLOCKS:
+        for m0 in range(0, gm, 2):
+            for n0 in range(0, gn, 2):
+                for kt in range(nk):
+                    for pm in range(m0, min(m0 + 2, gm)):
+                        for pn in range(n0, min(n0 + 2, gn)):
+                            yield pm, pn, kt
+        return
+    if walk == g.SGEMM_WALK_ROWS:
+        tiles = [(pm, pn) for pm in range(gm) for pn in range(gn)]
+    else:   # growing squares: shell s = row s left of the diagonal, column s
+        tiles = []   # above it, then the corner (s, s)
+        for sh in range(max(gm, gn)):
+            if sh < gm:
+                tiles += [(sh, pn) for pn in range(min(sh, gn))]
+            if sh < gn:
+                tiles += [(pm, sh) for pm in range(min(sh, gm))]
+            if sh < gm and sh < gn:
+                tiles.append((sh, sh))
+    for pm, pn in tiles:
+        for kt in range(nk):
+            yield pm, pn, kt
+
+
+def _lru_loads(seq, slots):
+    """Number of loads an LRU set of `slots` slots makes over the tile ids `seq`."""
+    from collections import OrderedDict
+    held, loads = OrderedDict(), 0
+    for t in seq:
+        if t in held:
+            held.move_to_end(t)
+        else:
+            loads += 1
+            if len(held) == slots:
+                held.popitem(last=False)
+            held[t] = True
+    return loads
+
+
 @pytest.mark.parametrize("M,N,K", SHAPES)
 def test_plan_is_a_candidate_and_fits_the_budget(M, N, K):
     for budget, beta in itertools.product(BUDGETS, (0.0, 1.0)):
@@ -48,22 +89,32 @@ def test_plan_is_a_candidate_and_fits_the_budget(M, N, K):
             continue
         assert p.TM in _extents(M) and p.TN in _extents(N) and p.TK in _extents(K)
         gm, gn, nk = _cdiv(M, p.TM), _cdiv(N, p.TN), _cdiv(K, p.TK)
-        assert p.a_slots in (min(2, nk), nk, gm * nk)
-        assert p.b_slots in (min(2, nk), nk * gn)
-        assert p.c_slots == min(2, gm * gn)
+        assert p.a_slots in (min(2, nk), nk, min(2 * nk, gm * nk), gm * nk)
+        assert p.b_slots in (min(2, nk), min(2 * nk, nk * gn), nk * gn)
+        live = min(2, gm) * min(2, gn)
         if p.walk == g.SGEMM_WALK_SHELLS:
             # growing squares only when every A and B super-tile stays resident
             assert p.a_slots == gm * nk and p.b_slots == nk * gn and gm > 1 and gn > 1
+            assert p.c_slots == min(2, gm * gn)
+        elif p.walk == g.SGEMM_WALK_ROWS:
+            assert p.a_slots <= nk and p.b_slots in (min(2, nk), nk * gn)
+            assert p.c_slots == min(2, gm * gn)
         else:
-            assert p.walk == g.SGEMM_WALK_ROWS and p.a_slots <= nk
+            # blocks: a C slot for every tile of a block, or of two blocks
+            assert p.walk == g.SGEMM_WALK_BLOCKS and live > 1
+            assert p.c_slots in (live, min(2 * live, gm * gn))
         # the slot bytes the executor allocates, within the budget
         assert p.device_bytes == _device_bytes(p) <= budget
-        # host<->device bytes: A once or once per column of super-tiles, B
-        # once or once per row, C out (and in unless beta == 0)
-        a = 4 * M * K * (1 if p.a_slots >= nk else gn)
-        b = 4 * K * N * (1 if p.b_slots >= nk * gn else gm)
+        # host<->device bytes: what LRU slot sets load over the walk (all
+        # super-tiles of a kind have the same extents when they divide M, N
+        # and K), plus C out (and in unless beta == 0)
         c = 4 * M * N * (2 if beta else 1)
-        assert p.transfer_bytes == pytest.approx(a + b + c, rel=1e-12)
+        if M % p.TM == 0 and N % p.TN == 0 and K % p.TK == 0 and gm * gn * nk <= 4096:
+            steps = list(_steps(gm, gn, nk, p.walk))
+            a = _lru_loads([pm * nk + kt for pm, pn, kt in steps], p.a_slots) * 4 * p.TM * p.TK
+            b = _lru_loads([kt * gn + pn for pm, pn, kt in steps], p.b_slots) * 4 * p.TK * p.TN
+            assert p.transfer_bytes == pytest.approx(a + b + c, rel=1e-12)
+        assert p.transfer_bytes >= 4.0 * (M * K + K * N) + c
         assert p.modeled_ms > 0
 
 
@@ -88,7 +139,8 @@ def test_plan_when_everything_fits_keeps_operands_resident():
     M = N = K = 16384
     p = g.sgemm_plan_supertiles(M, N, K, 1.0, 16 << 30)
     gm, gn, nk = _cdiv(M, p.TM), _cdiv(N, p.TN), _cdiv(K, p.TK)
-    assert p.a_slots in (nk, gm * nk) and p.b_slots == nk * gn
+    # a row (or a block's rows) of A resident, or all of it; all of B
+    assert p.a_slots in (nk, 2 * nk, gm * nk) and p.b_slots == nk * gn
     assert p.transfer_bytes == 4.0 * (M * K + K * N + 2 * M * N)
     # super-tiles large enough to fill the 256 CUs with 256x256 workgroup tiles
     assert _cdiv(p.TM, 256) * _cdiv(p.TN, 256) >= 256
@@ -104,11 +156,22 @@ def test_plan_struct_layout_matches_the_header():
     assert g.sgemm_plan.walk.offset == 36
 
 
-def test_planner_prefers_shells_when_b_would_arrive_all_at_once():
+def test_planner_avoids_rows_when_b_would_arrive_all_at_once():
     """Everything resident, square grid: a row-major walk needs all of B during
-    the first row of outputs, growing squares spread the loads."""
+    the first row of outputs; growing squares or blocks with the K loop
+    outside spread the loads."""
     p = g.sgemm_plan_supertiles(16384, 16384, 16384, 1.0, 16 << 30)
-    assert p.walk == g.SGEMM_WALK_SHELLS
+    assert p.walk in (g.SGEMM_WALK_SHELLS, g.SGEMM_WALK_BLOCKS)
+
+
+def test_blocks_walk_at_small_budgets():
+    """With room for a few super-tiles only, blocks with the K loop outside
+    share each resident A and B chunk among a block's output tiles: the
+    planner takes them, and models them faster than the best row-major plan
+    of the same budget."""
+    M = N = K = 16384
+    p = g.sgemm_plan_supertiles(M, N, K, 1.0, 256 << 20)
+    assert p.walk == g.SGEMM_WALK_BLOCKS and p.c_slots >= 4
 
 
 def test_plan_streams_when_memory_is_short():
@@ -174,7 +237,18 @@ def test_host_executor_argument_checks(args, want):
 
 
 @pytest.mark.parametrize("plan", [None, _plan(TM=0), _plan(TN=-1), _plan(TK=0), _plan(a=0),
-                                  _plan(b=0), _plan(c=0), _plan(walk=2), _plan(walk=-1)])
+                                  _plan(b=0), _plan(c=0), _plan(walk=3), _plan(walk=-1)])
 def test_host_executor_plan_checks(plan):
     assert g.sgemm_supertiled_host_raw(4, 4, 4, 1.0, 8, 4, 8, 4, 1.0, 8, 4, plan,
                                        stream=0) == -12
+
+
+def test_host_executor_blocks_need_a_c_slot_per_tile_of_a_block():
+    """A 2 x 2 block of output super-tiles is live at once: fewer C slots are
+    rejected before anything is allocated."""
+    blocks = g.SGEMM_WALK_BLOCKS
+    assert g.sgemm_supertiled_host_raw(200, 200, 64, 1.0, 8, 200, 8, 200, 1.0, 8, 200,
+                                       _plan(TM=64, TN=64, c=3, walk=blocks), stream=0) == -12
+    # a 1 x 4 grid has blocks of two tiles
+    assert g.sgemm_supertiled_host_raw(64, 200, 64, 1.0, 8, 64, 8, 200, 1.0, 8, 200,
+                                       _plan(TM=64, TN=64, c=1, walk=blocks), stream=0) == -12

@@ -54,7 +54,7 @@ def _check(w, x, plan, **kw):
     return out
 
 
-ROWS, SHELLS = g.SGEMM_WALK_ROWS, g.SGEMM_WALK_SHELLS
+ROWS, SHELLS, BLOCKS = g.SGEMM_WALK_ROWS, g.SGEMM_WALK_SHELLS, g.SGEMM_WALK_BLOCKS
 
 # (M, N, K), (TM, TN, TK), slots a/b/c, walk, alpha, beta
 CASES = [
@@ -68,6 +68,11 @@ CASES = [
     ((500, 200, 130), (96, 64, 64), (18, 12, 2), SHELLS, 1.0, 0.0),    # 6x4 grid: rows past the square
     ((200, 500, 130), (64, 96, 64), (12, 18, 1), SHELLS, 1.0, 1.0),    # 4x6: columns past the square
     ((300, 270, 200), (128, 128, 64), (2, 2, 2), SHELLS, 2.0, -1.0),   # shells with evictions
+    # blocks of 2 x 2 output super-tiles, the K loop outside inside a block
+    ((300, 270, 200), (128, 128, 64), (2, 2, 4), BLOCKS, 1.5, 0.5),    # 3x3 grid: edge blocks, evictions
+    ((300, 270, 200), (128, 128, 64), (8, 12, 8), BLOCKS, 1.0, 1.0),   # a block row of A, all of B
+    ((500, 200, 130), (96, 64, 64), (6, 6, 4), BLOCKS, 1.0, 0.0),      # 6x4 grid, beta = 0
+    ((64, 200, 70), (64, 64, 16), (1, 1, 2), BLOCKS, 2.0, -1.0),       # 1x4 grid: blocks of two
 ]
 
 
@@ -93,11 +98,12 @@ def test_host_executor_without_steps():
     for K, alpha, beta in ((0, 1.0, -2.0), (50, 0.0, 0.5), (50, 0.0, 0.0)):
         w = wl.custom(90, 70, K, alpha, beta, seed=3, lda=max(K, 1))
         x = wl.make_inputs(w)
-        out, _, _ = run_host(w, x, _plan(32, 32, 16, 2, 2, 2))
         want = (np.float32(beta) * x.logical("C")).astype(np.float32) if beta else \
             np.zeros((w.M, w.N), np.float32)
-        assert np.array_equal(gu.logical_c(w, out).view(np.int32), want.view(np.int32))
-        gu.check_pads(w, x, out)
+        for plan in (_plan(32, 32, 16, 2, 2, 2), _plan(32, 32, 16, 2, 2, 4, walk=BLOCKS)):
+            out, _, _ = run_host(w, x, plan)
+            assert np.array_equal(gu.logical_c(w, out).view(np.int32), want.view(np.int32))
+            gu.check_pads(w, x, out)
 
 
 def test_host_executor_pageable_memory_and_side_stream():
