@@ -10,9 +10,9 @@
 // br = Nq for the monolithic form), each worked by ceil(br/64) workgroups of
 // one launch.  One workgroup owns 64 query rows of its super-tile, 16 per
 // query group; each group has two waves that take alternate blocks of 64
-// keys (the workgroup stages 128 keys of K and V per step through LDS,
-// double-buffered, loaded one step ahead through registers) and merge their
-// running statistics at the end.  Both products run on the FP32 matrix cores
+// keys (the workgroup stages 128 keys of K and V per step in rings of LDS
+// stages, loaded one step ahead by direct global-to-LDS loads) and merge
+// their running statistics at the end.  Both products run on the FP32 matrix cores
 // (v_mfma_f32_16x16x4_f32, lane layout checked on the GPU with an in-bounds
 // probe; l = lane, g = l / 16, q = l % 16):
 //   src A: lane l holds A'[q][g]   (16 x 4)
@@ -48,9 +48,6 @@ constexpr int kRowB = kD * 4;                      // bytes of one K or V row in
 constexpr int kTile = kBC * kRowB;                 // bytes of one K or V tile
 constexpr int kStage = 2 * kTile;                  // K and V
 constexpr float kLog2e = 1.4426950408889634f;
-// Fourth word of a raw buffer descriptor on gfx9-class GPUs: 32-bit data
-// format, no swizzle, no index stride.
-constexpr int kBufferWord3 = 0x00020000;
 
 // K rows are stored with their 16-byte pieces XOR-swizzled by row.  The LDS
 // serves a 128-bit read for 16 lanes per cycle, from a 256-byte bank window,
@@ -67,15 +64,15 @@ __device__ __forceinline__ int kswz(int row, int piece) { return piece ^ (row & 
 // running (maximum, weight sum, weighted sum) are merged at the end.
 //
 // K has a ring of two stages and V one of three: K stage it & 1 and V stage
-// it % 3 hold the rows of step it while those of step it+1 are in flight
-// through registers.  The two waves of a query group share a SIMD (waves w
+// it % 3 hold the rows of step it while those of step it+1 are loaded into
+// the next stages.  The two waves of a query group share a SIMD (waves w
 // and w+4), and the barrier that ends each step would keep them in the same
 // phase, taking their exponentials at the same time while the matrix core
 // idles.  So the second wave runs half a step behind: in step it it takes
 // the exponentials and output products of step it-1 (whose V rows the third
 // V stage keeps), then the scores of step it, and finishes step ni-1 after
 // the loop.
-template <bool VEC, bool BUF, int KSPLIT>
+template <bool VEC, bool DMA, int KSPLIT>
 __global__ __launch_bounds__(256 * KSPLIT) void attention_kernel(AttnArgs p) {
     constexpr int NT = 256 * KSPLIT;           // threads
     constexpr int KI = kBC * KSPLIT;           // keys per step
@@ -114,35 +111,51 @@ __global__ __launch_bounds__(256 * KSPLIT) void attention_kernel(AttnArgs p) {
     }
 
     // ---- K / V rows of one step: thread t moves 16-byte pieces t + NT*i ----
-    // BUF: buffer loads.  A step's rows lie within 4 GiB of its first row, so
-    // each load is that row's buffer descriptor (scalar registers) plus a
-    // 32-bit byte offset per lane, with no per-lane address arithmetic or
-    // branch.  The descriptor's size ends after row Nk-1, and the hardware
-    // returns zeros past it, which is the zero fill of the rows past Nk.
-    f32x4 sk[LD], sv[LD];
+    // DMA: direct global-to-LDS loads, no registers and no LDS stores.  The
+    // wave's i-th load fills the 64 16-byte slots (i*NW + wave)*64 + lane of
+    // a tile; slot u holds row u/16 and stored piece u%16, which for K is
+    // logical piece (u%16) ^ swizzle(row), so the swizzle is applied to the
+    // global address.  Each load takes the step's first row as a
+    // wave-uniform base and a 32-bit byte offset per lane.  Rows past Nk read
+    // row Nk-1 instead: their scores are masked and their weights are 0.  The
+    // loads of step it+1 are issued at the start of step it and land by the
+    // barrier that ends it.
+    // Otherwise the rows come through registers and are stored to LDS before
+    // that barrier.
+    constexpr int NW = NT / 64;
+    f32x4 sk[DMA ? 1 : LD], sv[DMA ? 1 : LD];
+    auto issue_dma = [&](const float* src, int64_t ld, int it, char* tile, bool swizzled) {
+        const int k0 = it * KI, last = p.Nk - 1 - k0;
+        const float* base = src + (int64_t)k0 * ld;
+#pragma unroll
+        for (int i = 0; i < LD; ++i) {
+            const int u = (i * NW + wave) * 64 + lane, row = u >> 4, sp = u & 15;
+            const int lp = swizzled ? kswz(row, sp) : sp;
+            const uint32_t off = ((uint32_t)min(row, last) * (uint32_t)ld + 4 * lp) * 4;
+            dma16s(base, off, tile + (i * NW + wave) * 1024);
+        }
+    };
     auto load_rows = [&](const float* src, int64_t ld, int it, f32x4* dst) {
         const int k0 = it * KI;
-        if constexpr (BUF) {
-            const int64_t bytes = ((int64_t)(p.Nk - k0 - 1) * ld + kD) * 4;
-            const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-                const_cast<float*>(src + (int64_t)k0 * ld), (short)0,
-                (int)(uint32_t)min<int64_t>(bytes, UINT32_MAX), kBufferWord3);
 #pragma unroll
-            for (int i = 0; i < LD; ++i) {
-                const int u = t + NT * i, row = u >> 4, piece = u & 15;
-                dst[i] = __builtin_amdgcn_raw_buffer_load_b128(
-                    rsrc, (row * (uint32_t)ld + 4 * piece) * 4, 0, 0);
-            }
+        for (int i = 0; i < LD; ++i) {
+            const int u = t + NT * i, row = u >> 4, piece = u & 15, key = k0 + row;
+            dst[i] = key < p.Nk ? load4<VEC>(src + (int64_t)key * ld + 4 * piece, 4)
+                                : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    };
+    // the loads of step it into K stage it & 1 and V stage it % 3
+    auto fetch = [&](int it) {
+        if constexpr (DMA) {
+            issue_dma(p.K, p.ldk, it, kring + (it & 1) * TILE, true);
+            issue_dma(p.V, p.ldv, it, vring + (it % 3) * TILE, false);
         } else {
-#pragma unroll
-            for (int i = 0; i < LD; ++i) {
-                const int u = t + NT * i, row = u >> 4, piece = u & 15, key = k0 + row;
-                dst[i] = key < p.Nk ? load4<VEC>(src + (int64_t)key * ld + 4 * piece, 4)
-                                    : f32x4{0.f, 0.f, 0.f, 0.f};
-            }
+            load_rows(p.K, p.ldk, it, sk);
+            load_rows(p.V, p.ldv, it, sv);
         }
     };
     auto store_k = [&](int buf) {
+        if constexpr (DMA) return;
         char* ks = kring + buf * TILE;
 #pragma unroll
         for (int i = 0; i < LD; ++i) {
@@ -151,6 +164,7 @@ __global__ __launch_bounds__(256 * KSPLIT) void attention_kernel(AttnArgs p) {
         }
     };
     auto store_v = [&](int buf) {
+        if constexpr (DMA) return;
         char* vs = vring + buf * TILE;
 #pragma unroll
         for (int i = 0; i < LD; ++i) {
@@ -239,18 +253,15 @@ __global__ __launch_bounds__(256 * KSPLIT) void attention_kernel(AttnArgs p) {
         }
     };
 
-    load_rows(p.K, p.ldk, 0, sk);
-    load_rows(p.V, p.ldv, 0, sv);
+    fetch(0);
     store_k(0);
     store_v(0);
+    __builtin_amdgcn_s_waitcnt(kWaitVm<0>);
     __syncthreads();
     f32x4 s[4];
     for (int it = 0; it < ni; ++it) {
         const bool more = it + 1 < ni;
-        if (more) {
-            load_rows(p.K, p.ldk, it + 1, sk);
-            load_rows(p.V, p.ldv, it + 1, sv);
-        }
+        if (more) fetch(it + 1);
         if (KSPLIT == 1 || half == 0) {
             scores(it & 1, s);
             consume(it, s);
@@ -266,6 +277,7 @@ __global__ __launch_bounds__(256 * KSPLIT) void attention_kernel(AttnArgs p) {
             store_k((it + 1) & 1);
             store_v((it + 1) % 3);
         }
+        __builtin_amdgcn_s_waitcnt(kWaitVm<0>);   // this wave's loads of step it+1
         __syncthreads();
     }
     if (KSPLIT == 2 && half == 1) consume(ni - 1, s);
@@ -322,7 +334,7 @@ hipError_t launch_attention(const AttnArgs& p, bool vec, hipStream_t stream) {
     constexpr int KS = 2;
     const int64_t tiles = (p.Nq + (int64_t)p.br - 1) / p.br;
     const dim3 grid((unsigned)(tiles * p.blocks_per_tile)), block(256 * KS);
-    // buffer loads when 32-bit byte offsets cover the rows of one step of K
+    // direct loads when 32-bit byte offsets cover the rows of one step of K
     // and of V, and the rows are 16-byte aligned
     const int64_t span = ((int64_t)(kBC * KS - 1) * std::max(p.ldk, p.ldv) + kD) * 4;
     if (vec && span <= (int64_t)UINT32_MAX)
