@@ -59,6 +59,23 @@ constexpr float kLog2e = 1.4426950408889634f;
 // row).  The plain swizzle row & 15 put lanes 0-3 and 20-23 on the same groups.
 __device__ __forceinline__ int kswz(int row, int piece) { return piece ^ (row & 11); }
 
+// Maximum and sum over the four lanes l, l^16, l^32, l^48 (the lanes that hold
+// one query), with the register swaps of 16- and 32-lane halves: a value
+// swapped with a copy of itself leaves lane l and lane l^32 (l^16) in the
+// same lane of the two registers.  No LDS permute is involved.
+__device__ __forceinline__ float quad_max(float x) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float quad_sum(float x) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // KSPLIT = 2: two waves per group of 16 queries, each taking every other
 // block of 64 keys (128 keys per step), two waves per SIMD in all; their
 // running (maximum, weight sum, weighted sum) are merged at the end.
@@ -220,8 +237,7 @@ __global__ __launch_bounds__(256 * KSPLIT) void attention_kernel(AttnArgs p) {
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
             for (int r = 0; r < 4; ++r) bm = fmaxf(bm, s[kb][r]);
-        bm = fmaxf(bm, __shfl_xor(bm, 16));
-        bm = fmaxf(bm, __shfl_xor(bm, 32));
+        bm = quad_max(bm);
         const float mn = fmaxf(m, bm);
         // a key half that has met no key yet keeps weight 0 (not exp2(-inf + inf))
         const float base = (mn == -INFINITY) ? 0.0f : mn;
@@ -307,8 +323,7 @@ __global__ __launch_bounds__(256 * KSPLIT) void attention_kernel(AttnArgs p) {
     }
 
     // ---- epilogue: the weight sum over all keys, O = o / l ----
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    l = quad_sum(l);
     if (!qin) return;
     const float inv = 1.0f / l;
     float* dst = p.O + (int64_t)qrow * p.ldo + 16 * g;
