@@ -80,15 +80,17 @@ __device__ __forceinline__ float quad_sum(float x) {
 // block of 64 keys (128 keys per step), two waves per SIMD in all; their
 // running (maximum, weight sum, weighted sum) are merged at the end.
 //
-// K has a ring of two stages and V one of three: K stage it & 1 and V stage
-// it % 3 hold the rows of step it while those of step it+1 are loaded into
-// the next stages.  The two waves of a query group share a SIMD (waves w
-// and w+4), and the barrier that ends each step would keep them in the same
-// phase, taking their exponentials at the same time while the matrix core
-// idles.  So the second wave runs half a step behind: in step it it takes
-// the exponentials and output products of step it-1 (whose V rows the third
-// V stage keeps), then the scores of step it, and finishes step ni-1 after
-// the loop.
+// With direct loads, K and V have rings of two LDS stages, and each wave
+// forms the scores of the next step before the softmax of the current one
+// (see the loop).  With the register path, K has two stages and V three: K
+// stage it & 1 and V stage it % 3 hold the rows of step it while those of
+// step it+1 are in flight.  The two waves of a query group share a SIMD
+// (waves w and w+4), and the barrier that ends each step would keep them in
+// the same phase, taking their exponentials at the same time while the
+// matrix core idles.  So there the second wave runs half a step behind: in
+// step it it takes the exponentials and output products of step it-1 (whose
+// V rows the third V stage keeps), then the scores of step it, and finishes
+// step ni-1 after the loop.
 template <bool VEC, bool DMA, int KSPLIT>
 __global__ __launch_bounds__(256 * KSPLIT) void attention_kernel(AttnArgs p) {
     constexpr int NT = 256 * KSPLIT;           // threads
@@ -221,7 +223,7 @@ __global__ __launch_bounds__(256 * KSPLIT) void attention_kernel(AttnArgs p) {
     for (int db = 0; db < 4; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // softmax of one step's scores s (in place) and the output products
-    auto consume = [&](int it, f32x4* s) {
+    auto consume = [&](int it, f32x4* s, int vstage) {
         // online softmax in base 2; keys past Nk weigh nothing (only the
         // last step can hold any)
         float bm = -INFINITY;
@@ -257,7 +259,7 @@ __global__ __launch_bounds__(256 * KSPLIT) void attention_kernel(AttnArgs p) {
         for (int db = 0; db < 4; ++db) o[db] *= alpha;
 
         // O^T += V^T P^T: step ts uses keys 16(ts/4) + 4g + ts%4 (lane group g)
-        const char* vs = vring + (it % 3) * TILE + half * (kBC * kRowB);
+        const char* vs = vring + vstage * TILE + half * (kBC * kRowB);
 #pragma unroll
         for (int ts = 0; ts < 16; ++ts) {
             const int vrow = 16 * (ts >> 2) + 4 * g + (ts & 3);
@@ -269,6 +271,34 @@ __global__ __launch_bounds__(256 * KSPLIT) void attention_kernel(AttnArgs p) {
         }
     };
 
+  if constexpr (DMA) {
+    // Scores one step ahead: in step it the wave forms the scores of step
+    // it+1 (K stage (it+1) & 1) before the softmax and output products of
+    // step it (V stage it & 1), so its exponentials of step it can overlap
+    // its own MFMAs.  K(it+2) and V(it+1) are loaded meanwhile.
+    issue_dma(p.K, p.ldk, 0, kring, true);
+    issue_dma(p.V, p.ldv, 0, vring, false);
+    if (ni > 1) issue_dma(p.K, p.ldk, 1, kring + TILE, true);
+    __builtin_amdgcn_s_waitcnt(kWaitVm<0>);
+    __syncthreads();
+    f32x4 s[4];
+    scores(0, s);
+    for (int it = 0; it < ni; ++it) {
+        // K stage it & 1 held K(it), read in step it-1; V stage (it+1) & 1
+        // held V(it-1), read in step it-1
+        if (it + 2 < ni) issue_dma(p.K, p.ldk, it + 2, kring + (it & 1) * TILE, true);
+        if (it + 1 < ni) issue_dma(p.V, p.ldv, it + 1, vring + ((it + 1) & 1) * TILE, false);
+        f32x4 sn[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) sn[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (it + 1 < ni) scores((it + 1) & 1, sn);
+        consume(it, s, it & 1);
+        __builtin_amdgcn_s_waitcnt(kWaitVm<0>);
+        __syncthreads();
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) s[kb] = sn[kb];
+    }
+  } else {
     fetch(0);
     store_k(0);
     store_v(0);
@@ -280,11 +310,11 @@ __global__ __launch_bounds__(256 * KSPLIT) void attention_kernel(AttnArgs p) {
         if (more) fetch(it + 1);
         if (KSPLIT == 1 || half == 0) {
             scores(it & 1, s);
-            consume(it, s);
+            consume(it, s, it % 3);
         } else {
             // half a step behind: the previous step's softmax and output
             // products first, then this step's scores
-            if (it > 0) consume(it - 1, s);
+            if (it > 0) consume(it - 1, s, (it - 1) % 3);
             scores(it & 1, s);
         }
         // K stage (it+1) & 1 held K(it-1) and V stage (it+1) % 3 held
@@ -296,7 +326,8 @@ __global__ __launch_bounds__(256 * KSPLIT) void attention_kernel(AttnArgs p) {
         __builtin_amdgcn_s_waitcnt(kWaitVm<0>);   // this wave's loads of step it+1
         __syncthreads();
     }
-    if (KSPLIT == 2 && half == 1) consume(ni - 1, s);
+    if (KSPLIT == 2 && half == 1) consume(ni - 1, s, (ni - 1) % 3);
+  }
 
     if constexpr (KSPLIT == 2) {
         // merge the second key half into the first: both hold the same lanes'
