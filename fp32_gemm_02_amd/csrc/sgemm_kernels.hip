@@ -134,20 +134,18 @@ __global__ __launch_bounds__(64 * WM * WN) void sgemm_mfma_kernel(GemmArgs p) {
     struct Staged {
         f32x4 a[T::LA], b[T::LB];
     };
-    auto load_regs = [&](Staged& r, int k0) {
-#pragma unroll
-        for (int i = 0; i < T::LA; ++i) {
-            const int idx = tid + i * T::NT;
+    // Piece j (0 .. LA+LB-1) of a chunk: A's pieces first, then B's.
+    auto load_piece = [&](Staged& r, int k0, int j) {
+        if (j < T::LA) {
+            const int idx = tid + j * T::NT;
             const int row = idx / T::QA;
             const int gk = k0 + (idx % T::QA) * 4;
             const int grow = m0 + row;
             const int nvalid = (grow < p.M) ? (p.K - gk) : 0;
             const float* src = p.A + (int64_t)(grow < p.M ? grow : 0) * p.lda + gk;
-            r.a[i] = load4<VEC>(src, nvalid);
-        }
-#pragma unroll
-        for (int i = 0; i < T::LB; ++i) {
-            const int idx = tid + i * T::NT;
+            r.a[j] = load4<VEC>(src, nvalid);
+        } else {
+            const int i = j - T::LA, idx = tid + i * T::NT;
             const int gk = k0 + idx / T::QB;
             const int gn = n0 + (idx % T::QB) * 4;
             const int nvalid = (gk < p.K) ? (p.N - gn) : 0;
@@ -155,21 +153,26 @@ __global__ __launch_bounds__(64 * WM * WN) void sgemm_mfma_kernel(GemmArgs p) {
             r.b[i] = load4<VEC>(src, nvalid);
         }
     };
-    auto store_regs = [&](const Staged& r, int s) {
+    auto store_piece = [&](const Staged& r, int s, int j) {
         float* As = smem + s * T::STAGE;
         float* Bs = As + T::A_FLOATS;
-#pragma unroll
-        for (int i = 0; i < T::LA; ++i) {
-            const int idx = tid + i * T::NT;
+        if (j < T::LA) {
+            const int idx = tid + j * T::NT;
             const int row = idx / T::QA;
             const int q = (idx % T::QA) ^ swz<T::QA>(row);
-            *reinterpret_cast<f32x4*>(As + row * BK + 4 * q) = r.a[i];
+            *reinterpret_cast<f32x4*>(As + row * BK + 4 * q) = r.a[j];
+        } else {
+            const int idx = tid + (j - T::LA) * T::NT;
+            *reinterpret_cast<f32x4*>(Bs + 4 * idx) = r.b[j - T::LA];
         }
+    };
+    auto load_regs = [&](Staged& r, int k0) {
 #pragma unroll
-        for (int i = 0; i < T::LB; ++i) {
-            const int idx = tid + i * T::NT;
-            *reinterpret_cast<f32x4*>(Bs + 4 * idx) = r.b[i];
-        }
+        for (int j = 0; j < T::LA + T::LB; ++j) load_piece(r, k0, j);
+    };
+    auto store_regs = [&](const Staged& r, int s) {
+#pragma unroll
+        for (int j = 0; j < T::LA + T::LB; ++j) store_piece(r, s, j);
     };
 
     // ---- direct path: global -> LDS, whole K chunks of aligned operands ----
@@ -305,22 +308,25 @@ __global__ __launch_bounds__(64 * WM * WN) void sgemm_mfma_kernel(GemmArgs p) {
         store_regs(st, buf);
         return false;
     };
-    // ---- interior fast path ----
-    // A tile clear of the N edge, with K a whole number of chunks, loads
-    // every chunk directly.  With a two-stage ring its stage loop then has no
-    // data-dependent branch, and the work between MFMAs is spread out: the
-    // fragment reads for the next k-step, the direct loads and the stage
-    // barrier are each issued right after one MFMA, while it runs, instead of
-    // as one group between k-steps that leaves the matrix core idle until the
-    // group has issued.  The loop body is straight-line code, so the
-    // compiler's LDS waits are exact: before an MFMA it waits only for the
-    // fragments that MFMA reads, not for the next stage's first reads issued
-    // after the barrier.
+    // ---- fast path ----
+    // With a two-stage ring, the stage loop of a tile has no data-dependent
+    // branch, and the work between MFMAs is spread out: the fragment reads
+    // for the next k-step, the loads of the next chunk and the stage barrier
+    // are each issued right after one MFMA, while it runs, instead of as one
+    // group between k-steps that leaves the matrix core idle until the group
+    // has issued.  The loop body is straight-line code, so the compiler's LDS
+    // waits are exact: before an MFMA it waits only for the fragments that
+    // MFMA reads, not for the next stage's first reads issued after the
+    // barrier.  Every chunk loads directly except, on a tile at the N edge or
+    // when K is not a whole number of chunks, the last one, which holds row
+    // K-1 of B: that one comes through registers with bounds checks.
     constexpr int MFMAS = T::MB * T::NB;                // MFMAs per k-step
     constexpr int DMA_AT = (MFMAS >= 10) ? 6 : MFMAS - DMA_PER_STEP;
+    const bool reg_last = !n_inside || p.K % BK != 0;
+    const int nk_direct = reg_last ? (p.K - 1) / BK : p.K / BK;   // chunks loaded directly
     bool done = false;
     if constexpr (NS == 2 && T::MB + 2 <= MFMAS && DMA_AT >= 0) {
-        if (VEC && narrow && n_inside && p.K % BK == 0) {
+        if (VEC && narrow && nk_direct >= 1) {
             auto read_a_one = [&](const float* base, int c, f32x4* dst, int i) {
                 dst[i] = *reinterpret_cast<const f32x4*>(base + a_row + i * 32 * BK + a_piece[c]);
             };
@@ -330,11 +336,12 @@ __global__ __launch_bounds__(64 * WM * WN) void sgemm_mfma_kernel(GemmArgs p) {
             read_a(smem, 0, fa[0]);
             fb[0] = read_b(smem, 0);
             int cur = 0;
-            // One stage: k-steps of stage kt from buffer cur; with MORE, the
-            // loads of stage kt+1 into the other buffer and, at the last
-            // k-step, the barrier and the first reads of stage kt+1.
-            auto stage = [&](int kt, auto more_tag) {
-                constexpr bool MORE = decltype(more_tag)::value;
+            // One stage: the k-steps of chunk kt from buffer cur, while chunk
+            // kt+1 is loaded directly into the other buffer (NEXT 1; 0: no
+            // next chunk here); at the last k-step, the barrier and the first
+            // reads of chunk kt+1.
+            auto stage = [&](int kt, auto next_tag) {
+                constexpr int NEXT = decltype(next_tag)::value;
                 const float* base = smem + cur * T::STAGE;
                 const int nb = cur ^ 1;
                 const float* nbase = smem + nb * T::STAGE;
@@ -352,10 +359,11 @@ __global__ __launch_bounds__(64 * WM * WN) void sgemm_mfma_kernel(GemmArgs p) {
                             if (m == 0) fb[(kk + 1) & 1] = read_b(base, kk + 1);
                             if ((kk + 1) % 4 == 0 && m >= 1 && m <= T::MB)
                                 read_a_one(base, (kk + 1) / 4, fa[((kk + 1) / 4) & 1], m - 1);
-                        } else if (MORE) {
-                            // stage kt+1 has landed everywhere, and every
-                            // wave has read stage kt's buffer for the last
-                            // time (its fragments are in registers)
+                        } else if (NEXT != 0) {
+                            // chunk kt+1 has landed (and its register-path
+                            // stores are done) everywhere, and every wave has
+                            // read chunk kt's buffer for the last time (its
+                            // fragments are in registers)
                             if (m == 0) {
                                 __builtin_amdgcn_s_waitcnt(kWaitVm<0>);
                                 asm volatile("s_barrier" ::: "memory");
@@ -363,7 +371,7 @@ __global__ __launch_bounds__(64 * WM * WN) void sgemm_mfma_kernel(GemmArgs p) {
                             if (m == 1) fb[0] = read_b(nbase, 0);
                             if (m >= 2 && m < 2 + T::MB) read_a_one(nbase, 0, fa[0], m - 2);
                         }
-                        if (MORE && kk < DMA_STEPS && m >= DMA_AT && m < DMA_AT + DMA_PER_STEP) {
+                        if (NEXT == 1 && kk < DMA_STEPS && m >= DMA_AT && m < DMA_AT + DMA_PER_STEP) {
                             const int j = kk * DMA_PER_STEP + (m - DMA_AT);
                             if (j < DIRECT_LOADS) load_direct_one(lk0, nb, j);
                         }
@@ -372,13 +380,27 @@ __global__ __launch_bounds__(64 * WM * WN) void sgemm_mfma_kernel(GemmArgs p) {
                 }
                 cur = nb;
             };
-            for (int kt = 0; kt + 1 < nk; ++kt) stage(kt, std::true_type{});
-            stage(nk - 1, std::false_type{});
+            using Direct = std::integral_constant<int, 1>;
+            using Last = std::integral_constant<int, 0>;
+            for (int kt = 0; kt + 1 < nk_direct; ++kt) stage(kt, Direct{});
+            stage(nk_direct - 1, Last{});
+            if (reg_last) {
+                // The last chunk through registers, into the buffer chunk
+                // nk_direct-2 used (read for the last time before the barrier
+                // that ended it); one barrier publishes it.
+                Staged st;
+                load_regs(st, nk_direct * BK);
+                store_regs(st, cur);
+                __syncthreads();
+                read_a(smem + cur * T::STAGE, 0, fa[0]);
+                fb[0] = read_b(smem + cur * T::STAGE, 0);
+                stage(nk_direct, Last{});
+            }
             done = true;
         }
     }
 
-    // ---- general path: edge tiles, K tails, three-stage rings ----
+    // ---- general path: three-stage rings, unaligned operands, K below two chunks ----
     if (!done) {
         bool pend = false;
         issue(0, 0);
