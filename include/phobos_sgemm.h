@@ -138,7 +138,12 @@ int sgemm_set_config(const sgemm_config* cfg);
 /*
  * The tile tuner, after "Show HN: Phobos", section "Runtime": every candidate
  * tile is built ahead of time; each is timed once, the best three get a
- * longer run, and the fastest of those wins.
+ * longer run, and the fastest of those wins.  Before the first timing the
+ * built-in choice runs for about 100 ms, so that the chip's clock has risen;
+ * the short timings each cover about 1 ms of launches.  The built-in choice
+ * joins the longer run, which takes five rounds of `reps` runs of each
+ * contender in turn and ranks them by their median; it stays the choice
+ * unless another tile is more than 0.5% faster.
  * sgemm_tune_candidates (host only, no GPU work) writes into `out` (room for
  * `cap`) the compiled configurations that survive pruning for this shape:
  * tile extents inside the @autotune ranges of the "@cluster" page's matmul
@@ -150,8 +155,8 @@ int sgemm_set_config(const sgemm_config* cfg);
  * itself (inputs filled with a fixed pseudo-random pattern), then records
  * the winner for this (M, N, K, lda, ldb, ldc) so that later sgemm calls of
  * that shape use it.  `reps` is the number of timed runs of each of the top
- * three (>= 1; the pages' long probe).  `winner` (may be NULL) receives the
- * choice and `winner_ms` (may be NULL) its mean time.  Synchronises
+ * three in each round (>= 1; the pages' long probe).  `winner` (may be NULL)
+ * receives the choice and `winner_ms` (may be NULL) its median time per call.  Synchronises
  * `stream`.  Arguments: 1 M, 2 N, 3 K, 4 lda, 5 ldb, 6 ldc, 7 reps,
  * 8 stream, 9 winner, 10 winner_ms.
  */
