@@ -428,16 +428,19 @@ struct Tc16Shape {
     static constexpr int MB = TWM / 32, NB = TWN / 32;
     static constexpr int ROWB = BK * 2, PR = ROWB / 16;
     static constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB, STAGE = A_BYTES + B_BYTES;
-    static constexpr int LDS_BYTES = NS * STAGE;
+    // NS == 5: a ring of five one-operand slots (A and B of a chunk apart)
+    static constexpr bool SPLIT = NS == 5;
+    static constexpr int LDS_BYTES = SPLIT ? 5 * A_BYTES : NS * STAGE;
     static constexpr int DA = A_BYTES / 1024 / NW, DB = B_BYTES / 1024 / NW;   // per wave
     static constexpr int D = DA + DB;
     static_assert(BK == 32 || BK == 64, "4 or 8 pieces per LDS row");
     static_assert(KS % 2 == 0, "operand double buffer returns to slot 0 each chunk");
-    static_assert(NS >= 2 && NS <= 4, "ring depth");
+    static_assert(NS >= 2 && NS <= 5, "ring depth");
+    static_assert(!SPLIT || A_BYTES == B_BYTES, "one slot size");
     static_assert(DA * 1024 * NW == A_BYTES && DB * 1024 * NW == B_BYTES, "whole loads per wave");
     static_assert(TWM % 32 == 0 && TWN % 32 == 0 && (NB == 1 || NB == 2 || NB == 4), "wave tile");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS of one CU");
-    static_assert((NS - 2) * D <= 63, "s_waitcnt vmcnt range");
+    static_assert((SPLIT ? DA : (NS - 2) * D) <= 63, "s_waitcnt vmcnt range");
 };
 
 // s_waitcnt for at most n outstanding direct loads (n a multiple of d, at
@@ -541,6 +544,86 @@ __global__ __launch_bounds__(64 * WM * WN) void tc16_kernel(Tc16Args p) {
     constexpr int GAP = 1;                           // loads as early as possible
     static_assert(T::D * GAP <= (KS - 1) * MF, "a chunk's loads are issued before its barrier");
     static_assert(MB + NB <= MF, "the next k-step's reads fit between this one's MFMAs");
+    if constexpr (T::SPLIT) {
+        // Five slots of one operand chunk each: A of chunk c in slot 2c mod 5,
+        // B in slot 2c+1 mod 5.  While chunk c is computed, B of chunk c+1 and
+        // then A of chunk c+2 are loaded into the two slots chunk c-1 used, so
+        // half of every chunk is in flight for two chunks' time and the
+        // barrier that ends chunk c waits only for the loads issued before A
+        // of c+2.  A two-stage ring of whole chunks makes that barrier wait
+        // for all 64 KB issued at the start of the chunk, and the loads'
+        // latency at that depth, not their rate, bounds the loop.
+        constexpr int SLOT = T::A_BYTES;
+        auto mod5 = [](int x) { return x >= 5 ? x - 5 : x; };
+        auto load_a = [&](int c, int slot, int j) {
+            dma16s(p.A + (int64_t)m0 * p.ld + (int64_t)c * BK, da[j],
+                   lds + slot * SLOT + (j * NW + wave) * 1024);
+        };
+        auto load_b = [&](int c, int slot, int j) {
+            dma16s(p.B + (int64_t)n0 * p.ld + (int64_t)c * BK, db[j],
+                   lds + slot * SLOT + (j * NW + wave) * 1024);
+        };
+        auto frag2 = [&](const char* As, const char* Bs, int s, int slot, int r) {
+            if (r < MB)
+                fa[slot][r] = frag(As, wm * TWM + r * 32 + l32, s);
+            else
+                fb[slot][r - MB] = frag(Bs, wn * TWN + (r - MB) * 32 + l32, s);
+        };
+#pragma unroll
+        for (int j = 0; j < DA; ++j) load_a(0, 0, j);
+#pragma unroll
+        for (int j = 0; j < DB; ++j) load_b(0, 1, j);
+        if (nk > 1) {
+#pragma unroll
+            for (int j = 0; j < DA; ++j) load_a(1, 2, j);
+            __builtin_amdgcn_s_waitcnt(kWaitVm<DA>);
+        } else {
+            __builtin_amdgcn_s_waitcnt(kWaitVm<0>);
+        }
+        asm volatile("s_barrier" ::: "memory");
+#pragma unroll
+        for (int r = 0; r < MB + NB; ++r) frag2(lds, lds + SLOT, 0, 0, r);
+        int sa = 0;   // slot of A of the chunk being computed
+        // One chunk.  MORE: a chunk follows (B of c+1 is loaded during this
+        // one); LA: A of c+2 is loaded too.
+        auto chunk2 = [&](int c, auto more_tag, auto la_tag) {
+            constexpr bool MORE = decltype(more_tag)::value, LA = decltype(la_tag)::value;
+            const char* As = lds + sa * SLOT;
+            const char* Bs = lds + mod5(sa + 1) * SLOT;
+            const int sa_n = mod5(sa + 2);
+            const char* As_n = lds + sa_n * SLOT;
+            const char* Bs_n = lds + mod5(sa + 3) * SLOT;
+            const int sb_load = mod5(sa + 3), sa_load = mod5(sa + 4);   // chunk c-1's slots
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+#pragma unroll
+                for (int m = 0; m < MF; ++m) {
+                    const int i = m / NB, j = m % NB;
+                    acc[i][j] = F::mma(fa[s & 1][i], fb[s & 1][j], acc[i][j]);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (s + 1 < KS) {
+                        if (m < MB + NB) frag2(As, Bs, s + 1, (s + 1) & 1, m);
+                    } else if (MORE) {
+                        if (m == 0) {
+                            __builtin_amdgcn_s_waitcnt(kWaitVm<LA ? DA : 0>);
+                            asm volatile("s_barrier" ::: "memory");
+                        }
+                        if (m < MB + NB) frag2(As_n, Bs_n, 0, 0, m);
+                    }
+                    const int g = s * MF + m;
+                    if (MORE && g < DB) load_b(c + 1, sb_load, g);
+                    if (LA && g >= DB && g < DB + DA) load_a(c + 2, sa_load, g - DB);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            sa = sa_n;
+        };
+        using T1 = std::true_type;
+        using F0 = std::false_type;
+        for (int c = 0; c + 2 < nk; ++c) chunk2(c, T1{}, T1{});
+        if (nk >= 2) chunk2(nk - 2, T1{}, F0{});
+        chunk2(nk - 1, F0{}, F0{});
+    } else {
 #pragma unroll
     for (int c = 0; c < NS - 1; ++c)
         if (c < nk) issue(c, c);
@@ -608,6 +691,7 @@ __global__ __launch_bounds__(64 * WM * WN) void tc16_kernel(Tc16Args p) {
         // each barrier waits for every load still in flight
         for (int kt = 0; kt + 1 < nk; ++kt) chunk(kt, T1{}, F0{}, std::integral_constant<int, 0>{});
         chunk(nk - 1, F0{}, F0{}, std::integral_constant<int, 0>{});
+    }
     }
 
     // ---- epilogue: C <- alpha*acc + beta*C (beta == 0: C not read) ----
@@ -719,7 +803,7 @@ hipError_t launch_tc_cast(int fmt, const float* A, int64_t lda, bool vec_a, cons
 #define PHOBOS_TC16_TABLE(FMT)                                                              \
     {                                                                                       \
         PHOBOS_TC16_CFG(FMT, 256, 256, 32, 4, 2, 2), PHOBOS_TC16_CFG(FMT, 256, 256, 32, 4, 4, 2), \
-            PHOBOS_TC16_CFG(FMT, 256, 256, 64, 2, 2, 2), PHOBOS_TC16_CFG(FMT, 256, 256, 64, 2, 4, 2), \
+            PHOBOS_TC16_CFG(FMT, 256, 256, 64, 5, 2, 2), PHOBOS_TC16_CFG(FMT, 256, 256, 64, 5, 4, 2), \
             PHOBOS_TC16_CFG(FMT, 256, 128, 32, 4, 2, 2), PHOBOS_TC16_CFG(FMT, 128, 128, 64, 2, 2, 2), \
     }
 

@@ -90,17 +90,24 @@ def test_quick_returns(fmt):
         gu.check_pads(w, x, out)
 
 
+# the staged 256x256 tile with 64-k chunks in the ring of five one-operand slots
+STAGED64 = (256, 256, 64, 4, 2, 1)
+
+
+@pytest.mark.parametrize("staged", [STAGED, STAGED64], ids=["k32_ring4", "k64_ring5"])
 @pytest.mark.parametrize("shape", [(1000, 777, 300), (512, 512, 1024), (300, 1100, 70)])
 @pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)
-def test_staged_equals_fused(fmt, shape):
-    """Same tile, same k order, same conversion: the staged form (cast pass +
-    16-bit GEMM) gives the fused form's values exactly."""
+def test_staged_equals_fused(fmt, shape, staged):
+    """Same wave tile, same k order, same conversion: the staged form (cast
+    pass + 16-bit GEMM) gives the fused form's values exactly, whatever its
+    chunk depth."""
     M, N, K = shape
     w = wl.custom(M, N, K, 0.75, -1.25, seed=M + K, lda=K + 3, ldb=N + 1, ldc=N + 5)
     x = wl.make_inputs(w)
     g.sgemm_tc_set_config(fmt, FUSED)
     fused = gu.logical_c(w, gu.run(w, x, fmt=fmt))
-    g.sgemm_tc_set_config(fmt, STAGED)
+    print(f"tc fmt {fmt} staged {staged} shape {shape}", flush=True)
+    g.sgemm_tc_set_config(fmt, staged)
     staged_out = gu.run(w, x, fmt=fmt)
     staged = gu.logical_c(w, staged_out)
     bad = np.argwhere(fused != staged)
