@@ -526,7 +526,8 @@ __global__ __launch_bounds__(64 * WM * WN) void tc16_kernel(Tc16Args p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    // Ring of NS buffers; chunk c lives in buffer c % NS.  Chunk c+NS-1 is
+    // NS of 2 to 4: a ring of NS buffers of whole chunks (NS == 5 is the
+    // split ring below); chunk c lives in buffer c % NS.  Chunk c+NS-1 is
     // loaded during chunk c into the buffer chunk c-1 used (every wave
     // finished reading it before the barrier that ended chunk c-1).  The
     // barrier that ends chunk c comes after the first MFMA of its last
@@ -536,10 +537,9 @@ __global__ __launch_bounds__(64 * WM * WN) void tc16_kernel(Tc16Args p) {
     //
     // Between MFMAs: each MFMA is followed by at most one fragment read (for
     // the next k-step), one direct load (the chunk's loads follow its first
-    // MFMAs, as early as possible: with a two-stage ring they have one chunk
-    // to land) and, at the last k-step, the barrier.  Each is issued while the MFMA before it
-    // runs, and the stage loop is straight-line code, so the compiler's LDS
-    // waits are exact.
+    // MFMAs, as early as possible) and, at the last k-step, the barrier.
+    // Each is issued while the MFMA before it runs, and the stage loop is
+    // straight-line code, so the compiler's LDS waits are exact.
     constexpr int MF = MB * NB;                      // MFMAs per k-step
     constexpr int GAP = 1;                           // loads as early as possible
     static_assert(T::D * GAP <= (KS - 1) * MF, "a chunk's loads are issued before its barrier");
@@ -625,73 +625,73 @@ __global__ __launch_bounds__(64 * WM * WN) void tc16_kernel(Tc16Args p) {
         chunk2(nk - 1, F0{}, F0{});
     } else {
 #pragma unroll
-    for (int c = 0; c < NS - 1; ++c)
-        if (c < nk) issue(c, c);
-    wait_loads_and_barrier<T::D>(min(NS - 2, nk - 1));
-    read_step(0, 0, 0);
-    int cur = 0;
-    auto frag_one = [&](int buf, int s, int slot, int r) {
-        const char* As = lds + buf * T::STAGE;
-        const char* Bs = As + T::A_BYTES;
-        if (r < MB)
-            fa[slot][r] = frag(As, wm * TWM + r * 32 + l32, s);
-        else
-            fb[slot][r - MB] = frag(Bs, wn * TWN + (r - MB) * 32 + l32, s);
-    };
-    // One chunk.  LOAD: chunk kt+NS-1 is loaded during it; MORE: a chunk
-    // follows; LATER: loads that may still be in flight at its barrier.
-    auto chunk = [&](int kt, auto more_tag, auto load_tag, auto later_tag) {
-        constexpr bool MORE = decltype(more_tag)::value, LOAD = decltype(load_tag)::value;
-        constexpr int LATER = decltype(later_tag)::value;
-        const int nxt = (cur + 1 == NS) ? 0 : cur + 1;
-        const int lbuf = (cur == 0) ? NS - 1 : cur - 1;
-        char* As = lds + lbuf * T::STAGE;
-        char* Bs = As + T::A_BYTES;
-        const int64_t k0 = (int64_t)(kt + NS - 1) * BK;
-        const uint16_t* a0 = p.A + (int64_t)m0 * p.ld + k0;
-        const uint16_t* b0 = p.B + (int64_t)n0 * p.ld + k0;
+        for (int c = 0; c < NS - 1; ++c)
+            if (c < nk) issue(c, c);
+        wait_loads_and_barrier<T::D>(min(NS - 2, nk - 1));
+        read_step(0, 0, 0);
+        int cur = 0;
+        auto frag_one = [&](int buf, int s, int slot, int r) {
+            const char* As = lds + buf * T::STAGE;
+            const char* Bs = As + T::A_BYTES;
+            if (r < MB)
+                fa[slot][r] = frag(As, wm * TWM + r * 32 + l32, s);
+            else
+                fb[slot][r - MB] = frag(Bs, wn * TWN + (r - MB) * 32 + l32, s);
+        };
+        // One chunk.  LOAD: chunk kt+NS-1 is loaded during it; MORE: a chunk
+        // follows; LATER: loads that may still be in flight at its barrier.
+        auto chunk = [&](int kt, auto more_tag, auto load_tag, auto later_tag) {
+            constexpr bool MORE = decltype(more_tag)::value, LOAD = decltype(load_tag)::value;
+            constexpr int LATER = decltype(later_tag)::value;
+            const int nxt = (cur + 1 == NS) ? 0 : cur + 1;
+            const int lbuf = (cur == 0) ? NS - 1 : cur - 1;
+            char* As = lds + lbuf * T::STAGE;
+            char* Bs = As + T::A_BYTES;
+            const int64_t k0 = (int64_t)(kt + NS - 1) * BK;
+            const uint16_t* a0 = p.A + (int64_t)m0 * p.ld + k0;
+            const uint16_t* b0 = p.B + (int64_t)n0 * p.ld + k0;
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
+            for (int s = 0; s < KS; ++s) {
 #pragma unroll
-            for (int m = 0; m < MF; ++m) {
-                const int i = m / NB, j = m % NB;
-                acc[i][j] = F::mma(fa[s & 1][i], fb[s & 1][j], acc[i][j]);
-                __builtin_amdgcn_sched_barrier(0);
-                if (s + 1 < KS) {
-                    if (m < MB + NB) frag_one(cur, s + 1, (s + 1) & 1, m);
-                } else if (MORE) {
-                    if (m == 0) {
-                        __builtin_amdgcn_s_waitcnt(kWaitVm<LATER * T::D>);
-                        asm volatile("s_barrier" ::: "memory");
+                for (int m = 0; m < MF; ++m) {
+                    const int i = m / NB, j = m % NB;
+                    acc[i][j] = F::mma(fa[s & 1][i], fb[s & 1][j], acc[i][j]);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (s + 1 < KS) {
+                        if (m < MB + NB) frag_one(cur, s + 1, (s + 1) & 1, m);
+                    } else if (MORE) {
+                        if (m == 0) {
+                            __builtin_amdgcn_s_waitcnt(kWaitVm<LATER * T::D>);
+                            asm volatile("s_barrier" ::: "memory");
+                        }
+                        if (m < MB + NB) frag_one(nxt, 0, 0, m);
                     }
-                    if (m < MB + NB) frag_one(nxt, 0, 0, m);
+                    const int g = s * MF + m;
+                    if (LOAD && g % GAP == 0 && g / GAP < T::D) {
+                        const int d = g / GAP;
+                        if (d < DA)
+                            dma16s(a0, da[d], As + (d * NW + wave) * 1024);
+                        else
+                            dma16s(b0, db[d - DA], Bs + ((d - DA) * NW + wave) * 1024);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-                const int g = s * MF + m;
-                if (LOAD && g % GAP == 0 && g / GAP < T::D) {
-                    const int d = g / GAP;
-                    if (d < DA)
-                        dma16s(a0, da[d], As + (d * NW + wave) * 1024);
-                    else
-                        dma16s(b0, db[d - DA], Bs + ((d - DA) * NW + wave) * 1024);
-                }
-                __builtin_amdgcn_sched_barrier(0);
             }
+            cur = nxt;
+        };
+        using T1 = std::true_type;
+        using F0 = std::false_type;
+        if (nk >= NS) {
+            for (int kt = 0; kt + NS - 1 < nk; ++kt) chunk(kt, T1{}, T1{}, std::integral_constant<int, NS - 2>{});
+            if constexpr (NS >= 4) chunk(nk - 3, T1{}, F0{}, std::integral_constant<int, 1>{});
+            if constexpr (NS >= 3) chunk(nk - 2, T1{}, F0{}, std::integral_constant<int, 0>{});
+            chunk(nk - 1, F0{}, F0{}, std::integral_constant<int, 0>{});
+        } else {
+            // fewer chunks than ring stages: the prologue issued all of them, and
+            // each barrier waits for every load still in flight
+            for (int kt = 0; kt + 1 < nk; ++kt) chunk(kt, T1{}, F0{}, std::integral_constant<int, 0>{});
+            chunk(nk - 1, F0{}, F0{}, std::integral_constant<int, 0>{});
         }
-        cur = nxt;
-    };
-    using T1 = std::true_type;
-    using F0 = std::false_type;
-    if (nk >= NS) {
-        for (int kt = 0; kt + NS - 1 < nk; ++kt) chunk(kt, T1{}, T1{}, std::integral_constant<int, NS - 2>{});
-        if constexpr (NS >= 4) chunk(nk - 3, T1{}, F0{}, std::integral_constant<int, 1>{});
-        if constexpr (NS >= 3) chunk(nk - 2, T1{}, F0{}, std::integral_constant<int, 0>{});
-        chunk(nk - 1, F0{}, F0{}, std::integral_constant<int, 0>{});
-    } else {
-        // fewer chunks than ring stages: the prologue issued all of them, and
-        // each barrier waits for every load still in flight
-        for (int kt = 0; kt + 1 < nk; ++kt) chunk(kt, T1{}, F0{}, std::integral_constant<int, 0>{});
-        chunk(nk - 1, F0{}, F0{}, std::integral_constant<int, 0>{});
-    }
     }
 
     // ---- epilogue: C <- alpha*acc + beta*C (beta == 0: C not read) ----
