@@ -85,6 +85,9 @@ WORKLOADS = [
              0.5, 2.0, ("N", "N/64", "U"), 3),
     Workload("unaligned_5003x3001x2047", "sgemm", 5003, 3001, 2047, 2048, 3008, 3008,
              -1.0, 0.25, ("U", "U", "U"), 4),
+    # the super-tiled product's shape and inputs (same seed) as one monolithic call
+    Workload("monolithic_16384", "sgemm", 16384, 16384, 16384, 16384, 16384, 16384, 1.0, 1.0,
+             ("U", "U", "U"), 2),
 ]
 
 BY_NAME = {w.name: w for w in WORKLOADS}
