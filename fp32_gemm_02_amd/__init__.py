@@ -23,6 +23,7 @@ SGEMM_ERR_NO_CONFIG = 2
 SGEMM_ERR_TOO_LARGE = 3
 SGEMM_ERR_ALLOC = 4
 SGEMM_ERR_BUDGET = 5
+SGEMM_ERR_IO = 6
 SGEMM_ERR_HIP_BASE = 1000
 SGEMM_WALK_ROWS = 0
 SGEMM_WALK_SHELLS = 1
@@ -100,6 +101,9 @@ _SIGNATURES = {
                               ctypes.c_int),
     "sgemm_tune": ([_i64, _i64, _i64, _i64, _i64, _i64, _i32, _vp,
                     ctypes.POINTER(sgemm_config), ctypes.POINTER(_f32)], ctypes.c_int),
+    "sgemm_tune_cache_load": ([ctypes.c_char_p, ctypes.POINTER(_i32)], ctypes.c_int),
+    "sgemm_tune_cache_save": ([ctypes.c_char_p, ctypes.POINTER(_i32)], ctypes.c_int),
+    "sgemm_tune_forget": ([], ctypes.c_int),
     "sgemm_tc": ([_i64, _i64, _i64, _f32, _vp, _i64, _vp, _i64, _f32, _vp, _i64, _i32, _vp],
                  ctypes.c_int),
     "sgemm_tc_config_count": ([_i32], ctypes.c_int),
@@ -298,6 +302,27 @@ def sgemm_tune(M, N, K, lda, ldb, ldc, reps=20, stream=None):
     _check(lib().sgemm_tune(M, N, K, lda, ldb, ldc, reps, _stream(stream), ctypes.byref(c),
                             ctypes.byref(ms)), "sgemm_tune")
     return c, ms.value
+
+
+def sgemm_tune_cache_load(path):
+    """Add a tuning cache file's entries to the process's table; returns their number."""
+    n = _i32()
+    _check(lib().sgemm_tune_cache_load(os.fsencode(path), ctypes.byref(n)),
+           "sgemm_tune_cache_load")
+    return n.value
+
+
+def sgemm_tune_cache_save(path):
+    """Write the process's tuned table to a cache file; returns the entries written."""
+    n = _i32()
+    _check(lib().sgemm_tune_cache_save(os.fsencode(path), ctypes.byref(n)),
+           "sgemm_tune_cache_save")
+    return n.value
+
+
+def sgemm_tune_forget():
+    """Empty the process's tuned table; returns the number of entries removed."""
+    return lib().sgemm_tune_forget()
 
 
 def sgemm_plan_supertiles(M, N, K, beta, device_bytes, gemm_tflops=None, link_gbs=None):

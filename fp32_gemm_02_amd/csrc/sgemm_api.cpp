@@ -4,13 +4,17 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include <unistd.h>
+
 #include <algorithm>
+#include <cerrno>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <map>
 #include <mutex>
+#include <string>
 #include <tuple>
 #include <vector>
 
@@ -109,7 +113,112 @@ int env_forced_entry() {
     return entry;
 }
 
+// ---- tuning cache: one JSON object per line, read key by key
+
+// The integer after "key": on the line; false if absent or not a number.
+bool json_int(const char* line, const char* key, int64_t* out) {
+    char pat[24];
+    std::snprintf(pat, sizeof pat, "\"%s\"", key);
+    const char* q = std::strstr(line, pat);
+    if (q == nullptr) return false;
+    q += std::strlen(pat);
+    while (*q == ' ' || *q == '\t') ++q;
+    if (*q++ != ':') return false;
+    char* end = nullptr;
+    errno = 0;
+    const long long v = std::strtoll(q, &end, 10);
+    if (end == q || errno != 0) return false;
+    *out = (int64_t)v;
+    return true;
+}
+
+int cache_load(const char* path, int32_t* count) {
+    FILE* f = std::fopen(path, "r");
+    if (f == nullptr) return SGEMM_ERR_IO;
+    static const char* const keys[] = {"M", "N", "K", "lda", "ldb", "ldc",
+                                       "bm", "bn", "bk", "wm", "wn"};
+    std::vector<std::pair<ShapeKey, int>> got;
+    std::string line;
+    char buf[256];
+    bool more = true;
+    while (more) {
+        line.clear();
+        // one whole line, however long
+        while ((more = std::fgets(buf, sizeof buf, f) != nullptr)) {
+            line += buf;
+            if (!line.empty() && line.back() == '\n') break;
+        }
+        if (line.empty()) continue;
+        int64_t v[11];
+        bool ok = true;
+        for (int i = 0; i < 11 && ok; ++i) ok = json_int(line.c_str(), keys[i], &v[i]);
+        if (!ok) continue;
+        const int64_t M = v[0], N = v[1], K = v[2], lda = v[3], ldb = v[4], ldc = v[5];
+        if (M < 1 || N < 1 || K < 1 || M > kMaxDim || N > kMaxDim || K > kMaxDim || lda < K ||
+            ldb < N || ldc < N)
+            continue;
+        bool small = true;
+        for (int i = 6; i < 11; ++i) small = small && v[i] >= 1 && v[i] <= 4096;
+        if (!small) continue;
+        const int e = find_entry(sgemm_config{(int)v[6], (int)v[7], (int)v[8], (int)v[9],
+                                              (int)v[10]});
+        if (e < 0) continue;
+        got.emplace_back(ShapeKey{M, N, K, lda, ldb, ldc}, e);
+    }
+    const bool read_error = std::ferror(f) != 0;
+    std::fclose(f);
+    if (read_error) return SGEMM_ERR_IO;
+    std::lock_guard<std::mutex> lk(g_mu);
+    for (const auto& kv : got) g_tuned[kv.first] = kv.second;
+    if (count) *count = (int32_t)got.size();
+    return SGEMM_OK;
+}
+
+int cache_save(const char* path, int32_t* count) {
+    std::vector<std::pair<ShapeKey, int>> rows;
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        rows.assign(g_tuned.begin(), g_tuned.end());
+    }
+    const std::string tmp = std::string(path) + ".tmp." + std::to_string((long long)getpid());
+    FILE* f = std::fopen(tmp.c_str(), "w");
+    if (f == nullptr) return SGEMM_ERR_IO;
+    bool ok = true;
+    for (const auto& kv : rows) {
+        const sgemm_config& c = kKernelTable[kv.second].cfg;
+        ok = ok && std::fprintf(f,
+                                "{\"M\": %lld, \"N\": %lld, \"K\": %lld, \"lda\": %lld, "
+                                "\"ldb\": %lld, \"ldc\": %lld, \"bm\": %d, \"bn\": %d, "
+                                "\"bk\": %d, \"wm\": %d, \"wn\": %d}\n",
+                                (long long)std::get<0>(kv.first), (long long)std::get<1>(kv.first),
+                                (long long)std::get<2>(kv.first), (long long)std::get<3>(kv.first),
+                                (long long)std::get<4>(kv.first), (long long)std::get<5>(kv.first),
+                                c.bm, c.bn, c.bk, c.wm, c.wn) > 0;
+    }
+    ok = (std::fclose(f) == 0) && ok;
+    if (!ok || std::rename(tmp.c_str(), path) != 0) {
+        (void)std::remove(tmp.c_str());
+        return SGEMM_ERR_IO;
+    }
+    if (count) *count = (int32_t)rows.size();
+    return SGEMM_OK;
+}
+
+// SGEMM_TUNE_CACHE: the file named there, if present, is loaded once, before
+// the process's first configuration choice.
+const char* env_cache_path() {
+    const char* v = std::getenv("SGEMM_TUNE_CACHE");
+    return (v && *v) ? v : nullptr;
+}
+void load_env_cache_once() {
+    static std::once_flag once;
+    std::call_once(once, [] {
+        if (const char* path = env_cache_path()) (void)cache_load(path, nullptr);
+    });
+}
+
 int choose_entry(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc) {
+    load_env_cache_once();
     {
         std::lock_guard<std::mutex> lk(g_mu);
         if (g_forced >= 0) return g_forced;
@@ -639,6 +748,7 @@ int sgemm_tune(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_
     if (reps < 1) return -7;
     if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return SGEMM_ERR_TOO_LARGE;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    load_env_cache_once();
 
     std::vector<sgemm_config> cands(kKernelCount);
     const int nc = sgemm_tune_candidates(M, N, K, cands.data(), kKernelCount);
@@ -745,7 +855,25 @@ int sgemm_tune(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_
     }
     if (winner) *winner = kKernelTable[best].cfg;
     if (winner_ms) *winner_ms = best_ms;
+    if (const char* path = env_cache_path()) return cache_save(path, nullptr);
     return SGEMM_OK;
+}
+
+int sgemm_tune_cache_load(const char* path, int32_t* count) {
+    if (path == nullptr) return -1;
+    return cache_load(path, count);
+}
+
+int sgemm_tune_cache_save(const char* path, int32_t* count) {
+    if (path == nullptr) return -1;
+    return cache_save(path, count);
+}
+
+int sgemm_tune_forget(void) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    const int n = (int)g_tuned.size();
+    g_tuned.clear();
+    return n;
 }
 
 int sgemm_trace_begin(int64_t capacity) {
@@ -809,6 +937,7 @@ const char* sgemm_status_string(int status) {
         case SGEMM_ERR_TOO_LARGE: return "a dimension exceeds 2^30 or the grid 2^32-1 work-items";
         case SGEMM_ERR_ALLOC: return "a device allocation failed";
         case SGEMM_ERR_BUDGET: return "no plan fits the device memory budget";
+        case SGEMM_ERR_IO: return "the tuning cache file could not be read or written";
         default: break;
     }
     if (status >= SGEMM_ERR_HIP_BASE) return hipGetErrorString((hipError_t)(status - SGEMM_ERR_HIP_BASE));

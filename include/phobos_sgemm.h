@@ -55,6 +55,8 @@ extern "C" {
                                    /* grid exceeds 2^32-1 work-items           */
 #define SGEMM_ERR_ALLOC 4          /* a device allocation failed               */
 #define SGEMM_ERR_BUDGET 5         /* no plan fits the device memory budget    */
+#define SGEMM_ERR_IO 6             /* the tuning cache file could not be read  */
+                                   /* or written                               */
 #define SGEMM_ERR_HIP_BASE 1000    /* 1000 + hipError_t                        */
 
 /*
@@ -156,7 +158,9 @@ int sgemm_set_config(const sgemm_config* cfg);
  * the winner for this (M, N, K, lda, ldb, ldc) so that later sgemm calls of
  * that shape use it.  `reps` is the number of timed runs of each of the top
  * three in each round (>= 1; the pages' long probe).  `winner` (may be NULL)
- * receives the choice and `winner_ms` (may be NULL) its median time per call.  Synchronises
+ * receives the choice and `winner_ms` (may be NULL) its median time per call.
+ * With SGEMM_TUNE_CACHE set, the table is then saved to that file (see the
+ * tuning cache below; SGEMM_ERR_IO if the save fails).  Synchronises
  * `stream`.  Arguments: 1 M, 2 N, 3 K, 4 lda, 5 ldb, 6 ldc, 7 reps,
  * 8 stream, 9 winner, 10 winner_ms.
  */
@@ -164,6 +168,34 @@ int sgemm_tune_candidates(int64_t M, int64_t N, int64_t K, sgemm_config* out,
                           int32_t cap);
 int sgemm_tune(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
                int32_t reps, void* stream, sgemm_config* winner, float* winner_ms);
+
+/*
+ * Tuning cache: the tuner's table kept between processes (the pages' tuner
+ * keeps nothing; this is the library's own addition).  The file is text,
+ * one JSON object per line, e.g.
+ *   {"M": 4096, "N": 4096, "K": 4096, "lda": 4096, "ldb": 4096, "ldc": 4096,
+ *    "bm": 256, "bn": 256, "bk": 32, "wm": 2, "wn": 2}
+ * (on one line; keys in any order).  sgemm_tune_cache_load adds the file's
+ * entries to the in-process table, replacing entries of the same shape; a
+ * line that lacks a key, names a configuration that is not compiled or a
+ * shape that sgemm would reject is skipped.  `count` (may be NULL) receives
+ * the number of entries taken.  Returns SGEMM_OK, -1 for a NULL path, or
+ * SGEMM_ERR_IO if the file cannot be opened or read.
+ * sgemm_tune_cache_save writes the whole table to `path` through a
+ * temporary file in the same directory renamed into place; `count` (may be
+ * NULL) receives the number of entries written.  Returns SGEMM_OK, -1 for a
+ * NULL path, or SGEMM_ERR_IO on failure (the file is then unchanged).
+ * sgemm_tune_forget empties the in-process table (the file is untouched)
+ * and returns the number of entries removed; it cannot fail.
+ * Environment: with SGEMM_TUNE_CACHE=path the file, if it exists, is loaded
+ * before the process's first configuration choice, and the table is saved
+ * there after every successful sgemm_tune (which then returns SGEMM_ERR_IO
+ * if that save fails; the winner is recorded and reported all the same).
+ * Processes that share one file: the last save wins.  Host only; no GPU work.
+ */
+int sgemm_tune_cache_load(const char* path, int32_t* count);
+int sgemm_tune_cache_save(const char* path, int32_t* count);
+int sgemm_tune_forget(void);
 
 /*
  * Matrix-core variant ("Show HN: Phobos", section "Are we cuBLAS yet?", the

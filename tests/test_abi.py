@@ -27,7 +27,8 @@ def test_header_declares_the_entry_points():
                  "flash_attention_supertiled",
                  "sgemm_tune_candidates", "sgemm_set_config", "sgemm_get_config",
                  "sgemm_config_count", "sgemm_config_at", "sgemm_trace_begin",
-                 "sgemm_trace_end", "sgemm_status_string", "sgemm_version"):
+                 "sgemm_trace_end", "sgemm_status_string", "sgemm_version",
+                 "sgemm_tune_cache_load", "sgemm_tune_cache_save", "sgemm_tune_forget"):
         assert want in names
 
 

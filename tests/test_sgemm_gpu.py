@@ -219,6 +219,24 @@ def test_tuner_records_a_winner_that_is_correct():
     gu.check_full(w, x, gu.run(w, x))
 
 
+def test_tuner_saves_its_table_to_the_cache_file(tmp_path, monkeypatch):
+    """With SGEMM_TUNE_CACHE set, a tune leaves its winner in that file, and
+    loading the file into an emptied table restores the choice."""
+    path = tmp_path / "tune.jsonl"
+    monkeypatch.setenv("SGEMM_TUNE_CACHE", str(path))
+    M, N, K = 520, 600, 200
+    cfg, ms = g.sgemm_tune(M, N, K, K, N, N, reps=3)
+    assert ms > 0
+    lines = path.read_text().splitlines()
+    want = {"M": M, "N": N, "K": K, "lda": K, "ldb": N, "ldc": N, "bm": cfg.bm, "bn": cfg.bn,
+            "bk": cfg.bk, "wm": cfg.wm, "wn": cfg.wn}
+    assert any(all(f'"{k}": {v}' in line for k, v in want.items()) for line in lines), lines
+    g.sgemm_tune_forget()
+    assert g.sgemm_tune_cache_load(str(path)) == len(lines)
+    assert g.sgemm_get_config(M, N, K, K, N, N).as_tuple() == cfg.as_tuple()
+    g.sgemm_tune_forget()
+
+
 # ---------------------------------------------------------------------------
 # IEEE special values inside the logical A and B (not the pads)
 @pytest.mark.parametrize("special", [np.nan, np.inf])
