@@ -69,6 +69,15 @@ def check_full(w, x, out, steps=1, exact=False, relaxed=False, fmt=None):
     return ref
 
 
+def assert_well_inside(name, worst, limit=0.25):
+    """The bound 2Ku(...) is a worst case: the error of a correct fp32 path is
+    a random walk far inside it (a largest err/bound of order 1e-2 at these
+    sizes).  A ratio above a quarter of the bound marks a path that is wrong
+    yet still within it, e.g. one that drops or repeats a small term."""
+    print(f"{name}: max err/bound {worst:.3g}", flush=True)
+    assert worst < limit, f"{name}: max err/bound {worst:.3g}, expected well below {limit}"
+
+
 def check_pads(w, x, out):
     pads = wl.c_pad_mask(w)
     same = out[pads].view(np.int32) == x.C[pads].view(np.int32)

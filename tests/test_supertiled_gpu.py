@@ -78,12 +78,11 @@ def test_workload_supertiled_16384():
     w = wl.BY_NAME["supertiled_16384_t4096"]
     x = wl.make_inputs(w)
     st = gu.run(w, x)
-    worst = gu.check_sampled(w, x, st, count=3000)
-    print(f"supertiled 16384: sampled max err/bound {worst:.3g}", flush=True)
+    gu.assert_well_inside(w.name, gu.check_sampled(w, x, st, count=3000))
     gu.check_freivalds(w, x, st)
     gu.check_pads(w, x, st)
     mono = gu.run(w, x, entry="sgemm")
-    gu.check_sampled(w, x, mono, count=3000)
+    gu.assert_well_inside("monolithic_16384", gu.check_sampled(w, x, mono, count=3000))
     rows, cols = wl.sample_entries(w, 3000, seed=7)
     _, bnd = gu.oracle.sgemm_entries(w.M, w.N, w.K, w.alpha, x.A, x.B, w.beta, x.C, rows, cols)
     d = np.abs(gu.logical_c(w, st)[rows, cols].astype(np.float64)
