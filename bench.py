@@ -14,6 +14,9 @@ Printed: one JSON line with the metric (GFLOP/s = 2*M*N*K / time per step),
 the roofline of the dominant kernel (the step leaf; its duration per launch
 from HIP events the library records on the launch stream during the timed
 region) and the CPU oracle's rate on a bounded slab of the same product.
+The config also carries the device's own FP32 matrix peak (compute units x
+peak shader clock x 256 FLOP per clock per CU, from the HIP runtime) beside
+the published 157.3 TFLOP/s.
 
 Other options: --workload runs one of the other seeded workloads of
 sgemm_workloads.py instead (one step = one sgemm call); --tune runs the tile
@@ -33,6 +36,7 @@ known-size reference for the HBM byte counters); --skip-cpu-baseline leaves
 the oracle leg out.
 """
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -44,6 +48,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_FP32_MFMA_TFLOPS = 157.3     # MI355X published dense FP32 matrix peak
+FP32_MFMA_FLOP_PER_CLK_PER_CU = 256
+# hipDeviceAttribute_t values of the HIP runtime's header
+HIP_ATTR_CLOCK_RATE_KHZ = 5
+HIP_ATTR_MULTIPROCESSOR_COUNT = 63
 PEAK_HBM_GBS = 8000.0             # MI355X published HBM3E bandwidth
 PEAK_F16_MFMA_TFLOPS = 2500.0     # MI355X published dense fp16 / bf16 matrix peak
 DEFAULT_WORKLOAD = "supertiled_16384_t4096"
@@ -55,6 +63,25 @@ KERNEL_SOURCES = [os.path.join(ROOT, "fp32_gemm_02_amd", "csrc", f)
 def gflops(M, N, K, ms):
     """The pages' convention: 2*M*N*K floating-point operations per product."""
     return 2.0 * M * N * K / (ms * 1e-3) / 1e9
+
+
+def device_fp32_matrix_peak(device=0):
+    """The FP32 matrix peak of this device from its own figures: compute units
+    x peak shader clock x 256 FLOP per clock per CU, as the HIP runtime
+    reports them; None if it cannot be asked."""
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+    except OSError:
+        return None
+    vals = []
+    for attr in (HIP_ATTR_MULTIPROCESSOR_COUNT, HIP_ATTR_CLOCK_RATE_KHZ):
+        v = ctypes.c_int()
+        if hip.hipDeviceGetAttribute(ctypes.byref(v), ctypes.c_int(attr), ctypes.c_int(device)) != 0:
+            return None
+        vals.append(v.value)
+    cus, khz = vals
+    return {"cus": cus, "max_sclk_mhz": khz / 1e3,
+            "tflops": round(cus * khz * 1e3 * FP32_MFMA_FLOP_PER_CLK_PER_CU / 1e12, 2)}
 
 
 def kernel_source_hash():
@@ -343,6 +370,7 @@ def main():
     traffic = None if (host or tc is not None) else measured_traffic(args.workload)
     peak = PEAK_FP32_MFMA_TFLOPS if tc is None else PEAK_F16_MFMA_TFLOPS
 
+    dev_peak = device_fp32_matrix_peak() if tc is None else None
     out = {
         "metric": "SGEMM GFLOP/s and % of MI355X FP32 matrix peak at 16384^3, 1 GPU",
         "value": round(value, 1),
@@ -385,7 +413,11 @@ def main():
                        "inputs_rounded_to": args.tc,
                        "pct_of_f16_matrix_peak": round(100.0 * value / 1e3 / PEAK_F16_MFMA_TFLOPS, 2)}
                       if tc is not None else
-                      {"pct_of_fp32_matrix_peak": round(100.0 * value / 1e3 / PEAK_FP32_MFMA_TFLOPS, 2)})},
+                      {"pct_of_fp32_matrix_peak": round(100.0 * value / 1e3 / PEAK_FP32_MFMA_TFLOPS, 2),
+                       **({"device_fp32_matrix_peak": dev_peak,
+                           "pct_of_device_fp32_matrix_peak":
+                               round(100.0 * value / 1e3 / dev_peak["tflops"], 2)}
+                          if dev_peak else {})})},
         "roofline": {"bound": "mfma", "achieved": round(achieved_tflops, 2),
                      "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved_tflops / peak, 4),
