@@ -9,12 +9,16 @@ step leaves of 4096^3 each (64 GEMM launches per step).  Inputs are seeded
 synthetic uniform[-1, 1) matrices (the oracle's generators), resident in HBM
 before the timed region.  C keeps accumulating across steps (beta = 1); that
 changes no timing and the result is checked separately by the GPU tests.
+--warmup W runs exactly W untimed steps first; without it, untimed steps run
+until at least 2 have run and at least 0.2 s has passed (the count is reported).
 
 Printed: one JSON line with the metric (GFLOP/s = 2*M*N*K / time per step),
 the roofline of the dominant kernel (the step leaf; its duration per launch
 from HIP events the library records on the launch stream during the timed
 region) and the CPU oracle's rate on a bounded slab of the same product.
-The config also carries the device's own FP32 matrix peak (compute units x
+The timed region records one more event after each step, so the config also
+gives each step's median, mean, standard deviation, min and max (ms), and the
+device with its HIP runtime; and the device's own FP32 matrix peak (compute units x
 peak shader clock x 256 FLOP per clock per CU, from the HIP runtime) beside
 the published 157.3 TFLOP/s.
 
@@ -82,6 +86,63 @@ def device_fp32_matrix_peak(device=0):
     cus, khz = vals
     return {"cus": cus, "max_sclk_mhz": khz / 1e3,
             "tflops": round(cus * khz * 1e3 * FP32_MFMA_FLOP_PER_CLK_PER_CU / 1e12, 2)}
+
+
+MIN_WARMUP_S = 0.2
+
+
+def warm_up(step, warmup, stream):
+    """Untimed steps before the timed region: exactly `warmup` when it is
+    given; otherwise at least 2 steps and at least MIN_WARMUP_S seconds of them
+    (each waited for), since the shader clock rises over tens of ms of load
+    and short steps timed after a few calls measure up to 12% slow.
+    Returns the number of steps run."""
+    if warmup is not None:
+        for _ in range(warmup):
+            step()
+        stream.synchronize()
+        return warmup
+    n, t0 = 0, time.perf_counter()
+    while n < 2 or (time.perf_counter() - t0 < MIN_WARMUP_S and n < 100000):
+        step()
+        stream.synchronize()
+        n += 1
+    return n
+
+
+def timed_steps(step, steps, stream):
+    """Run `steps` steps between HIP events on `stream`, one more event after
+    each step (recording events adds no work to the timed region).  Returns
+    the total on the stream, each step's time (ms) and the host wall time (s)."""
+    import torch
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    evs[0].record(stream)
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step()
+        evs[i + 1].record(stream)
+    stream.synchronize()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_step = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+    return evs[0].elapsed_time(evs[-1]), per_step, wall
+
+
+def step_stats(per_step):
+    """Median, mean, standard deviation, min and max of the per-step times (ms)."""
+    import numpy as np
+    v = np.asarray(per_step, dtype=np.float64)
+    return {"median": round(float(np.median(v)), 4), "mean": round(float(v.mean()), 4),
+            "std": round(float(v.std(ddof=1)) if v.size > 1 else 0.0, 4),
+            "min": round(float(v.min()), 4), "max": round(float(v.max()), 4)}
+
+
+def device_info(device=0):
+    import torch
+    props = torch.cuda.get_device_properties(device)
+    return {"name": props.name, "arch": props.gcnArchName, "cus": props.multi_processor_count,
+            "hip_runtime": torch.version.hip}
 
 
 def kernel_source_hash():
@@ -196,19 +257,9 @@ def main_attention(args):
         g.flash_attention_supertiled(w.Nq, w.Nk, w.D, dQ, w.ldq, dK, w.ldk, dV, w.ldv, dO, w.ldo,
                                      w.scale, w.BR, stream=stream)
 
-    for _ in range(args.warmup):
-        step()
-    stream.synchronize()
+    args.warmup = warm_up(step, args.warmup, stream)
     g.sgemm_trace_begin(args.steps + 16)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    stream.synchronize()
-    ms_total = e0.elapsed_time(e1)
+    ms_total, per_step, _ = timed_steps(step, args.steps, stream)
     ms_kern, kinds, n = g.sgemm_trace_end(cap=args.steps + 16)
     launch_ms = float(np.mean([t for t, k in zip(ms_kern, kinds) if k == g.SGEMM_KIND_ATTENTION]))
     ms_per_step = ms_total / args.steps
@@ -232,7 +283,8 @@ def main_attention(args):
                    "Nk": w.Nk, "D": w.D, "scale": w.scale, "BR": w.BR,
                    "inputs": "Q/K/V %s/%s/%s, seed %d" % (*w.dists, w.seed),
                    "launches_per_step": 1,
-                   "pct_of_fp32_matrix_peak": round(100.0 * value / 1e3 / PEAK_FP32_MFMA_TFLOPS, 2)},
+                   "pct_of_fp32_matrix_peak": round(100.0 * value / 1e3 / PEAK_FP32_MFMA_TFLOPS, 2),
+                   "step_ms": step_stats(per_step), "device": device_info()},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_FP32_MFMA_TFLOPS, 4), "traffic": None},
@@ -248,7 +300,8 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps first (default: at least 2 and at least 0.2 s)")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--tune", action="store_true")
     ap.add_argument("--host-resident", type=int, default=None, metavar="MIB")
@@ -334,9 +387,7 @@ def main():
     if args.tune and tc is None:
         tuned, _ = g.sgemm_tune(*step_shape, w.lda, w.ldb, w.ldc, reps=10, stream=stream)
 
-    for _ in range(args.warmup):
-        step()
-    stream.synchronize()
+    args.warmup = warm_up(step, args.warmup, stream)
 
     if supertiled:
         launches_per_step = (-(-w.M // tiles[0])) * (-(-w.N // tiles[1])) * (-(-w.K // tiles[2]))
@@ -345,18 +396,7 @@ def main():
     else:
         launches_per_step = 1
     g.sgemm_trace_begin(args.steps * launches_per_step * 2 + 16)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    stream.synchronize()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_total = e0.elapsed_time(e1)
+    ms_total, per_step, wall = timed_steps(step, args.steps, stream)
     ms_kern, kinds, n = g.sgemm_trace_end(cap=args.steps * launches_per_step * 2 + 16)
     ms_per_step = ms_total / args.steps
     value = gflops(w.M, w.N, w.K, ms_per_step)
@@ -407,6 +447,8 @@ def main():
                        "bm=%d bn=%d bk=%d wm=%d wn=%d" %
                        g.sgemm_get_config(*step_shape, w.lda, w.ldb, w.ldc).as_tuple()),
                    "tuned": tuned is not None,
+                   "step_ms": step_stats(per_step),
+                   "device": device_info(),
                    "launches_per_step": launches_per_step,
                    **({"cast_pass_ms": round(float(np.mean(cast_ms)), 4) if cast_ms else 0.0,
                        "gemm_ms": round(avg_launch_ms, 4),
