@@ -236,3 +236,17 @@ def test_attention_argument_checks(args, want):
 def test_attention_supertile_rows_checked():
     assert g.flash_attention_supertiled_raw(4, 4, 64, 8, 64, 8, 64, 8, 64, 8, 64, 0.1, 0,
                                             stream=0) == -13
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """No CPU fallback: without the built library every entry point raises."""
+    monkeypatch.setattr(g, "LIB_PATH", str(tmp_path / "libphobos_sgemm.so"))
+    monkeypatch.setattr(g, "_lib", None)
+    for call in (lambda: g.sgemm(4, 4, 4, 1.0, 0, 4, 0, 4, 0.0, 0, 4, stream=0),
+                 lambda: g.sgemm_supertiled(4, 4, 4, 1.0, 0, 4, 0, 4, 0.0, 0, 4, 2, 2, 2,
+                                            stream=0),
+                 lambda: g.flash_attention(4, 4, 64, 0, 64, 0, 64, 0, 64, 0, 64, 1.0, stream=0),
+                 lambda: g.sgemm_tc(4, 4, 4, 1.0, 0, 4, 0, 4, 0.0, 0, 4, stream=0),
+                 g.version):
+        with pytest.raises(RuntimeError, match="not built"):
+            call()
