@@ -60,8 +60,11 @@ PEAK_HBM_GBS = 8000.0             # MI355X published HBM3E bandwidth
 PEAK_F16_MFMA_TFLOPS = 2500.0     # MI355X published dense fp16 / bf16 matrix peak
 DEFAULT_WORKLOAD = "supertiled_16384_t4096"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sgemm_step_4096_ld16384.txt")
+TC_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "tc16_gemm_f16_16384_counters.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "fp32_gemm_02_amd", "csrc", f)
                   for f in ("sgemm_kernels.hip", "sgemm_device.h")]
+TC_KERNEL_SOURCES = [os.path.join(ROOT, "fp32_gemm_02_amd", "csrc", f)
+                     for f in ("sgemm_tc.hip", "sgemm_device.h")]
 
 
 def gflops(M, N, K, ms):
@@ -145,23 +148,33 @@ def device_info(device=0):
             "hip_runtime": torch.version.hip}
 
 
-def kernel_source_hash():
+def kernel_source_hash(sources=None):
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in sources or KERNEL_SOURCES:
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload):
-    """HBM bytes per step-leaf launch from the committed counter summary, if it
-    was taken on the current kernel source for this workload; else None."""
-    if workload != DEFAULT_WORKLOAD or not os.path.exists(TRAFFIC_FILE):
+def measured_traffic(workload, tc=None):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, if it was taken on the current kernel source for this workload
+    (the fp32 step leaf of the default workload, or the fp16 GEMM of the
+    matrix-core variant); else None."""
+    if workload != DEFAULT_WORKLOAD:
         return None
-    text = open(TRAFFIC_FILE).read()
+    if tc is None:
+        path, sources = TRAFFIC_FILE, KERNEL_SOURCES
+    elif tc == "f16":
+        path, sources = TC_TRAFFIC_FILE, TC_KERNEL_SOURCES
+    else:
+        return None
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
     m_hash = re.search(r"^kernel_source_sha256_16:\s*(\S+)", text, re.M)
     m_bytes = re.search(r"^hbm_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
-    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash(sources):
         return None
     return float(m_bytes.group(1))
 
@@ -407,7 +420,7 @@ def main():
     avg_launch_ms = float(np.mean(step_ms))
     step_flops = 2.0 * step_shape[0] * step_shape[1] * step_shape[2]
     achieved_tflops = step_flops / (avg_launch_ms * 1e-3) / 1e12
-    traffic = None if (host or tc is not None) else measured_traffic(args.workload)
+    traffic = None if host else measured_traffic(args.workload, tc)
     peak = PEAK_FP32_MFMA_TFLOPS if tc is None else PEAK_F16_MFMA_TFLOPS
 
     dev_peak = device_fp32_matrix_peak() if tc is None else None
