@@ -7,6 +7,7 @@
 #include <unistd.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cerrno>
 #include <cmath>
 #include <cstdio>
@@ -180,7 +181,10 @@ int cache_save(const char* path, int32_t* count) {
         std::lock_guard<std::mutex> lk(g_mu);
         rows.assign(g_tuned.begin(), g_tuned.end());
     }
-    const std::string tmp = std::string(path) + ".tmp." + std::to_string((long long)getpid());
+    // a name of its own for every save of every process
+    static std::atomic<unsigned> serial{0};
+    const std::string tmp = std::string(path) + ".tmp." + std::to_string((long long)getpid()) +
+                            "." + std::to_string(serial.fetch_add(1));
     FILE* f = std::fopen(tmp.c_str(), "w");
     if (f == nullptr) return SGEMM_ERR_IO;
     bool ok = true;
