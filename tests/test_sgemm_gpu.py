@@ -318,3 +318,27 @@ def test_concurrent_calls_on_two_streams():
         torch.cuda.synchronize()
         steps = 1 if w.entry == "sgemm" else -(-w.K // w.TK)
         gu.check_full(w, x, dC3.cpu().numpy(), steps=steps, relaxed=True)
+
+
+@pytest.mark.parametrize("cfg", [None, (64, 64, 16, 1, 1)], ids=["default", "64x64"])
+@pytest.mark.parametrize("a_val,b_val", [(2.0 ** -140, 1.0), (2.0 ** -70, 2.0 ** -70)],
+                         ids=["subnormal_input", "subnormal_product"])
+def test_subnormals_are_kept(cfg, a_val, b_val):
+    """fp32 subnormals, given as inputs or produced by a product of normal
+    values, come out exactly (2^-140 here) rather than flushed to zero, so the
+    result equals the oracle's correctly rounded one."""
+    M, N, K = 300, 300, 64
+    A = np.zeros((M, K), np.float32)
+    B = np.zeros((K, N), np.float32)
+    idx = np.arange(K)
+    A[idx, idx] = a_val
+    B[idx, idx] = b_val
+    C = np.full((M, N), np.nan, np.float32)
+    dA, dB, dC = gu.to_dev(A), gu.to_dev(B), gu.to_dev(C)
+    with _forced(cfg):                  # None: the built-in choice
+        g.sgemm(M, N, K, 1.0, dA, K, dB, N, 0.0, dC, N)
+        torch.cuda.synchronize()
+    out = dC.cpu().numpy()
+    ref, _ = gu.oracle.sgemm(M, N, K, 1.0, A, B, 0.0, np.zeros((M, N), np.float32))
+    assert np.array_equal(out, ref)
+    assert out[5, 5] == np.float32(2.0 ** -140) and out[5, 5] != 0
