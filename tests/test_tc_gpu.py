@@ -194,3 +194,38 @@ def test_tc_16384(fmt):
     print(f"tc fmt {fmt} 16384: sampled max err/bound {worst:.3g}", flush=True)
     gu.check_freivalds(w, x, out, fmt=fmt)
     gu.check_pads(w, x, out)
+
+
+_T24, _T133 = 2.0 ** -24, 2.0 ** -133
+SUBNORMALS = {
+    g.SGEMM_TC_F16: [_T24, 1.5 * _T24, 2.5 * _T24, 2.0 ** -25, 0.75 * _T24, 2.0 ** -14 - _T24,
+                     3.3e-6, -1.5 * _T24, 2.0 ** -14, 0.4 * _T24, 1023.5 * _T24, 6.1e-5],
+    g.SGEMM_TC_BF16: [_T133, 1.5 * _T133, 2.5 * _T133, 2.0 ** -134, 2.0 ** -126 - _T133, 1.3e-39,
+                      -3.7e-40, 2.0 ** -126, 9.1e-39, 0.4 * _T133, 5e-41, 1e-45],
+}
+
+
+@pytest.mark.parametrize("form", FORMS + [STAGED64], ids=FORM_IDS + ["staged_k64_ring5"])
+@pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)
+def test_subnormals_of_the_format_round_as_the_oracle(fmt, form):
+    """Values in the 16-bit format's subnormal range, ties between its
+    subnormals, and values that round to zero or to the smallest normal, on
+    A's diagonal with B the identity: C's diagonal is each value as the
+    format rounds it, the oracle's bits exactly, in every form."""
+    M, N, K = 300, 300, 64
+    vals = SUBNORMALS[fmt]
+    A = np.zeros((M, K), np.float32)
+    B = np.zeros((K, N), np.float32)
+    for i in range(K):
+        A[i, i] = np.float32(vals[i % len(vals)])
+        B[i, i] = 1.0
+    g.sgemm_tc_set_config(fmt, form)
+    dA, dB = torch.from_numpy(A).to(gu.device()), torch.from_numpy(B).to(gu.device())
+    dC = torch.full((M, N), float("nan"), device=gu.device())
+    g.sgemm_tc(M, N, K, 1.0, dA, K, dB, N, 0.0, dC, N, fmt=fmt)
+    torch.cuda.synchronize()
+    out = dC.cpu().numpy()
+    ref, _ = oracle.sgemm(M, N, K, 1.0, A, B, 0.0, None, fmt=fmt)
+    bad = np.argwhere(out.view(np.uint32) != ref.view(np.uint32))
+    assert bad.size == 0, f"{len(bad)} elements differ, first {bad[:5].tolist()}"
+    assert np.count_nonzero(np.diagonal(out)[:K]) > K // 2   # not everything flushed
