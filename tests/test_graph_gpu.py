@@ -7,8 +7,9 @@ eagerly (which also leaves the library's lazy state initialised), is captured
 into a graph on the capturing stream, and is replayed three times with eager
 work (a reset of the output) and a synchronisation between replays.  Every
 replay must equal the eager result bit for bit, and the result the oracle.
-The matrix-core variant is not covered: its staged form takes a workspace
-from a stream-ordered pool."""
+The matrix-core variant's staged form takes its workspace from a
+stream-ordered pool: captured, the allocation and the free become nodes of
+the graph, and the replays must still equal the eager call."""
 import numpy as np
 import pytest
 import torch
@@ -97,3 +98,20 @@ def test_attention_graph_replays_equal_eager(BR):
     ref, bnd = oracle.attention(Nq, Nk, D, Q, K, V, scale)
     err = np.abs(eager.view(np.float32).reshape(Nq, D).astype(np.float64) - ref)
     assert np.all(err <= bnd)
+
+
+@pytest.mark.parametrize("fmt", [g.SGEMM_TC_F16, g.SGEMM_TC_BF16], ids=["f16", "bf16"])
+def test_tc_staged_graph_replays_equal_eager(fmt):
+    M = N = K = 2048                      # large enough for the staged form
+    assert g.sgemm_tc_get_config(fmt, M, N, K).staged == 1
+    w = wl.custom(M, N, K, 1.0, 0.5, seed=73)
+    x = wl.make_inputs(w)
+    dA, dB, dC0 = gu.to_dev(x.A), gu.to_dev(x.B), gu.to_dev(x.C)
+    dC = dC0.clone()
+    print(f"graph sgemm_tc fmt {fmt}", flush=True)
+
+    def call(C):
+        g.sgemm_tc(M, N, K, w.alpha, dA, w.lda, dB, w.ldb, w.beta, C, w.ldc, fmt=fmt)
+
+    eager = _capture_and_replay(call, dC, dC0)
+    gu.check_sampled(w, x, eager.view(np.float32), count=2000, fmt=fmt)
