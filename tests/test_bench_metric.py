@@ -22,3 +22,49 @@ def test_bench_refuses_more_than_one_gpu():
     p = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=60)
     assert p.returncode == 2 and "one GPU" in p.stderr
+
+
+def test_step_stats():
+    s = bench.step_stats([3.0, 1.0, 2.0, 4.0])
+    assert s == {"median": 2.5, "mean": 2.5, "std": round(float((5 / 3) ** 0.5), 4), "min": 1.0,
+                 "max": 4.0}
+    assert bench.step_stats([7.0])["std"] == 0.0
+
+
+class _Stream:
+    def __init__(self):
+        self.syncs = 0
+
+    def synchronize(self):
+        self.syncs += 1
+
+
+def test_warm_up_runs_exactly_w_steps_when_given():
+    n = []
+    s = _Stream()
+    assert bench.warm_up(lambda: n.append(1), 3, s) == 3
+    assert len(n) == 3 and s.syncs == 1
+    assert bench.warm_up(lambda: n.append(1), 0, s) == 0
+
+
+def test_warm_up_default_runs_two_steps_and_the_minimum_time():
+    import time
+    n = []
+    t0 = time.perf_counter()
+    ran = bench.warm_up(lambda: (n.append(1), time.sleep(0.001)), None, _Stream())
+    assert ran == len(n) >= 2
+    assert time.perf_counter() - t0 >= bench.MIN_WARMUP_S
+    slow = []
+    assert bench.warm_up(lambda: (slow.append(1), time.sleep(0.15)), None, _Stream()) == 2
+
+
+def test_traffic_only_for_the_counted_kernel_source(tmp_path, monkeypatch):
+    f = tmp_path / "traffic.txt"
+    f.write_text("hbm_bytes_per_launch: 1234\nkernel_source_sha256_16: %s\n"
+                 % bench.kernel_source_hash())
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
+    assert bench.measured_traffic(bench.DEFAULT_WORKLOAD) == 1234.0
+    assert bench.measured_traffic("sgemm_256") is None
+    assert bench.measured_traffic(bench.DEFAULT_WORKLOAD, "bf16") is None
+    f.write_text("hbm_bytes_per_launch: 1234\nkernel_source_sha256_16: 0000000000000000\n")
+    assert bench.measured_traffic(bench.DEFAULT_WORKLOAD) is None
