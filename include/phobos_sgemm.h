@@ -218,9 +218,12 @@ int sgemm_tune_forget(void);
  * conversion.  The workspace, (ceil256(M) + ceil256(N)) * ceil64(K) * 2
  * bytes, comes from a stream-ordered memory pool of the library's own on
  * the current device (allocated and freed on `stream`; the pool keeps freed
- * memory for later calls); when it cannot be allocated the fused form runs
- * instead.  Large products (M, N >= 2048 and K >= 1024) take the staged form
- * by default.
+ * memory for later calls); when it cannot be allocated, or when a tile's
+ * 256 rows of it would span more than 4 GiB (the 16-bit GEMM addresses them
+ * with 32-bit byte offsets), the fused form runs instead.  Under stream
+ * capture the workspace's allocation and free become nodes of the graph.
+ * Large products (M, N >= 2048 and K >= 1024) take the staged form by
+ * default.
  *
  * Accuracy: within 2*K*2^-24 * (|alpha| sum_k |A'[i][k]| |B'[k][j]| +
  * |beta C[i][j]|) of the exact value of the expression above.  Against the
