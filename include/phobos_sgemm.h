@@ -129,7 +129,11 @@ int sgemm_init_leaf(int64_t M, int64_t N, float beta, float* C, int64_t ldc,
  * `cfg` names no compiled configuration.  Order of precedence: a config set
  * here, then the environment variable SGEMM_FORCE_CFG="BMxBNxBKxWMxWN" (read
  * once per process; ignored with a message on stderr when malformed or not
- * compiled), then a tuned config for the exact shape, then the default.
+ * compiled), then a tuned config for the exact shape, then the default: the
+ * largest of 256x256, 256x128, 128x128, 128x64 and 64x64 tiles whose count
+ * reaches the chip's 256 CUs, unless that count leaves more than a quarter
+ * of its last wave idle, in which case the tile with the least estimated
+ * time (waves x tile area / the tile's relative rate) is used.
  */
 int sgemm_config_count(void);
 int sgemm_config_at(int32_t index, sgemm_config* out);
