@@ -386,34 +386,44 @@ __global__ __launch_bounds__(256) void tc_cast_rows_kernel(const float* A, int64
 }
 
 // B16[n][k] = round(B[k][n]) for k < K, n < N, 0 elsewhere in Np x Kp: a
-// 64 x 64 transpose through LDS per workgroup step (reads along n, writes
-// along k, both 16 bytes per lane).
+// 64 (k) x 128 (n) transpose through LDS per workgroup step, tiles taken n
+// first.  Reads take 512 contiguous bytes of a row of B, writes 128 bytes of
+// a row of B16, both 16 bytes per lane.  (64 x 64 tiles ran 12% slower at
+// 16384 x 16384; taller tiles or banded tile orders did not help either.)
+// The tile sits in LDS unpadded, as 16-byte pieces; piece q of row r is kept
+// at q ^ 2*((r >> 3) & 7).  A row is stored with one 16-byte write per lane,
+// each 16 lanes filling the 16 pieces of a 256-byte window; in a column read
+// (8 rows o..o+7 of one n per lane, o a multiple of 8, 8 n per wave) the 8
+// row groups take 8 different even offsets, so the wave's 64 lanes read 64
+// different 4-byte words modulo 256 bytes.
 template <int FMT, bool VEC>
 __global__ __launch_bounds__(256) void tc_cast_cols_kernel(const float* B, int64_t ldb, int K,
                                                            int N, uint16_t* out, int Np, int Kp) {
     using F = TcFmt<FMT>;
-    __shared__ float t[64][65];
-    const int tn = Np / 64, tk = Kp / 64;
+    constexpr int TK = 64, TN = 128;
+    constexpr int LPR = TN / 4, RPP = 256 / LPR, UPR = TK / 8;   // lanes per row, rows per pass
+    static_assert(kTcPadMN % TN == 0 && kTcPadK % TK == 0, "whole tiles of the padded B16");
+    __shared__ f32x4 t[TK][TN / 4];
+    const float* tf = reinterpret_cast<const float*>(&t[0][0]);
+    auto piece = [](int r, int q) { return q ^ (2 * ((r >> 3) & 7)); };
+    auto at = [&](int r, int n) { return tf[r * TN + 4 * piece(r, n >> 2) + (n & 3)]; };
+    const int tn = Np / TN, tk = Kp / TK;
     const int64_t tiles = (int64_t)tn * tk;
     for (int64_t b = blockIdx.x; b < tiles; b += gridDim.x) {
-        const int n0 = (int)(b % tn) * 64, k0 = (int)(b / tn) * 64;
+        const int n0 = (int)(b % tn) * TN, k0 = (int)(b / tn) * TK;
 #pragma unroll
-        for (int pass = 0; pass < 4; ++pass) {
-            const int kr = 16 * pass + (int)threadIdx.x / 16, c = 4 * ((int)threadIdx.x % 16);
-            const int k = k0 + kr, n = n0 + c;
-            const f32x4 v = (k < K) ? load4<VEC>(B + (int64_t)k * ldb + n, N - n)
-                                    : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-            t[kr][c] = v[0];
-            t[kr][c + 1] = v[1];
-            t[kr][c + 2] = v[2];
-            t[kr][c + 3] = v[3];
+        for (int pass = 0; pass < TK / RPP; ++pass) {
+            const int kr = RPP * pass + (int)threadIdx.x / LPR, q = (int)threadIdx.x % LPR;
+            const int k = k0 + kr, n = n0 + 4 * q;
+            t[kr][piece(kr, q)] = (k < K) ? load4<VEC>(B + (int64_t)k * ldb + n, N - n)
+                                          : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         }
         __syncthreads();
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int u = (int)threadIdx.x + 256 * j, n = u / 8, o = 8 * (u % 8);
-            const u32x4 v = {F::pack(t[o][n], t[o + 1][n]), F::pack(t[o + 2][n], t[o + 3][n]),
-                             F::pack(t[o + 4][n], t[o + 5][n]), F::pack(t[o + 6][n], t[o + 7][n])};
+        for (int j = 0; j < TN * UPR / 256; ++j) {
+            const int u = (int)threadIdx.x + 256 * j, n = u / UPR, o = 8 * (u % UPR);
+            const u32x4 v = {F::pack(at(o, n), at(o + 1, n)), F::pack(at(o + 2, n), at(o + 3, n)),
+                             F::pack(at(o + 4, n), at(o + 5, n)), F::pack(at(o + 6, n), at(o + 7, n))};
             *reinterpret_cast<u32x4*>(out + (int64_t)(n0 + n) * Kp + k0 + o) = v;
         }
         __syncthreads();
@@ -770,7 +780,7 @@ hipError_t launch_tc_cast(int fmt, const float* A, int64_t lda, bool vec_a, cons
                           uint16_t* B16, int Mp, int Np, int Kp, hipStream_t stream) {
     const int64_t units = (int64_t)Mp * (Kp / 8);
     const unsigned ga = (unsigned)std::min<int64_t>((units + 255) / 256, 1 << 20);
-    const int64_t tiles = (int64_t)(Np / 64) * (Kp / 64);
+    const int64_t tiles = (int64_t)(Np / 128) * (Kp / 64);
     const unsigned gb = (unsigned)std::min<int64_t>(tiles, 1 << 20);
 #define PHOBOS_CAST(F)                                                                         \
     do {                                                                                       \
