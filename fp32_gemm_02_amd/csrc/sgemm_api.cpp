@@ -92,15 +92,17 @@ int default_entry(int64_t M, int64_t N, int64_t K) {
         {128, 64, 16, 2, 1, 0.75},  {64, 64, 16, 1, 1, 0.50},
     };
     constexpr int kPicks = (int)(sizeof(order) / sizeof(order[0]));
-    (void)K;
     const int64_t slots = 256;   // one workgroup per CU for the large tiles
     auto tiles = [&](const Pick& p) { return ((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn); };
     int first = -1;
     for (int i = 0; i < kPicks && first < 0; ++i)
         if (tiles(order[i]) >= slots) first = i;
     if (first < 0) {
-        if (M <= 32 && N <= 32) return find_entry({32, 32, 16, 1, 1});
-        return find_entry({64, 64, 16, 1, 1});
+        // Too few 64x64 tiles to fill the chip: single-wave 32x32 tiles give
+        // four times the workgroups, each with a quarter of the MFMA work on
+        // its SIMD, and 32-deep chunks halve each one's chain of chunk loads
+        // (256^3: 10.2 us against 22.5 us with 64x64x16).
+        return find_entry({32, 32, K > 16 ? 32 : 16, 1, 1});
     }
     const int64_t t0 = tiles(order[first]), w0 = (t0 + slots - 1) / slots;
     int pick = first;

@@ -557,6 +557,8 @@ const KernelEntry* kernel_table(int* count) {
         PHOBOS_CFG(64, 128, 16, 1, 2),
         PHOBOS_CFG(64, 64, 16, 1, 1),
         PHOBOS_CFG(32, 32, 16, 1, 1),
+        PHOBOS_CFG(64, 64, 32, 1, 1),
+        PHOBOS_CFG(32, 32, 32, 1, 1),
     };
     *count = (int)(sizeof(table) / sizeof(table[0]));
     return table;
