@@ -8,6 +8,13 @@ torch.cuda.Stream, an integer hipStream_t or None (torch's current stream on
 the current device).  A non-zero status raises SgemmError, except in the
 ``raw`` entry points, which return it.
 
+Tensors are checked before the call: device operands must be float32,
+contiguous tensors on the current GPU that hold the whole matrix their
+shape and leading dimension span (host operands of sgemm_supertiled_host:
+float32 host arrays or tensors of that size); anything else raises
+ValueError before the library is called.  Integer addresses are passed on
+unchecked.
+
 The library is loaded from this directory.  There is no fallback: if it has
 not been built (python -m fp32_gemm_02_amd.build), importing works but the
 first call raises.
@@ -120,10 +127,12 @@ _SIGNATURES = {
     "sgemm_supertiled_host": ([_i64, _i64, _i64, _f32, _vp, _i64, _vp, _i64, _f32, _vp, _i64,
                                ctypes.POINTER(sgemm_plan), _vp], ctypes.c_int),
     "sgemm_trace_begin": ([_i64], ctypes.c_int),
+    "sgemm_trace_begin_sampled": ([_i64, _i64], ctypes.c_int),
     "sgemm_trace_end": ([ctypes.POINTER(_f32), ctypes.POINTER(_i32), _i64,
                          ctypes.POINTER(_i64)], ctypes.c_int),
     "sgemm_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "sgemm_version": ([], ctypes.c_int),
+    "sgemm_set_log": ([_i32], ctypes.c_int),
 }
 
 
@@ -150,6 +159,63 @@ def _ptr(x):
     return int(x)
 
 
+def _need(rows, cols, ld):
+    """Floats a row-major rows x cols matrix with leading dimension ld spans."""
+    return (rows - 1) * ld + cols if rows > 0 and cols > 0 else 0
+
+
+def _dev_shape(x, rows, cols, ld, name, where):
+    """ValueError unless the tensor x is float32, contiguous and holds at least
+    (rows-1)*ld + cols elements from its first one (integers pass)."""
+    if x is None or not hasattr(x, "data_ptr"):
+        return
+    import torch
+    if x.dtype != torch.float32:
+        raise ValueError(f"{where}: {name} must be a float32 tensor, got {x.dtype}")
+    need = _need(rows, cols, ld)
+    if need:
+        if not x.is_contiguous():
+            raise ValueError(f"{where}: {name} must be contiguous (or pass its address)")
+        if x.numel() < need:
+            raise ValueError(f"{where}: {name} holds {x.numel()} floats, a {rows}x{cols} "
+                             f"matrix with leading dimension {ld} spans {need}")
+
+
+def _dev_addr(x, name, where):
+    """Address of a device operand: an integer (or None) as it is; a tensor
+    only if it lives on the current GPU (ValueError otherwise)."""
+    if x is None or not hasattr(x, "data_ptr"):
+        return _ptr(x)
+    import torch
+    if not x.is_cuda:
+        raise ValueError(f"{where}: {name} is on {x.device}, not on a GPU")
+    if x.device.index != torch.cuda.current_device():
+        raise ValueError(f"{where}: {name} is on {x.device}, the current device is "
+                         f"cuda:{torch.cuda.current_device()}")
+    return x.data_ptr()
+
+
+def _dev_ptrs(where, *ops):
+    """Checked addresses of device operands given as (x, rows, cols, ld, name):
+    every operand's dtype and extent first, then where each lives, so that
+    nothing reaches the library unless all of them pass."""
+    for x, rows, cols, ld, name in ops:
+        _dev_shape(x, rows, cols, ld, name, where)
+    return tuple(_dev_addr(x, name, where) for x, _, _, _, name in ops)
+
+
+def _dev(x, rows, cols, ld, name, where):
+    return _dev_ptrs(where, (x, rows, cols, ld, name))[0]
+
+
+def _gemm_ptrs(M, N, K, alpha, A, lda, B, ldb, C, ldc, where):
+    """Checked addresses of A, B and C for an M x N x K product (A and B are
+    only sized when the product reads them)."""
+    reads = M > 0 and N > 0 and K > 0 and alpha != 0
+    return _dev_ptrs(where, (A, M if reads else 0, K, lda, "A"),
+                     (B, K if reads else 0, N, ldb, "B"), (C, M if N > 0 else 0, N, ldc, "C"))
+
+
 def _stream(s):
     if s is None:
         import torch
@@ -172,9 +238,15 @@ def version():
     return lib().sgemm_version()
 
 
+def sgemm_set_log(on):
+    """Turn the library's dispatch log (one stderr line per decision) on or
+    off; returns whether it was on."""
+    return bool(lib().sgemm_set_log(1 if on else 0))
+
+
 def sgemm_raw(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None):
-    return lib().sgemm(M, N, K, alpha, _ptr(A), lda, _ptr(B), ldb, beta, _ptr(C), ldc,
-                       _stream(stream))
+    a, b, c = _gemm_ptrs(M, N, K, alpha, A, lda, B, ldb, C, ldc, "sgemm")
+    return lib().sgemm(M, N, K, alpha, a, lda, b, ldb, beta, c, ldc, _stream(stream))
 
 
 def sgemm(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None):
@@ -184,8 +256,9 @@ def sgemm(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None):
 
 def sgemm_supertiled_raw(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, TM, TN, TK,
                          stream=None):
-    return lib().sgemm_supertiled(M, N, K, alpha, _ptr(A), lda, _ptr(B), ldb, beta, _ptr(C),
-                                  ldc, TM, TN, TK, _stream(stream))
+    a, b, c = _gemm_ptrs(M, N, K, alpha, A, lda, B, ldb, C, ldc, "sgemm_supertiled")
+    return lib().sgemm_supertiled(M, N, K, alpha, a, lda, b, ldb, beta, c, ldc, TM, TN, TK,
+                                  _stream(stream))
 
 
 def sgemm_supertiled(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, TM, TN, TK, stream=None):
@@ -196,12 +269,13 @@ def sgemm_supertiled(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, TM, TN, TK, s
 
 def sgemm_init_leaf(M, N, beta, C, ldc, stream=None):
     """C <- beta*C (C <- 0 without reading C when beta == 0)."""
-    _check(lib().sgemm_init_leaf(M, N, beta, _ptr(C), ldc, _stream(stream)), "sgemm_init_leaf")
+    c = _dev(C, M if N > 0 else 0, N, ldc, "C", "sgemm_init_leaf")
+    _check(lib().sgemm_init_leaf(M, N, beta, c, ldc, _stream(stream)), "sgemm_init_leaf")
 
 
 def sgemm_tc_raw(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, fmt, stream=None):
-    return lib().sgemm_tc(M, N, K, alpha, _ptr(A), lda, _ptr(B), ldb, beta, _ptr(C), ldc, fmt,
-                          _stream(stream))
+    a, b, c = _gemm_ptrs(M, N, K, alpha, A, lda, B, ldb, C, ldc, "sgemm_tc")
+    return lib().sgemm_tc(M, N, K, alpha, a, lda, b, ldb, beta, c, ldc, fmt, _stream(stream))
 
 
 def sgemm_tc(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, fmt=None, stream=None):
@@ -236,9 +310,17 @@ def sgemm_tc_set_config(fmt, cfg):
            "sgemm_tc_set_config")
 
 
+def _attn_ptrs(Nq, Nk, D, Q, ldq, K, ldk, V, ldv, O, ldo, where):
+    rows = Nq if Nq > 0 else 0
+    keys = Nk if Nq > 0 else 0
+    return _dev_ptrs(where, (Q, rows, D, ldq, "Q"), (K, keys, D, ldk, "K"),
+                     (V, keys, D, ldv, "V"), (O, rows, D, ldo, "O"))
+
+
 def flash_attention_raw(Nq, Nk, D, Q, ldq, K, ldk, V, ldv, O, ldo, scale, stream=None):
-    return lib().flash_attention(Nq, Nk, D, _ptr(Q), ldq, _ptr(K), ldk, _ptr(V), ldv, _ptr(O),
-                                 ldo, scale, _stream(stream))
+    q, k, v, o = _attn_ptrs(Nq, Nk, D, Q, ldq, K, ldk, V, ldv, O, ldo, "flash_attention")
+    return lib().flash_attention(Nq, Nk, D, q, ldq, k, ldk, v, ldv, o, ldo, scale,
+                                 _stream(stream))
 
 
 def flash_attention(Nq, Nk, D, Q, ldq, K, ldk, V, ldv, O, ldo, scale, stream=None):
@@ -249,8 +331,10 @@ def flash_attention(Nq, Nk, D, Q, ldq, K, ldk, V, ldv, O, ldo, scale, stream=Non
 
 def flash_attention_supertiled_raw(Nq, Nk, D, Q, ldq, K, ldk, V, ldv, O, ldo, scale, BR,
                                    stream=None):
-    return lib().flash_attention_supertiled(Nq, Nk, D, _ptr(Q), ldq, _ptr(K), ldk, _ptr(V),
-                                            ldv, _ptr(O), ldo, scale, BR, _stream(stream))
+    q, k, v, o = _attn_ptrs(Nq, Nk, D, Q, ldq, K, ldk, V, ldv, O, ldo,
+                            "flash_attention_supertiled")
+    return lib().flash_attention_supertiled(Nq, Nk, D, q, ldq, k, ldk, v, ldv, o, ldo, scale, BR,
+                                            _stream(stream))
 
 
 def flash_attention_supertiled(Nq, Nk, D, Q, ldq, K, ldk, V, ldv, O, ldo, scale, BR,
@@ -336,21 +420,46 @@ def sgemm_plan_supertiles(M, N, K, beta, device_bytes, gemm_tflops=None, link_gb
     return plan
 
 
-def _host_ptr(x):
-    """Address of a host buffer (numpy array, CPU tensor or integer)."""
+def _host_ptr(x, rows=0, cols=0, ld=0, name="", where=""):
+    """Address of a host buffer (numpy array, CPU tensor or integer).  Arrays
+    and tensors must be float32, contiguous, in host memory and hold at least
+    (rows-1)*ld + cols elements; otherwise ValueError."""
     if x is None:
         return None
-    if hasattr(x, "ctypes"):
+    need = _need(rows, cols, ld)
+    if hasattr(x, "ctypes") and hasattr(x, "dtype"):
+        import numpy as np
+        if x.dtype != np.float32:
+            raise ValueError(f"{where}: {name} must be float32, got {x.dtype}")
+        if need and not x.flags.c_contiguous:
+            raise ValueError(f"{where}: {name} must be C-contiguous")
+        if x.size < need:
+            raise ValueError(f"{where}: {name} holds {x.size} floats, a {rows}x{cols} "
+                             f"matrix with leading dimension {ld} spans {need}")
         return x.ctypes.data
     if hasattr(x, "data_ptr"):
+        import torch
+        if x.dtype != torch.float32:
+            raise ValueError(f"{where}: {name} must be float32, got {x.dtype}")
+        if x.is_cuda:
+            raise ValueError(f"{where}: {name} must be in host memory, not on {x.device}")
+        if need and not x.is_contiguous():
+            raise ValueError(f"{where}: {name} must be contiguous")
+        if x.numel() < need:
+            raise ValueError(f"{where}: {name} holds {x.numel()} floats, a {rows}x{cols} "
+                             f"matrix with leading dimension {ld} spans {need}")
         return x.data_ptr()
     return int(x)
 
 
 def sgemm_supertiled_host_raw(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, plan, stream=None):
-    return lib().sgemm_supertiled_host(M, N, K, alpha, _host_ptr(A), lda, _host_ptr(B), ldb,
-                                       beta, _host_ptr(C), ldc,
-                                       None if plan is None else ctypes.byref(plan),
+    where = "sgemm_supertiled_host"
+    reads = M > 0 and N > 0 and K > 0 and alpha != 0
+    return lib().sgemm_supertiled_host(M, N, K, alpha,
+                                       _host_ptr(A, M if reads else 0, K, lda, "A", where), lda,
+                                       _host_ptr(B, K if reads else 0, N, ldb, "B", where), ldb,
+                                       beta, _host_ptr(C, M if N > 0 else 0, N, ldc, "C", where),
+                                       ldc, None if plan is None else ctypes.byref(plan),
                                        _stream(stream))
 
 
@@ -360,8 +469,9 @@ def sgemm_supertiled_host(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, plan, st
            "sgemm_supertiled_host")
 
 
-def sgemm_trace_begin(capacity):
-    _check(lib().sgemm_trace_begin(capacity), "sgemm_trace_begin")
+def sgemm_trace_begin(capacity, every=1):
+    """Bracket the next launches with HIP events (one in every `every`)."""
+    _check(lib().sgemm_trace_begin_sampled(capacity, every), "sgemm_trace_begin_sampled")
 
 
 def sgemm_trace_end(cap=1 << 16):
