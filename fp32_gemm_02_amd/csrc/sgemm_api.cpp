@@ -9,6 +9,7 @@
 #include <algorithm>
 #include <atomic>
 #include <cerrno>
+#include <cstdarg>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -68,11 +69,57 @@ struct TraceRec {
 };
 bool g_trace_on = false;
 int64_t g_trace_cap = 0;
+int64_t g_trace_every = 1;   // trace one launch in every g_trace_every
+int64_t g_trace_seen = 0;    // launches seen since the trace began
 std::vector<TraceRec> g_trace;
+// Mirrors g_trace_on so that an untraced launch does not take g_mu.
+std::atomic<bool> g_trace_flag{false};
 
 int env_int(const char* name, int dflt) {
     const char* v = std::getenv(name);
     return (v && *v) ? std::atoi(v) : dflt;
+}
+
+// Launch settings taken from the environment, read once per process:
+// SGEMM_GROUP_M (tile rows per raster group, default 4), SGEMM_XCD_REMAP
+// (0 turns the XCD-aware tile order off) and SGEMM_LOG (a non-empty value
+// other than "0" turns the dispatch log on).
+struct LaunchEnv {
+    int group_m;
+    bool xcd_remap;
+    bool log;
+};
+const LaunchEnv& launch_env() {
+    static const LaunchEnv e = [] {
+        LaunchEnv v{};
+        v.group_m = std::max(1, env_int("SGEMM_GROUP_M", 4));
+        v.xcd_remap = env_int("SGEMM_XCD_REMAP", 1) != 0;
+        const char* l = std::getenv("SGEMM_LOG");
+        v.log = l != nullptr && *l != '\0' && std::strcmp(l, "0") != 0;
+        return v;
+    }();
+    return e;
+}
+
+// Dispatch log: one line on stderr per decision (quick return, walk, launch).
+// Starts as SGEMM_LOG says; sgemm_set_log changes it at run time.
+std::atomic<int> g_log{-1};   // -1: not yet read from the environment
+bool log_on() {
+    int v = g_log.load(std::memory_order_relaxed);
+    if (v < 0) {
+        int want = launch_env().log ? 1 : 0;
+        g_log.compare_exchange_strong(v, want);
+        v = g_log.load(std::memory_order_relaxed);
+    }
+    return v > 0;
+}
+__attribute__((format(printf, 1, 2))) void log_line(const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    std::fprintf(stderr, "phobos_sgemm: %s\n", buf);
 }
 
 // Built-in choice when nothing is forced or tuned: the largest tile that still
@@ -246,19 +293,43 @@ void load_env_cache_once() {
     });
 }
 
-int choose_entry(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc) {
+// Where a configuration choice came from (for the dispatch log).
+enum ChoiceSource { kForced, kEnv, kTuned, kDefault };
+const char* source_name(ChoiceSource s) {
+    switch (s) {
+        case kForced: return "forced";
+        case kEnv: return "SGEMM_FORCE_CFG";
+        case kTuned: return "tuned";
+        default: return "default";
+    }
+}
+
+int choose_entry(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
+                 ChoiceSource* src = nullptr) {
     load_env_cache_once();
+    ChoiceSource dummy;
+    ChoiceSource& from = src ? *src : dummy;
     {
         std::lock_guard<std::mutex> lk(g_mu);
-        if (g_forced >= 0) return g_forced;
+        if (g_forced >= 0) {
+            from = kForced;
+            return g_forced;
+        }
     }
     const int env = env_forced_entry();
-    if (env >= 0) return env;
+    if (env >= 0) {
+        from = kEnv;
+        return env;
+    }
     {
         std::lock_guard<std::mutex> lk(g_mu);
         auto it = g_tuned.find(ShapeKey{M, N, K, lda, ldb, ldc});
-        if (it != g_tuned.end()) return it->second;
+        if (it != g_tuned.end()) {
+            from = kTuned;
+            return it->second;
+        }
     }
+    from = kDefault;
     return default_entry(M, N, K);
 }
 
@@ -267,8 +338,11 @@ struct TraceScope {
     hipStream_t s;
     int idx = -1;
     TraceScope(hipStream_t stream, int32_t kind) : s(stream) {
+        if (!g_trace_flag.load(std::memory_order_acquire)) return;
         std::lock_guard<std::mutex> lk(g_mu);
-        if (!g_trace_on || (int64_t)g_trace.size() >= g_trace_cap) return;
+        if (!g_trace_on) return;
+        if (g_trace_seen++ % g_trace_every != 0) return;
+        if ((int64_t)g_trace.size() >= g_trace_cap) return;
         TraceRec r{};
         if (hipEventCreate(&r.start) != hipSuccess) return;
         if (hipEventCreate(&r.stop) != hipSuccess) {
@@ -293,11 +367,22 @@ struct TraceScope {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+const char* kind_name(int32_t kind) {
+    switch (kind) {
+        case SGEMM_KIND_GEMM: return "gemm";
+        case SGEMM_KIND_INIT_LEAF: return "init_leaf";
+        case SGEMM_KIND_TC: return "tc_gemm";
+        case SGEMM_KIND_TC_CAST: return "tc_cast";
+        case SGEMM_KIND_ATTENTION: return "attention";
+        default: return "?";
+    }
+}
+
 // One launch of kernel entry `e` on already-validated arguments (M, N, K > 0,
-// alpha != 0), traced as `kind`.
+// alpha != 0), traced as `kind`; `why` names where the configuration came from.
 int launch_entry(const KernelEntry& e, int32_t kind, int64_t M, int64_t N, int64_t K,
                  float alpha, const float* A, int64_t lda, const float* B, int64_t ldb,
-                 float beta, float* C, int64_t ldc, hipStream_t stream) {
+                 float beta, float* C, int64_t ldc, hipStream_t stream, const char* why) {
     GemmArgs p{};
     p.M = (int32_t)M;
     p.N = (int32_t)N;
@@ -313,12 +398,21 @@ int launch_entry(const KernelEntry& e, int32_t kind, int64_t M, int64_t N, int64
     const int64_t tm = (M + e.cfg.bm - 1) / e.cfg.bm;
     const int64_t tn = (N + e.cfg.bn - 1) / e.cfg.bn;
     if (tm * tn * e.threads > kMaxGridItems) return SGEMM_ERR_TOO_LARGE;
+    const LaunchEnv& env = launch_env();
     p.tiles_m = (int32_t)tm;
     p.tiles_n = (int32_t)tn;
-    p.group_m = std::max(1, env_int("SGEMM_GROUP_M", 4));
-    p.xcd_remap = ((tm * tn) % 8 == 0 && env_int("SGEMM_XCD_REMAP", 1) != 0) ? 1 : 0;
+    p.group_m = env.group_m;
+    p.xcd_remap = ((tm * tn) % 8 == 0 && env.xcd_remap) ? 1 : 0;
     const bool vec = aligned16(A) && aligned16(B) && aligned16(C) && lda % 4 == 0 &&
                      ldb % 4 == 0 && ldc % 4 == 0;
+    if (log_on())
+        log_line("launch %s M=%lld N=%lld K=%lld lda=%lld ldb=%lld ldc=%lld alpha=%g beta=%g "
+                 "tile=%dx%dx%d waves=%dx%d (%s) loads=%s grid=%lld group_m=%d xcd_remap=%d "
+                 "stream=%p",
+                 kind_name(kind), (long long)M, (long long)N, (long long)K, (long long)lda,
+                 (long long)ldb, (long long)ldc, (double)alpha, (double)beta, e.cfg.bm, e.cfg.bn,
+                 e.cfg.bk, e.cfg.wm, e.cfg.wn, why, vec ? "vec4" : "scalar",
+                 (long long)(tm * tn), p.group_m, p.xcd_remap, (void*)stream);
     TraceScope ts(stream, kind);
     const hipError_t err = vec ? e.vec4(p, stream) : e.scalar(p, stream);
     return hip_status(err);
@@ -326,9 +420,9 @@ int launch_entry(const KernelEntry& e, int32_t kind, int64_t M, int64_t N, int64
 
 int launch_gemm(int entry, int64_t M, int64_t N, int64_t K, float alpha, const float* A,
                 int64_t lda, const float* B, int64_t ldb, float beta, float* C, int64_t ldc,
-                hipStream_t stream) {
+                hipStream_t stream, ChoiceSource src) {
     return launch_entry(kKernelTable[entry], SGEMM_KIND_GEMM, M, N, K, alpha, A, lda, B, ldb,
-                        beta, C, ldc, stream);
+                        beta, C, ldc, stream, source_name(src));
 }
 
 // ---- matrix-core variant: per input format, a fused table (rounding on
@@ -441,6 +535,12 @@ int launch_tc_staged(int32_t fmt, const phobos::Tc16Entry& e, int64_t M, int64_t
     uint16_t* A16 = static_cast<uint16_t*>(ws);
     uint16_t* B16 = A16 + Mp * Kp;
     int st;
+    if (log_on())
+        log_line("launch tc_cast M=%lld N=%lld K=%lld -> workspace %lldx%lld + %lldx%lld "
+                 "(%zu bytes) fmt=%s stream=%p",
+                 (long long)M, (long long)N, (long long)K, (long long)Mp, (long long)Kp,
+                 (long long)Np, (long long)Kp, bytes, fmt == SGEMM_TC_F16 ? "f16" : "bf16",
+                 (void*)stream);
     {
         TraceScope ts(stream, SGEMM_KIND_TC_CAST);
         const bool va = aligned16(A) && lda % 4 == 0, vb = aligned16(B) && ldb % 4 == 0;
@@ -463,8 +563,15 @@ int launch_tc_staged(int32_t fmt, const phobos::Tc16Entry& e, int64_t M, int64_t
         p.vec_c = aligned16(C) && ldc % 4 == 0;
         p.tiles_m = (int32_t)tm;
         p.tiles_n = (int32_t)tn;
-        p.group_m = std::max(1, env_int("SGEMM_GROUP_M", 4));
-        p.xcd_remap = ((tm * tn) % 8 == 0 && env_int("SGEMM_XCD_REMAP", 1) != 0) ? 1 : 0;
+        p.group_m = launch_env().group_m;
+        p.xcd_remap = ((tm * tn) % 8 == 0 && launch_env().xcd_remap) ? 1 : 0;
+        if (log_on())
+            log_line("launch tc_gemm M=%lld N=%lld K=%lld (padded to %lld) ldc=%lld alpha=%g "
+                     "beta=%g fmt=%s tile=%dx%dx%d waves=%dx%d staged grid=%lld stream=%p",
+                     (long long)M, (long long)N, (long long)K, (long long)Kp, (long long)ldc,
+                     (double)alpha, (double)beta, fmt == SGEMM_TC_F16 ? "f16" : "bf16",
+                     e.cfg.bm, e.cfg.bn, e.cfg.bk, e.cfg.wm, e.cfg.wn, (long long)(tm * tn),
+                     (void*)stream);
         TraceScope ts(stream, SGEMM_KIND_TC);
         st = hip_status(e.launch(p, stream));
     }
@@ -515,12 +622,28 @@ int launch_attn(int64_t Nq, int64_t Nk, const float* Q, int64_t ldq, const float
     if (((Nq + br - 1) / br) * p.blocks_per_tile * 256 > kMaxGridItems) return SGEMM_ERR_TOO_LARGE;
     const bool vec = aligned16(Q) && aligned16(K) && aligned16(V) && aligned16(O) &&
                      ldq % 4 == 0 && ldk % 4 == 0 && ldv % 4 == 0 && ldo % 4 == 0;
+    if (log_on())
+        log_line("launch attention Nq=%lld Nk=%lld D=64 ldq=%lld ldk=%lld ldv=%lld ldo=%lld "
+                 "scale=%g super-tile rows=%lld grid=%lld loads=%s stream=%p",
+                 (long long)Nq, (long long)Nk, (long long)ldq, (long long)ldk, (long long)ldv,
+                 (long long)ldo, (double)scale, (long long)br,
+                 (long long)(((Nq + br - 1) / br) * p.blocks_per_tile), vec ? "vec4" : "scalar",
+                 (void*)stream);
     TraceScope ts(stream, SGEMM_KIND_ATTENTION);
     return hip_status(phobos::launch_attention(p, vec, stream));
 }
 
 int launch_init(int64_t M, int64_t N, float beta, float* C, int64_t ldc, hipStream_t stream) {
-    if (beta == 1.0f) return SGEMM_OK;
+    if (beta == 1.0f) {
+        if (log_on())
+            log_line("init_leaf M=%lld N=%lld beta=1: identity, nothing enqueued", (long long)M,
+                     (long long)N);
+        return SGEMM_OK;
+    }
+    if (log_on())
+        log_line("launch init_leaf M=%lld N=%lld ldc=%lld beta=%g (%s) stream=%p", (long long)M,
+                 (long long)N, (long long)ldc, (double)beta,
+                 beta == 0.0f ? "C <- 0, C not read" : "C <- beta*C", (void*)stream);
     TraceScope ts(stream, SGEMM_KIND_INIT_LEAF);
     return hip_status(phobos::launch_init_leaf(M, N, beta, C, ldc, stream));
 }
@@ -551,9 +674,10 @@ namespace phobos {
 int host_launch_gemm(int64_t M, int64_t N, int64_t K, float alpha, const float* A,
                      int64_t lda, const float* B, int64_t ldb, float beta, float* C,
                      int64_t ldc, hipStream_t stream) {
-    const int entry = choose_entry(M, N, K, lda, ldb, ldc);
+    ChoiceSource src;
+    const int entry = choose_entry(M, N, K, lda, ldb, ldc, &src);
     if (entry < 0) return SGEMM_ERR_NO_CONFIG;
-    return launch_gemm(entry, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+    return launch_gemm(entry, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, src);
 }
 int host_launch_init(int64_t M, int64_t N, float beta, float* C, int64_t ldc,
                      hipStream_t stream) {
@@ -567,12 +691,21 @@ int sgemm(int64_t M, int64_t N, int64_t K, float alpha, const float* A, int64_t 
           const float* B, int64_t ldb, float beta, float* C, int64_t ldc, void* stream) {
     const int st = check_gemm_args(M, N, K, alpha, A, lda, B, ldb, C, ldc);
     if (st != SGEMM_OK) return st;
-    if (M == 0 || N == 0) return SGEMM_OK;
+    if (M == 0 || N == 0) {
+        if (log_on()) log_line("sgemm M=%lld N=%lld: empty, nothing enqueued", (long long)M, (long long)N);
+        return SGEMM_OK;
+    }
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    if (K == 0 || alpha == 0.0f) return launch_init(M, N, beta, C, ldc, s);
-    const int entry = choose_entry(M, N, K, lda, ldb, ldc);
+    if (K == 0 || alpha == 0.0f) {
+        if (log_on())
+            log_line("sgemm M=%lld N=%lld K=%lld alpha=%g: A and B not read, C <- beta*C",
+                     (long long)M, (long long)N, (long long)K, (double)alpha);
+        return launch_init(M, N, beta, C, ldc, s);
+    }
+    ChoiceSource src;
+    const int entry = choose_entry(M, N, K, lda, ldb, ldc, &src);
     if (entry < 0) return SGEMM_ERR_NO_CONFIG;
-    return launch_gemm(entry, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s);
+    return launch_gemm(entry, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s, src);
 }
 
 int sgemm_supertiled(int64_t M, int64_t N, int64_t K, float alpha, const float* A,
@@ -583,11 +716,23 @@ int sgemm_supertiled(int64_t M, int64_t N, int64_t K, float alpha, const float* 
     if (TM < 1) return -12;
     if (TN < 1) return -13;
     if (TK < 1) return -14;
-    if (M == 0 || N == 0) return SGEMM_OK;
+    if (M == 0 || N == 0) {
+        if (log_on())
+            log_line("sgemm_supertiled M=%lld N=%lld: empty, nothing enqueued", (long long)M,
+                     (long long)N);
+        return SGEMM_OK;
+    }
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const bool steps = K > 0 && alpha != 0.0f;
     const int64_t tm = std::min(TM, M), tn = std::min(TN, N), tk = std::min(TK, std::max<int64_t>(K, 1));
     const int64_t gm = (M + tm - 1) / tm, gn = (N + tn - 1) / tn, gk = steps ? (K + tk - 1) / tk : 0;
+    if (log_on())
+        log_line("sgemm_supertiled M=%lld N=%lld K=%lld super-tiles %lldx%lldx%lld: grid %lldx%lld, "
+                 "%lld K steps each (%s), %lld step launches",
+                 (long long)M, (long long)N, (long long)K, (long long)tm, (long long)tn,
+                 (long long)tk, (long long)gm, (long long)gn, (long long)gk,
+                 steps ? "init leaf then steps" : "A and B not read: init leaf only",
+                 (long long)(gm * gn * gk));
     for (int64_t pm = 0; pm < gm; ++pm) {
         const int64_t r0 = pm * tm, rows = std::min(tm, M - r0);
         for (int64_t pn = 0; pn < gn; ++pn) {
@@ -601,10 +746,11 @@ int sgemm_supertiled(int64_t M, int64_t N, int64_t K, float alpha, const float* 
                 const int64_t k0 = kt * tk, depth = std::min(tk, K - k0);
                 const float* As = A + r0 * lda + k0;
                 const float* Bs = B + k0 * ldb + c0;
-                const int entry = choose_entry(rows, cols, depth, lda, ldb, ldc);
+                ChoiceSource src;
+                const int entry = choose_entry(rows, cols, depth, lda, ldb, ldc, &src);
                 if (entry < 0) return SGEMM_ERR_NO_CONFIG;
                 st = launch_gemm(entry, rows, cols, depth, alpha, As, lda, Bs, ldb, 1.0f, Cs,
-                                 ldc, s);
+                                 ldc, s, src);
                 if (st != SGEMM_OK) return st;
             }
         }
@@ -627,9 +773,17 @@ int sgemm_tc(int64_t M, int64_t N, int64_t K, float alpha, const float* A, int64
     const int st = check_gemm_args(M, N, K, alpha, A, lda, B, ldb, C, ldc);
     if (st != SGEMM_OK) return st;
     if (!tc_fmt_ok(fmt)) return -12;
-    if (M == 0 || N == 0) return SGEMM_OK;
+    if (M == 0 || N == 0) {
+        if (log_on()) log_line("sgemm_tc M=%lld N=%lld: empty, nothing enqueued", (long long)M, (long long)N);
+        return SGEMM_OK;
+    }
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    if (K == 0 || alpha == 0.0f) return launch_init(M, N, beta, C, ldc, s);
+    if (K == 0 || alpha == 0.0f) {
+        if (log_on())
+            log_line("sgemm_tc M=%lld N=%lld K=%lld alpha=%g: A and B not read, C <- beta*C",
+                     (long long)M, (long long)N, (long long)K, (double)alpha);
+        return launch_init(M, N, beta, C, ldc, s);
+    }
     const TcTable& t = tc_table();
     const int e = tc_choose(fmt, M, N, K);
     if (e < 0) return SGEMM_ERR_NO_CONFIG;
@@ -641,10 +795,10 @@ int sgemm_tc(int64_t M, int64_t N, int64_t K, float alpha, const float* A, int64
         int f = tc_find(fmt, sgemm_tc_config{256, 256, 32, 4, 2, 0});
         if (f < 0) return SGEMM_ERR_NO_CONFIG;
         return launch_entry(t.fused[fmt][f], SGEMM_KIND_TC, M, N, K, alpha, A, lda, B, ldb, beta,
-                            C, ldc, s);
+                            C, ldc, s, "fused fallback");
     }
     return launch_entry(t.fused[fmt][e], SGEMM_KIND_TC, M, N, K, alpha, A, lda, B, ldb, beta, C,
-                        ldc, s);
+                        ldc, s, "fused");
 }
 
 int sgemm_tc_config_count(int32_t fmt) { return tc_fmt_ok(fmt) ? tc_table().count(fmt) : -1; }
@@ -786,34 +940,36 @@ int sgemm_tune(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_
 
     float *A = nullptr, *B = nullptr, *C = nullptr;
     const int64_t na = (M - 1) * lda + K, nb = (K - 1) * ldb + N, ncm = (M - 1) * ldc + N;
-    if (hipMalloc(&A, na * sizeof(float)) != hipSuccess ||
-        hipMalloc(&B, nb * sizeof(float)) != hipSuccess ||
-        hipMalloc(&C, ncm * sizeof(float)) != hipSuccess) {
+    hipError_t me = hipMalloc(&A, na * sizeof(float));
+    if (me == hipSuccess) me = hipMalloc(&B, nb * sizeof(float));
+    if (me == hipSuccess) me = hipMalloc(&C, ncm * sizeof(float));
+    if (me != hipSuccess) {
         (void)hipGetLastError();   // a failed allocation must not fail later launches
         (void)hipFree(A);
         (void)hipFree(B);
         (void)hipFree(C);
-        return SGEMM_ERR_ALLOC;
+        return me == hipErrorOutOfMemory ? SGEMM_ERR_ALLOC : hip_status(me);
     }
     int st = SGEMM_OK;
     hipEvent_t e0 = nullptr, e1 = nullptr;
     std::vector<std::pair<float, int>> once;
     auto time_one = [&](int entry, int n, float* ms) -> int {
-        if (hipEventRecord(e0, s) != hipSuccess) return SGEMM_ERR_HIP_BASE;
+        hipError_t he = hipEventRecord(e0, s);
+        if (he != hipSuccess) return hip_status(he);
         for (int r = 0; r < n; ++r) {
-            const int rc = launch_gemm(entry, M, N, K, 1.0f, A, lda, B, ldb, 0.0f, C, ldc, s);
+            const int rc = launch_gemm(entry, M, N, K, 1.0f, A, lda, B, ldb, 0.0f, C, ldc, s, kTuned);
             if (rc != SGEMM_OK) return rc;
         }
-        if (hipEventRecord(e1, s) != hipSuccess) return SGEMM_ERR_HIP_BASE;
-        if (hipEventSynchronize(e1) != hipSuccess) return SGEMM_ERR_HIP_BASE;
-        if (hipEventElapsedTime(ms, e0, e1) != hipSuccess) return SGEMM_ERR_HIP_BASE;
+        if ((he = hipEventRecord(e1, s)) != hipSuccess) return hip_status(he);
+        if ((he = hipEventSynchronize(e1)) != hipSuccess) return hip_status(he);
+        if ((he = hipEventElapsedTime(ms, e0, e1)) != hipSuccess) return hip_status(he);
         *ms /= (float)n;
         return SGEMM_OK;
     };
     st = hip_status(phobos::launch_fill_pattern(A, na, 1u, s));
     if (st == SGEMM_OK) st = hip_status(phobos::launch_fill_pattern(B, nb, 2u, s));
-    if (st == SGEMM_OK && hipEventCreate(&e0) != hipSuccess) st = SGEMM_ERR_HIP_BASE;
-    if (st == SGEMM_OK && hipEventCreate(&e1) != hipSuccess) st = SGEMM_ERR_HIP_BASE;
+    if (st == SGEMM_OK) st = hip_status(hipEventCreate(&e0));
+    if (st == SGEMM_OK) st = hip_status(hipEventCreate(&e1));
     // The shader clock ramps up over tens of milliseconds of load: without a
     // warm-up the first candidates are timed slow.  About 100 ms of the
     // built-in choice first; its time also sizes the short timings below, so
@@ -825,12 +981,12 @@ int sgemm_tune(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_
     const int n_warm = (int)std::min(5000.0f, std::ceil(100.0f / t_est));
     const int n_short = (int)std::min(1000.0f, std::ceil(1.0f / t_est));
     for (int r = 0; st == SGEMM_OK && r < n_warm; ++r)
-        st = launch_gemm(dflt, M, N, K, 1.0f, A, lda, B, ldb, 0.0f, C, ldc, s);
+        st = launch_gemm(dflt, M, N, K, 1.0f, A, lda, B, ldb, 0.0f, C, ldc, s, kDefault);
     // every candidate once (after one untimed launch)
     for (int i = 0; st == SGEMM_OK && i < nc; ++i) {
         const int entry = find_entry(cands[i]);
         float ms = 0.0f;
-        st = launch_gemm(entry, M, N, K, 1.0f, A, lda, B, ldb, 0.0f, C, ldc, s);
+        st = launch_gemm(entry, M, N, K, 1.0f, A, lda, B, ldb, 0.0f, C, ldc, s, kTuned);
         if (st == SGEMM_OK) st = time_one(entry, n_short, &ms);
         if (st == SGEMM_OK) once.emplace_back(ms, entry);
     }
@@ -905,8 +1061,9 @@ int sgemm_tune_forget(void) {
     return n;
 }
 
-int sgemm_trace_begin(int64_t capacity) {
+int sgemm_trace_begin_sampled(int64_t capacity, int64_t every) {
     if (capacity < 1) return -1;
+    if (every < 1) return -2;
     std::lock_guard<std::mutex> lk(g_mu);
     for (auto& r : g_trace) {
         (void)hipEventDestroy(r.start);
@@ -915,9 +1072,14 @@ int sgemm_trace_begin(int64_t capacity) {
     g_trace.clear();
     g_trace.reserve((size_t)std::min<int64_t>(capacity, 1 << 20));
     g_trace_cap = capacity;
+    g_trace_every = every;
+    g_trace_seen = 0;
     g_trace_on = true;
+    g_trace_flag.store(true, std::memory_order_release);
     return SGEMM_OK;
 }
+
+int sgemm_trace_begin(int64_t capacity) { return sgemm_trace_begin_sampled(capacity, 1); }
 
 int sgemm_trace_end(float* ms_out, int32_t* kind_out, int64_t cap, int64_t* n_out) {
     if (cap < 0) return -3;
@@ -926,6 +1088,7 @@ int sgemm_trace_end(float* ms_out, int32_t* kind_out, int64_t cap, int64_t* n_ou
     {
         std::lock_guard<std::mutex> lk(g_mu);
         g_trace_on = false;
+        g_trace_flag.store(false, std::memory_order_release);
         recs.swap(g_trace);
     }
     int st = SGEMM_OK;
@@ -974,5 +1137,11 @@ const char* sgemm_status_string(int status) {
 }
 
 int sgemm_version(void) { return PHOBOS_SGEMM_VERSION; }
+
+int sgemm_set_log(int32_t on) {
+    const int was = log_on() ? 1 : 0;
+    g_log.store(on != 0 ? 1 : 0, std::memory_order_relaxed);
+    return was;
+}
 
 }  // extern "C"

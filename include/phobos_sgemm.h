@@ -12,7 +12,14 @@
  * Layout.  All matrices are row-major: element (i, j) of X is X[i*ldx + j].
  *   A is M x K (lda >= max(1, K)), B is K x N (ldb >= max(1, N)),
  *   C is M x N (ldc >= max(1, N)).  Elements past the logical width of a row
- *   (the pads) are never read and never written.
+ *   (the pads) are never written and never reach a result, whatever they hold
+ *   (NaN and Inf included).  Some of them may be read: in the fp32 GEMM
+ *   kernels, when a tile at the right edge of C loads a 16-byte piece of a
+ *   row of B that straddles column N-1, the piece's floats past N-1 (at most
+ *   three, always before column ldb: that load path needs ldb % 4 == 0) are
+ *   read and then feed only columns of the tile that are not stored.  Rows
+ *   of a tile past M read row M-1 of A instead, and are not stored either.
+ *   Rows past the last one are never read.  No other kernel reads a pad.
  * Memory.  A, B and C are device pointers (hipMalloc'ed or equivalent) owned
  *   by the caller.  The library neither frees nor retains them.  They must
  *   stay valid until the work enqueued on `stream` has finished.  C must not
@@ -384,6 +391,11 @@ int sgemm_supertiled_host(int64_t M, int64_t N, int64_t K, float alpha,
  * frees the events.  Arguments of begin: 1 capacity (>= 1).  Of end:
  * 1 ms_out, 2 kind_out, 3 cap, 4 n_out (the output arrays may be NULL when
  * cap is 0).
+ * sgemm_trace_begin_sampled(capacity, every) traces only launches 0, every,
+ * 2*every, ... of those enqueued after it (every >= 1, else -2): a pair of
+ * events costs the stream some microseconds, so a long run of equal
+ * launches can be timed on a sample of them without slowing the rest.
+ * sgemm_trace_begin(capacity) is sgemm_trace_begin_sampled(capacity, 1).
  */
 #define SGEMM_KIND_GEMM 0
 #define SGEMM_KIND_INIT_LEAF 1
@@ -391,6 +403,7 @@ int sgemm_supertiled_host(int64_t M, int64_t N, int64_t K, float alpha,
 #define SGEMM_KIND_TC_CAST 3     /* the cast pass of its staged form */
 #define SGEMM_KIND_ATTENTION 4   /* one attention leaf */
 int sgemm_trace_begin(int64_t capacity);
+int sgemm_trace_begin_sampled(int64_t capacity, int64_t every);
 int sgemm_trace_end(float* ms_out, int32_t* kind_out, int64_t cap, int64_t* n_out);
 
 /* Human-readable text for a status code (static storage, never NULL). */
@@ -398,6 +411,23 @@ const char* sgemm_status_string(int status);
 
 /* PHOBOS_SGEMM_VERSION of the built library. */
 int sgemm_version(void);
+
+/*
+ * Dispatch log.  When on, every entry point writes one line to stderr per
+ * decision it takes, each starting "phobos_sgemm: ": a quick return (empty
+ * product; K == 0 or alpha == 0; an init leaf at beta == 1 that enqueues
+ * nothing), the super-tile grid of a super-tiled call, and each kernel it
+ * enqueues with its shape, scalars, tile and wave grid, where the tile came
+ * from (forced, SGEMM_FORCE_CFG, tuned or default), the load path (vec4 or
+ * scalar), the grid and the stream.  The environment variable SGEMM_LOG (a
+ * non-empty value other than "0") turns it on at the first call;
+ * sgemm_set_log(on) turns it on (non-zero) or off (0) for the process and
+ * returns the previous state (1 on, 0 off).  Host only; cannot fail.
+ * SGEMM_GROUP_M (tile rows per raster group, default 4) and SGEMM_XCD_REMAP
+ * (0 turns the XCD-aware tile order off), read once per process, tune the
+ * tile order of the fp32 and 16-bit GEMM kernels.
+ */
+int sgemm_set_log(int32_t on);
 
 #ifdef __cplusplus
 }

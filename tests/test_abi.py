@@ -123,6 +123,30 @@ def test_get_config_checks():
     assert lib.sgemm_get_config(4, 4, 4, 4, 4, 4, None) == -7
 
 
+@pytest.mark.parametrize("shape,want", [
+    # too few 64x64 tiles to fill 256 CUs: single-wave 32x32 tiles, 32 deep
+    ((256, 256, 256), (32, 32, 32, 1, 1)),
+    ((960, 960, 960), (32, 32, 32, 1, 1)),
+    ((960, 960, 16384), (32, 32, 32, 1, 1)),
+    # ... and 16 deep when K fits one such chunk
+    ((200, 200, 8), (32, 32, 16, 1, 1)),
+    ((200, 200, 16), (32, 32, 16, 1, 1)),
+    # from 16 x 16 tiles of 64x64 up the 64x64 tile fills the chip
+    ((1008, 1008, 1008), (64, 64, 16, 1, 1)),
+    ((1024, 1024, 1024), (64, 64, 16, 1, 1)),
+    # the five workloads' shapes and the super-tiled step leaf
+    ((4096, 4096, 4096), (256, 256, 32, 2, 2)),
+    ((65536, 512, 4096), (256, 256, 32, 2, 2)),
+    ((5003, 3001, 2047), (256, 128, 16, 4, 2)),
+    # 3072^3: 256x128 leaves 1.125 waves; the estimate takes 128x128x32
+    ((3072, 3072, 3072), (128, 128, 32, 2, 2)),
+])
+def test_default_config_picks(shape, want):
+    """The built-in choice at the boundaries of its rule, fixed on the CPU."""
+    M, N, K = shape
+    assert g.sgemm_get_config(M, N, K, K, N, N).as_tuple() == want
+
+
 def test_default_config_fits_the_shape():
     names = {c.as_tuple() for c in g.configs()}
     for shape in [(1, 1, 1), (31, 17, 5), (256, 256, 256), (4096, 4096, 4096),
@@ -150,7 +174,7 @@ def test_tune_candidates_follow_the_autotune_ranges():
     assert small and all(c.bm <= 64 and c.bn <= 96 for c in small)
     assert len(small) < len(all_cfgs)
     tiny = g.sgemm_tune_candidates(1, 1, 1)
-    assert {c.as_tuple()[:2] for c in tiny} == {(32, 32)}
+    assert [c.as_tuple() for c in tiny] == [(32, 32, 16, 1, 1), (32, 32, 32, 1, 1)]
 
 
 def test_tune_candidates_and_tune_argument_checks():
@@ -172,6 +196,11 @@ def test_trace_argument_checks():
     assert lib.sgemm_trace_end(None, None, 0, ctypes.byref(n)) == 0
     assert n.value == 0
     assert lib.sgemm_trace_end(None, None, -1, None) == -3
+    assert lib.sgemm_trace_begin_sampled(0, 1) == -1
+    assert lib.sgemm_trace_begin_sampled(4, 0) == -2
+    assert lib.sgemm_trace_begin_sampled(4, 7) == 0
+    assert lib.sgemm_trace_end(None, None, 0, ctypes.byref(n)) == 0
+    assert n.value == 0
 
 
 @pytest.mark.parametrize("args,want", [
