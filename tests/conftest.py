@@ -8,3 +8,16 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    """The largest err/bound of every full-size parity check that ran."""
+    try:
+        from tests import gpu_util
+    except Exception:
+        return
+    if not gpu_util.REPORT:
+        return
+    terminalreporter.section("largest err/bound per workload")
+    for name, worst in gpu_util.REPORT:
+        terminalreporter.write_line(f"{name}: {worst:.3g}")

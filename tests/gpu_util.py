@@ -9,6 +9,15 @@ import sgemm_workloads as wl
 
 U = 2.0 ** -24
 
+# (workload, largest err/bound) of the checks run in this session; the
+# conftest prints them at the end of the run
+REPORT = []
+
+
+def report(name, worst):
+    REPORT.append((name, float(worst)))
+    print(f"{name}: max err/bound {worst:.3g}", flush=True)
+
 
 def device():
     assert torch.cuda.is_available(), "GPU tests need a GPU"
@@ -74,8 +83,59 @@ def assert_well_inside(name, worst, limit=0.25):
     a random walk far inside it (a largest err/bound of order 1e-2 at these
     sizes).  A ratio above a quarter of the bound marks a path that is wrong
     yet still within it, e.g. one that drops or repeats a small term."""
-    print(f"{name}: max err/bound {worst:.3g}", flush=True)
+    report(name, worst)
     assert worst < limit, f"{name}: max err/bound {worst:.3g}, expected well below {limit}"
+
+
+def check_rows(w, x, outs, exact=False, slab=None, row_slabs=None):
+    """Every element of the named outputs (dict name -> flat C buffer after a
+    run on the inputs x) against the full oracle, computed slab by slab of
+    rows (all rows when `slab` is None; only the (first, count) ranges of
+    `row_slabs` when given).  exact: bit for bit (integer inputs); else each
+    element within the oracle's bound, and with two outputs their difference
+    within the same bound too.  Pads and the guard row of every output must be
+    unchanged.  Returns {name: largest err/bound} ({} when exact)."""
+    names = list(outs)
+    worst = {n: 0.0 for n in names}
+    pair_worst = 0.0
+    if row_slabs is None:
+        step = slab or w.M
+        row_slabs = [(r0, min(step, w.M - r0)) for r0 in range(0, w.M, step)]
+    got_all = {n: logical_c(w, outs[n]) for n in names}
+    for r0, rows in row_slabs:
+        a = x.A[r0 * w.lda:]
+        c = x.C[r0 * w.ldc:]
+        ref, bnd = oracle.sgemm(rows, w.N, w.K, w.alpha, a, x.B, w.beta, c,
+                                lda=w.lda, ldb=w.ldb, ldc=w.ldc, bound=not exact)
+        for n in names:
+            got = got_all[n][r0:r0 + rows]
+            assert not np.isnan(got).any(), f"{w.name}/{n}: NaN in rows {r0}..{r0 + rows - 1}"
+            if exact:
+                bad = np.argwhere(got != ref)
+                assert bad.size == 0, (f"{w.name}/{n}: {len(bad)} elements differ in rows "
+                                       f"{r0}..{r0 + rows - 1}, first {(bad[:5] + [r0, 0]).tolist()}")
+                continue
+            err = np.abs(got.astype(np.float64) - ref.astype(np.float64))
+            ratio = err / bnd
+            at = np.unravel_index(np.argmax(ratio), ratio.shape)
+            assert np.all(err <= bnd), (f"{w.name}/{n}: err/bound {ratio.max():.3g} at row "
+                                        f"{r0 + at[0]}, column {at[1]}")
+            worst[n] = max(worst[n], float(ratio.max()))
+        if not exact and len(names) == 2:
+            d = np.abs(got_all[names[0]][r0:r0 + rows].astype(np.float64)
+                       - got_all[names[1]][r0:r0 + rows])
+            assert np.all(d <= bnd), (f"{w.name}: |{names[0]} - {names[1]}| above the bound, "
+                                      f"ratio {(d / bnd).max():.3g}")
+            pair_worst = max(pair_worst, float((d / bnd).max()))
+        if len(row_slabs) > 1:
+            print(f"  {w.name}: rows {r0}..{r0 + rows - 1} checked", flush=True)
+    for n in names:
+        check_pads(w, x, outs[n])
+    if exact:
+        return {}
+    if len(names) == 2:
+        report(f"{w.name}: |{names[0]} - {names[1]}|", pair_worst)
+    return worst
 
 
 def check_pads(w, x, out):

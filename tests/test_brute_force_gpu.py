@@ -53,12 +53,14 @@ def _all_cfgs():
 
 def test_brute_force_default_tile():
     """The full set for the tile large shapes use (256x256x32 on 4 waves):
-    M, N in 1..9, BM-1..BM+1, 2BM+-1 and K in 1..9, BK+-1, 2BK+-1."""
+    M, N in 1..9, BM-1..BM+1, 2BM+-1 and K in 1..9, BK-1..BK+1, 2BK-1..2BK+1.
+    K = BK and 2BK are whole chunks: with a tile inside N every chunk,
+    the last one included, takes the direct loads."""
     cfg = g.sgemm_config(256, 256, 32, 2, 2)
     bm, bn, bk = cfg.bm, cfg.bn, cfg.bk
     ms = list(range(1, 10)) + [bm - 1, bm, bm + 1, 2 * bm - 1, 2 * bm + 1]
     ns = list(range(1, 10)) + [bn - 1, bn, bn + 1, 2 * bn - 1, 2 * bn + 1]
-    ks = list(range(1, 10)) + [bk - 1, bk + 1, 2 * bk - 1, 2 * bk + 1]
+    ks = list(range(1, 10)) + [bk - 1, bk, bk + 1, 2 * bk - 1, 2 * bk, 2 * bk + 1]
     cases = [(M, N, K) for M in ms for N in ns for K in ks]
     print(f"brute force {_cfg_id(cfg)}: {len(cases)} shapes", flush=True)
     with _forced(cfg):
@@ -67,11 +69,12 @@ def test_brute_force_default_tile():
 
 @pytest.mark.parametrize("cfg", _all_cfgs(), ids=_cfg_id)
 def test_brute_force_every_tile(cfg):
-    """A smaller cross product for each compiled tile."""
+    """A smaller cross product for each compiled tile (K = BK and 2BK end on
+    whole chunks, which a tile inside N loads directly to the end)."""
     bm, bn, bk = cfg.bm, cfg.bn, cfg.bk
     ms = [1, 2, 5, 9, bm - 1, bm + 1]
     ns = [1, 3, 8, bn - 1, bn + 1]
-    ks = [1, 2, 7, bk - 1, bk + 1, 2 * bk + 1]
+    ks = [1, 2, 7, bk - 1, bk, bk + 1, 2 * bk, 2 * bk + 1]
     cases = [(M, N, K) for M in ms for N in ns for K in ks]
     print(f"brute force {_cfg_id(cfg)}: {len(cases)} shapes", flush=True)
     with _forced(cfg):
