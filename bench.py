@@ -7,15 +7,19 @@ the row-major walk over the 4 x 4 grid of output super-tiles, and per
 super-tile the init leaf (a no-op launch-free identity at beta = 1) and four
 step leaves of 4096^3 each (64 GEMM launches per step).  Inputs are seeded
 synthetic uniform[-1, 1) matrices (the oracle's generators), resident in HBM
-before the timed region.  C keeps accumulating across steps (beta = 1); that
-changes no timing and the result is checked separately by the GPU tests.
---warmup W runs exactly W untimed steps first; without it, untimed steps run
-until at least 2 have run and at least 0.2 s has passed (the count is reported).
+before the timed region.  Each timed step runs between its own pair of HIP
+events, and before each step C is restored from a device copy of its initial
+values, outside the events (beta = 1 would otherwise let it accumulate);
+ms_per_step is the mean of the step times.  --warmup W runs exactly W
+untimed steps first; without it, untimed steps run until at least 2 have run
+and at least 0.2 s has passed (the count is reported).
 
 Printed: one JSON line with the metric (GFLOP/s = 2*M*N*K / time per step),
 the roofline of the dominant kernel (the step leaf; its duration per launch
 from HIP events the library records on the launch stream during the timed
-region) and the CPU oracle's rate on a bounded slab of the same product.
+region, around one launch in seven) and the CPU oracle's rate on a bounded
+slab of the same product.  The shader clock is sampled from the driver's
+sysfs clock table by a host thread during the timed region.
 The timed region records one more event after each step, so the config also
 gives each step's median, mean, standard deviation, min and max (ms), and the
 device with its HIP runtime; and the device's own FP32 matrix peak (compute units x
@@ -59,6 +63,7 @@ HIP_ATTR_MULTIPROCESSOR_COUNT = 63
 PEAK_HBM_GBS = 8000.0             # MI355X published HBM3E bandwidth
 PEAK_F16_MFMA_TFLOPS = 2500.0     # MI355X published dense fp16 / bf16 matrix peak
 DEFAULT_WORKLOAD = "supertiled_16384_t4096"
+TRACE_EVERY = 7
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sgemm_step_4096_ld16384.txt")
 TC_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "tc16_gemm_f16_16384_counters.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "fp32_gemm_02_amd", "csrc", f)
@@ -113,23 +118,82 @@ def warm_up(step, warmup, stream):
     return n
 
 
-def timed_steps(step, steps, stream):
-    """Run `steps` steps between HIP events on `stream`, one more event after
-    each step (recording events adds no work to the timed region).  Returns
-    the total on the stream, each step's time (ms) and the host wall time (s)."""
+def timed_steps(step, steps, stream, restore=None):
+    """Run `steps` steps, each between a HIP event pair of its own on
+    `stream`; `restore` (when given) runs before every step, outside the
+    pairs, to put C back to its initial values.  Returns the sum of the step
+    times (ms), each step's time (ms) and the host wall time of the whole
+    loop (s)."""
     import torch
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     torch.cuda.synchronize()
-    evs[0].record(stream)
     t0 = time.perf_counter()
     for i in range(steps):
+        if restore is not None:
+            restore()
+        starts[i].record(stream)
         step()
-        evs[i + 1].record(stream)
+        ends[i].record(stream)
     stream.synchronize()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per_step = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
-    return evs[0].elapsed_time(evs[-1]), per_step, wall
+    per_step = [starts[i].elapsed_time(ends[i]) for i in range(steps)]
+    return float(sum(per_step)), per_step, wall
+
+
+class ClockSampler:
+    """The shader clock during the timed region, sampled by a host thread from
+    the driver's sysfs table of shader clock levels (the line marked '*' is
+    the level the GPU runs at) every `period` seconds.  Reading a sysfs file
+    puts no work on the GPU.  summary() is None when the table is absent."""
+
+    def __init__(self, period=0.05):
+        import glob
+        import threading
+        self.period = period
+        self.paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self):
+        for path in self.paths:
+            try:
+                for line in open(path):
+                    if "*" in line:
+                        m = re.search(r"(\d+)\s*[Mm][Hh]z", line)
+                        if m:
+                            return int(m.group(1))
+            except OSError:
+                continue
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            v = self._read()
+            if v is not None:
+                self.samples.append(v)
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self.paths:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread.is_alive():
+            self._thread.join()
+
+    def summary(self):
+        if not self.samples:
+            return None
+        import numpy as np
+        v = np.asarray(self.samples, dtype=np.float64)
+        return {"source": "sysfs pp_dpm_sclk, current level", "samples": int(v.size),
+                "median_mhz": float(np.median(v)), "min_mhz": float(v.min()),
+                "max_mhz": float(v.max())}
 
 
 def step_stats(per_step):
@@ -272,7 +336,8 @@ def main_attention(args):
 
     args.warmup = warm_up(step, args.warmup, stream)
     g.sgemm_trace_begin(args.steps + 16)
-    ms_total, per_step, _ = timed_steps(step, args.steps, stream)
+    with ClockSampler() as clock:
+        ms_total, per_step, _ = timed_steps(step, args.steps, stream)
     ms_kern, kinds, n = g.sgemm_trace_end(cap=args.steps + 16)
     launch_ms = float(np.mean([t for t, k in zip(ms_kern, kinds) if k == g.SGEMM_KIND_ATTENTION]))
     ms_per_step = ms_total / args.steps
@@ -296,6 +361,7 @@ def main_attention(args):
                    "Nk": w.Nk, "D": w.D, "scale": w.scale, "BR": w.BR,
                    "inputs": "Q/K/V %s/%s/%s, seed %d" % (*w.dists, w.seed),
                    "launches_per_step": 1,
+                   "sclk_during_timed_region": clock.summary(),
                    "pct_of_fp32_matrix_peak": round(100.0 * value / 1e3 / PEAK_FP32_MFMA_TFLOPS, 2),
                    "step_ms": step_stats(per_step), "device": device_info()},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
@@ -408,9 +474,26 @@ def main():
         launches_per_step = 1 + g.sgemm_tc_get_config(tc, w.M, w.N, w.K).staged   # cast pass
     else:
         launches_per_step = 1
-    g.sgemm_trace_begin(args.steps * launches_per_step * 2 + 16)
-    ms_total, per_step, wall = timed_steps(step, args.steps, stream)
-    ms_kern, kinds, n = g.sgemm_trace_end(cap=args.steps * launches_per_step * 2 + 16)
+    # A pair of HIP events around a launch costs the stream about 10 us; on the
+    # 64 launches of a super-tiled step that is 1% of the step.  The launches
+    # of a step are all alike, so one in TRACE_EVERY is traced (7, prime to
+    # the 4 K steps of a super-tile, so every K position is sampled).
+    every = TRACE_EVERY if launches_per_step > 1 else 1
+    restore = None
+    if w.beta != 0:
+        # every timed step starts from the initial C (restored outside the
+        # step's events); the copy lives on the device, or in pinned memory
+        # for the host-resident form
+        c0 = dC.clone()
+
+        def restore():
+            with torch.cuda.stream(stream):
+                dC.copy_(c0, non_blocking=not host)
+    cap = args.steps * launches_per_step * 2 + 16
+    g.sgemm_trace_begin(cap, every=every)
+    with ClockSampler() as clock:
+        ms_total, per_step, wall = timed_steps(step, args.steps, stream, restore)
+    ms_kern, kinds, n = g.sgemm_trace_end(cap=cap)
     ms_per_step = ms_total / args.steps
     value = gflops(w.M, w.N, w.K, ms_per_step)
 
@@ -460,6 +543,9 @@ def main():
                        "bm=%d bn=%d bk=%d wm=%d wn=%d" %
                        g.sgemm_get_config(*step_shape, w.lda, w.ldb, w.ldc).as_tuple()),
                    "tuned": tuned is not None,
+                   "c_restored_each_step": restore is not None,
+                   "traced_launches": {"every": every, "count": len(step_ms)},
+                   "sclk_during_timed_region": clock.summary(),
                    "step_ms": step_stats(per_step),
                    "device": device_info(),
                    "launches_per_step": launches_per_step,
@@ -487,8 +573,8 @@ def main():
     if tuned is not None:
         g.sgemm_set_config(None)
     print(f"# timed {args.steps} steps: {ms_total:.2f} ms on the stream ({wall * 1e3:.2f} ms "
-          f"wall); {len(step_ms)} step-leaf launches traced, mean {avg_launch_ms:.4f} ms",
-          file=sys.stderr, flush=True)
+          f"wall, C restores included); {len(step_ms)} step-leaf launches traced (one in "
+          f"{every}), mean {avg_launch_ms:.4f} ms", file=sys.stderr, flush=True)
     print(json.dumps(out), flush=True)
 
 

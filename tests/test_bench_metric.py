@@ -68,3 +68,20 @@ def test_traffic_only_for_the_counted_kernel_source(tmp_path, monkeypatch):
     assert bench.measured_traffic(bench.DEFAULT_WORKLOAD, "bf16") is None
     f.write_text("hbm_bytes_per_launch: 1234\nkernel_source_sha256_16: 0000000000000000\n")
     assert bench.measured_traffic(bench.DEFAULT_WORKLOAD) is None
+
+
+def test_clock_sampler_reads_the_marked_level(tmp_path):
+    f = tmp_path / "pp_dpm_sclk"
+    f.write_text("0: 500Mhz\n1: 1900Mhz *\n2: 2400Mhz\n")
+    c = bench.ClockSampler(period=0.01)
+    c.paths = [str(f)]
+    with c:
+        import time
+        time.sleep(0.05)
+    s = c.summary()
+    assert s["samples"] >= 1 and s["median_mhz"] == 1900.0 == s["min_mhz"] == s["max_mhz"]
+    empty = bench.ClockSampler()
+    empty.paths = []
+    with empty:
+        pass
+    assert empty.summary() is None
