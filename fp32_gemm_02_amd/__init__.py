@@ -31,6 +31,8 @@ SGEMM_ERR_TOO_LARGE = 3
 SGEMM_ERR_ALLOC = 4
 SGEMM_ERR_BUDGET = 5
 SGEMM_ERR_IO = 6
+SGEMM_ERR_SCRATCH = 7
+SGEMM_TC_SCRATCH_BYTES = 64 * 1024 * 1024
 SGEMM_ERR_HIP_BASE = 1000
 SGEMM_WALK_ROWS = 0
 SGEMM_WALK_SHELLS = 1
@@ -113,6 +115,8 @@ _SIGNATURES = {
     "sgemm_tune_forget": ([], ctypes.c_int),
     "sgemm_tc": ([_i64, _i64, _i64, _f32, _vp, _i64, _vp, _i64, _f32, _vp, _i64, _i32, _vp],
                  ctypes.c_int),
+    "sgemm_tc_noalloc": ([_i64, _i64, _i64, _f32, _vp, _i64, _vp, _i64, _f32, _vp, _i64, _i32,
+                          _vp], ctypes.c_int),
     "sgemm_tc_config_count": ([_i32], ctypes.c_int),
     "sgemm_tc_config_at": ([_i32, _i32, ctypes.POINTER(sgemm_tc_config)], ctypes.c_int),
     "sgemm_tc_get_config": ([_i32, _i64, _i64, _i64, ctypes.POINTER(sgemm_tc_config)],
@@ -283,6 +287,20 @@ def sgemm_tc(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, fmt=None, stream=None
     the default) or bf16 (SGEMM_TC_BF16) on load, fp32 accumulation."""
     fmt = SGEMM_TC_F16 if fmt is None else fmt
     _check(sgemm_tc_raw(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, fmt, stream), "sgemm_tc")
+
+
+def sgemm_tc_noalloc_raw(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, fmt, stream=None):
+    a, b, c = _gemm_ptrs(M, N, K, alpha, A, lda, B, ldb, C, ldc, "sgemm_tc_noalloc")
+    return lib().sgemm_tc_noalloc(M, N, K, alpha, a, lda, b, ldb, beta, c, ldc, fmt,
+                                  _stream(stream))
+
+
+def sgemm_tc_noalloc(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, fmt=None, stream=None):
+    """sgemm_tc's staged form on the library's static 16-bit workspace (no
+    allocation; the workspace must fit in SGEMM_TC_SCRATCH_BYTES)."""
+    fmt = SGEMM_TC_F16 if fmt is None else fmt
+    _check(sgemm_tc_noalloc_raw(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, fmt, stream),
+           "sgemm_tc_noalloc")
 
 
 def tc_configs(fmt):

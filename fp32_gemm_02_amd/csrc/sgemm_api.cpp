@@ -509,19 +509,82 @@ hipMemPool_t tc_pool(int dev) {
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
-// The staged form: cast pass into a workspace, 16-bit GEMM, workspace freed
-// on the stream.  Returns 1 (no launch) when the workspace cannot be had.
-int launch_tc_staged(int32_t fmt, const phobos::Tc16Entry& e, int64_t M, int64_t N, int64_t K,
-                     float alpha, const float* A, int64_t lda, const float* B, int64_t ldb,
-                     float beta, float* C, int64_t ldc, hipStream_t stream) {
+// The staged form's two launches on a workspace `ws` of at least
+// (Mp + Np) * Kp 16-bit values: the cast pass, then the 16-bit GEMM.
+int run_tc_staged(int32_t fmt, const phobos::Tc16Entry& e, int64_t M, int64_t N, int64_t K,
+                  float alpha, const float* A, int64_t lda, const float* B, int64_t ldb,
+                  float beta, float* C, int64_t ldc, uint16_t* ws, hipStream_t stream) {
     const int64_t Mp = round_up(M, phobos::kTcPadMN), Np = round_up(N, phobos::kTcPadMN),
                   Kp = round_up(K, phobos::kTcPadK);
+    const int64_t tm = (M + e.cfg.bm - 1) / e.cfg.bm, tn = (N + e.cfg.bn - 1) / e.cfg.bn;
+    const size_t bytes = (size_t)((Mp + Np) * Kp) * sizeof(uint16_t);
+    uint16_t* A16 = ws;
+    uint16_t* B16 = A16 + Mp * Kp;
+    int st;
+    if (log_on())
+        log_line("launch tc_cast M=%lld N=%lld K=%lld -> workspace %lldx%lld + %lldx%lld "
+                 "(%zu bytes at %p) fmt=%s stream=%p",
+                 (long long)M, (long long)N, (long long)K, (long long)Mp, (long long)Kp,
+                 (long long)Np, (long long)Kp, bytes, (void*)ws,
+                 fmt == SGEMM_TC_F16 ? "f16" : "bf16", (void*)stream);
+    {
+        TraceScope ts(stream, SGEMM_KIND_TC_CAST);
+        const bool va = aligned16(A) && lda % 4 == 0, vb = aligned16(B) && ldb % 4 == 0;
+        st = hip_status(phobos::launch_tc_cast(fmt, A, lda, va, B, ldb, vb, (int)M, (int)N,
+                                               (int)K, A16, B16, (int)Mp, (int)Np, (int)Kp,
+                                               stream));
+    }
+    if (st != SGEMM_OK) return st;
+    phobos::Tc16Args p{};
+    p.A = A16;
+    p.B = B16;
+    p.ld = Kp;
+    p.M = (int32_t)M;
+    p.N = (int32_t)N;
+    p.K = (int32_t)Kp;
+    p.alpha = alpha;
+    p.beta = beta;
+    p.C = C;
+    p.ldc = ldc;
+    p.vec_c = aligned16(C) && ldc % 4 == 0;
+    p.tiles_m = (int32_t)tm;
+    p.tiles_n = (int32_t)tn;
+    p.group_m = launch_env().group_m;
+    p.xcd_remap = ((tm * tn) % 8 == 0 && launch_env().xcd_remap) ? 1 : 0;
+    if (log_on())
+        log_line("launch tc_gemm M=%lld N=%lld K=%lld (padded to %lld) ldc=%lld alpha=%g "
+                 "beta=%g fmt=%s tile=%dx%dx%d waves=%dx%d staged grid=%lld stream=%p",
+                 (long long)M, (long long)N, (long long)K, (long long)Kp, (long long)ldc,
+                 (double)alpha, (double)beta, fmt == SGEMM_TC_F16 ? "f16" : "bf16",
+                 e.cfg.bm, e.cfg.bn, e.cfg.bk, e.cfg.wm, e.cfg.wn, (long long)(tm * tn),
+                 (void*)stream);
+    TraceScope ts(stream, SGEMM_KIND_TC);
+    return hip_status(e.launch(p, stream));
+}
+
+// Checks shared by both workspaces: grid size, the 40-bit workspace extent
+// and the 16-bit GEMM's 32-bit row offsets.  Returns SGEMM_OK, an error, or
+// 1 when the staged form cannot address this K (the fused form must run).
+int tc_staged_fits(const phobos::Tc16Entry& e, int64_t M, int64_t N, int64_t K) {
+    const int64_t Mp = round_up(M, phobos::kTcPadMN), Kp = round_up(K, phobos::kTcPadK);
     const int64_t tm = (M + e.cfg.bm - 1) / e.cfg.bm, tn = (N + e.cfg.bn - 1) / e.cfg.bn;
     if (tm * tn * e.threads > kMaxGridItems || Mp * Kp >= (int64_t(1) << 40))
         return SGEMM_ERR_TOO_LARGE;
     // the 16-bit kernel addresses a tile's rows with 32-bit byte offsets
     const int64_t span = (std::max(e.cfg.bm, e.cfg.bn) - 1) * Kp + e.cfg.bk;
     if (span * (int64_t)sizeof(uint16_t) > (int64_t)UINT32_MAX) return 1;
+    return SGEMM_OK;
+}
+
+// The staged form: cast pass into a workspace, 16-bit GEMM, workspace freed
+// on the stream.  Returns 1 (no launch) when the workspace cannot be had.
+int launch_tc_staged(int32_t fmt, const phobos::Tc16Entry& e, int64_t M, int64_t N, int64_t K,
+                     float alpha, const float* A, int64_t lda, const float* B, int64_t ldb,
+                     float beta, float* C, int64_t ldc, hipStream_t stream) {
+    const int fits = tc_staged_fits(e, M, N, K);
+    if (fits != SGEMM_OK) return fits;
+    const int64_t Mp = round_up(M, phobos::kTcPadMN), Np = round_up(N, phobos::kTcPadMN),
+                  Kp = round_up(K, phobos::kTcPadK);
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return hip_status(hipGetLastError());
     hipMemPool_t pool = tc_pool(dev);
@@ -532,49 +595,8 @@ int launch_tc_staged(int32_t fmt, const phobos::Tc16Entry& e, int64_t M, int64_t
         (void)hipGetLastError();
         return 1;
     }
-    uint16_t* A16 = static_cast<uint16_t*>(ws);
-    uint16_t* B16 = A16 + Mp * Kp;
-    int st;
-    if (log_on())
-        log_line("launch tc_cast M=%lld N=%lld K=%lld -> workspace %lldx%lld + %lldx%lld "
-                 "(%zu bytes) fmt=%s stream=%p",
-                 (long long)M, (long long)N, (long long)K, (long long)Mp, (long long)Kp,
-                 (long long)Np, (long long)Kp, bytes, fmt == SGEMM_TC_F16 ? "f16" : "bf16",
-                 (void*)stream);
-    {
-        TraceScope ts(stream, SGEMM_KIND_TC_CAST);
-        const bool va = aligned16(A) && lda % 4 == 0, vb = aligned16(B) && ldb % 4 == 0;
-        st = hip_status(phobos::launch_tc_cast(fmt, A, lda, va, B, ldb, vb, (int)M, (int)N,
-                                               (int)K, A16, B16, (int)Mp, (int)Np, (int)Kp,
-                                               stream));
-    }
-    if (st == SGEMM_OK) {
-        phobos::Tc16Args p{};
-        p.A = A16;
-        p.B = B16;
-        p.ld = Kp;
-        p.M = (int32_t)M;
-        p.N = (int32_t)N;
-        p.K = (int32_t)Kp;
-        p.alpha = alpha;
-        p.beta = beta;
-        p.C = C;
-        p.ldc = ldc;
-        p.vec_c = aligned16(C) && ldc % 4 == 0;
-        p.tiles_m = (int32_t)tm;
-        p.tiles_n = (int32_t)tn;
-        p.group_m = launch_env().group_m;
-        p.xcd_remap = ((tm * tn) % 8 == 0 && launch_env().xcd_remap) ? 1 : 0;
-        if (log_on())
-            log_line("launch tc_gemm M=%lld N=%lld K=%lld (padded to %lld) ldc=%lld alpha=%g "
-                     "beta=%g fmt=%s tile=%dx%dx%d waves=%dx%d staged grid=%lld stream=%p",
-                     (long long)M, (long long)N, (long long)K, (long long)Kp, (long long)ldc,
-                     (double)alpha, (double)beta, fmt == SGEMM_TC_F16 ? "f16" : "bf16",
-                     e.cfg.bm, e.cfg.bn, e.cfg.bk, e.cfg.wm, e.cfg.wn, (long long)(tm * tn),
-                     (void*)stream);
-        TraceScope ts(stream, SGEMM_KIND_TC);
-        st = hip_status(e.launch(p, stream));
-    }
+    int st = run_tc_staged(fmt, e, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                           static_cast<uint16_t*>(ws), stream);
     const hipError_t fe = hipFreeAsync(ws, stream);
     if (st == SGEMM_OK) st = hip_status(fe);
     return st;
@@ -799,6 +821,47 @@ int sgemm_tc(int64_t M, int64_t N, int64_t K, float alpha, const float* A, int64
     }
     return launch_entry(t.fused[fmt][e], SGEMM_KIND_TC, M, N, K, alpha, A, lda, B, ldb, beta, C,
                         ldc, s, "fused");
+}
+
+int sgemm_tc_noalloc(int64_t M, int64_t N, int64_t K, float alpha, const float* A,
+                     int64_t lda, const float* B, int64_t ldb, float beta, float* C,
+                     int64_t ldc, int32_t fmt, void* stream) {
+    const int st = check_gemm_args(M, N, K, alpha, A, lda, B, ldb, C, ldc);
+    if (st != SGEMM_OK) return st;
+    if (!tc_fmt_ok(fmt)) return -12;
+    if (M == 0 || N == 0) {
+        if (log_on())
+            log_line("sgemm_tc_noalloc M=%lld N=%lld: empty, nothing enqueued", (long long)M,
+                     (long long)N);
+        return SGEMM_OK;
+    }
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (K == 0 || alpha == 0.0f) {
+        if (log_on())
+            log_line("sgemm_tc_noalloc M=%lld N=%lld K=%lld alpha=%g: A and B not read, "
+                     "C <- beta*C", (long long)M, (long long)N, (long long)K, (double)alpha);
+        return launch_init(M, N, beta, C, ldc, s);
+    }
+    const TcTable& t = tc_table();
+    int e = -1;
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        e = g_tc_forced[fmt];
+    }
+    if (e < t.nfused[fmt]) e = tc_find(fmt, sgemm_tc_config{256, 256, 64, 4, 2, 1});
+    if (e < t.nfused[fmt]) return SGEMM_ERR_NO_CONFIG;
+    const phobos::Tc16Entry& entry = t.staged[fmt][e - t.nfused[fmt]];
+    const int64_t Mp = round_up(M, phobos::kTcPadMN), Np = round_up(N, phobos::kTcPadMN),
+                  Kp = round_up(K, phobos::kTcPadK);
+    if ((Mp + Np) * Kp * (int64_t)sizeof(uint16_t) > (int64_t)SGEMM_TC_SCRATCH_BYTES)
+        return SGEMM_ERR_SCRATCH;
+    const int fits = tc_staged_fits(entry, M, N, K);
+    if (fits != SGEMM_OK) return fits == 1 ? SGEMM_ERR_SCRATCH : fits;
+    hipError_t err = hipSuccess;
+    void* ws = phobos::tc_scratch(&err);
+    if (ws == nullptr) return hip_status(err);
+    return run_tc_staged(fmt, entry, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                         static_cast<uint16_t*>(ws), s);
 }
 
 int sgemm_tc_config_count(int32_t fmt) { return tc_fmt_ok(fmt) ? tc_table().count(fmt) : -1; }
@@ -1130,6 +1193,9 @@ const char* sgemm_status_string(int status) {
         case SGEMM_ERR_ALLOC: return "a device allocation failed";
         case SGEMM_ERR_BUDGET: return "no plan fits the device memory budget";
         case SGEMM_ERR_IO: return "the tuning cache file could not be read or written";
+        case SGEMM_ERR_SCRATCH:
+            return "the product's 16-bit workspace exceeds the static scratch of "
+                   "SGEMM_TC_SCRATCH_BYTES";
         default: break;
     }
     if (status >= SGEMM_ERR_HIP_BASE) return hipGetErrorString((hipError_t)(status - SGEMM_ERR_HIP_BASE));

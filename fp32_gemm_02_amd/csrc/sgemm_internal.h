@@ -74,6 +74,12 @@ hipError_t launch_tc_cast(int fmt, const float* A, int64_t lda, bool vec_a, cons
                           int64_t ldb, bool vec_b, int M, int N, int K, uint16_t* A16,
                           uint16_t* B16, int Mp, int Np, int Kp, hipStream_t stream);
 
+// Device address of the static workspace of SGEMM_TC_SCRATCH_BYTES on the
+// current device (sgemm_tc.hip), looked up on the first call on each device;
+// nullptr with *err set when the lookup fails.
+constexpr int kMaxDevices = 64;
+void* tc_scratch(hipError_t* err);
+
 // Attention O = softmax(scale * Q K^T) V over query rows 0 .. Nq-1 of the
 // given pointers, head dimension 64 (attention.hip), as one launch holding
 // the leaves of every super-tile of br rows.

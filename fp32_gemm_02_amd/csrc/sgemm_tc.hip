@@ -38,10 +38,19 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "sgemm_device.h"
 #include "sgemm_internal.h"
+
+// The staged form's 16-bit workspace for callers that cannot allocate
+// (sgemm_tc_noalloc): a static device array of SGEMM_TC_SCRATCH_BYTES that
+// every GPU the library runs on holds from the module's load until the
+// process ends.  Host code never uses this name as an address (on the host
+// it is only a stand-in for the symbol): tc_scratch() below looks up its
+// device address once per device and hands that out.
+static __device__ __align__(256) uint16_t scratch[SGEMM_TC_SCRATCH_BYTES / sizeof(uint16_t)];
 
 namespace phobos {
 
@@ -803,6 +812,34 @@ hipError_t launch_tc_cast(int fmt, const float* A, int64_t lda, bool vec_a, cons
         PHOBOS_CAST(SGEMM_TC_BF16);
 #undef PHOBOS_CAST
     return hipGetLastError();
+}
+
+void* tc_scratch(hipError_t* err) {
+    // device -> address of `scratch` there; looked up with that device current
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    *err = hipSuccess;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        *err = e;
+        return nullptr;
+    }
+    if (dev < 0 || dev >= kMaxDevices) {
+        *err = hipErrorInvalidDevice;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lk(mu);
+    if (addr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr) {
+            *err = e != hipSuccess ? e : hipErrorInvalidSymbol;
+            return nullptr;
+        }
+        addr[dev] = p;
+    }
+    return addr[dev];
 }
 
 #define PHOBOS_TC16_CFG(FMT, BM, BN, BK, NS, WM, WN)                                        \

@@ -64,6 +64,8 @@ extern "C" {
 #define SGEMM_ERR_BUDGET 5         /* no plan fits the device memory budget    */
 #define SGEMM_ERR_IO 6             /* the tuning cache file could not be read  */
                                    /* or written                               */
+#define SGEMM_ERR_SCRATCH 7        /* the product's workspace exceeds the      */
+                                   /* static scratch (sgemm_tc_noalloc)        */
 #define SGEMM_ERR_HIP_BASE 1000    /* 1000 + hipError_t                        */
 
 /*
@@ -262,6 +264,32 @@ typedef struct sgemm_tc_config {
 int sgemm_tc(int64_t M, int64_t N, int64_t K, float alpha, const float* A, int64_t lda,
              const float* B, int64_t ldb, float beta, float* C, int64_t ldc, int32_t fmt,
              void* stream);
+/*
+ * sgemm_tc_noalloc: sgemm_tc in its staged form without any allocation, for
+ * callers that cannot allocate device memory: code under HIP graph capture
+ * that must not record allocation nodes, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, quick returns, result and errors as
+ * sgemm_tc; the staged form always runs (the tile configuration forced for
+ * `fmt` by sgemm_tc_set_config when that is a staged one, else
+ * 256x256x64 on 4x2 waves), with the cast pass writing the 16-bit operands
+ * into a static device array of SGEMM_TC_SCRATCH_BYTES (64 MiB) instead of a
+ * pool allocation.  Its results are bit for bit those of sgemm_tc with the
+ * same staged configuration.  The array is the library's own, one per GPU,
+ * held until the process ends; its address on a GPU is looked up on the first
+ * call there.  The workspace, (ceil256(M) + ceil256(N)) * ceil64(K) * 2 bytes,
+ * must fit in it: larger products return SGEMM_ERR_SCRATCH before anything is
+ * enqueued (e.g. 4096^3 fits exactly; 8192 x 8192 x 2048 fits; 8192^3 does
+ * not).  No hipMalloc, hipFree or allocating library call is made.  Every
+ * call on a GPU shares that GPU's array and the cast pass rewrites all of the
+ * part a call uses (zero padding included), so nothing carries over between
+ * calls; calls that overlap in time on one GPU (different streams, or
+ * different host threads) race on the array and must be ordered by the caller.
+ */
+#define SGEMM_TC_SCRATCH_BYTES (64 * 1024 * 1024)
+int sgemm_tc_noalloc(int64_t M, int64_t N, int64_t K, float alpha, const float* A,
+                     int64_t lda, const float* B, int64_t ldb, float beta, float* C,
+                     int64_t ldc, int32_t fmt, void* stream);
+
 int sgemm_tc_config_count(int32_t fmt);
 int sgemm_tc_config_at(int32_t fmt, int32_t index, sgemm_tc_config* out);
 int sgemm_tc_get_config(int32_t fmt, int64_t M, int64_t N, int64_t K, sgemm_tc_config* out);

@@ -279,3 +279,19 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
                  g.version):
         with pytest.raises(RuntimeError, match="not built"):
             call()
+
+
+@pytest.mark.parametrize("args,want", [
+    ((-1, 4, 4, 1.0, 8, 4, 8, 4, 0.0, 8, 4, 1), -1),
+    ((4, 4, 5, 1.0, 8, 4, 8, 4, 0.0, 8, 4, 1), -6),
+    ((4, 4, 4, 1.0, 8, 4, 8, 4, 0.0, 8, 4, 5), -12),
+    ((0, 4, 4, 1.0, NULL, 4, NULL, 4, 0.0, NULL, 4, 2), 0),        # empty: nothing
+    ((4, 4, 0, 1.0, NULL, 4, NULL, 4, 1.0, 8, 4, 1), 0),           # K = 0, beta = 1: nothing
+    # workspaces past the static 64 MiB are refused before any HIP call
+    ((8192, 8192, 8192, 1.0, 8, 8192, 8, 8192, 0.0, 8, 8192, 1), g.SGEMM_ERR_SCRATCH),
+    ((4097, 4096, 4096, 1.0, 8, 4096, 8, 4096, 0.0, 8, 4096, 2), g.SGEMM_ERR_SCRATCH),
+    ((1 << 31, 4, 4, 1.0, 8, 4, 8, 4, 0.0, 8, 4, 2), g.SGEMM_ERR_TOO_LARGE),
+])
+def test_tc_noalloc_argument_checks(args, want):
+    assert g.sgemm_tc_noalloc_raw(*args, stream=0) == want
+    assert "static scratch" in g.status_string(g.SGEMM_ERR_SCRATCH)
