@@ -122,50 +122,48 @@ __attribute__((format(printf, 1, 2))) void log_line(const char* fmt, ...) {
     std::fprintf(stderr, "phobos_sgemm: %s\n", buf);
 }
 
-// Built-in choice when nothing is forced or tuned: the largest tile that still
-// gives every CU work, falling back to small tiles for small problems.  For
-// large shapes the 256x256x32 tile on 4 waves (one per SIMD, accumulators in
-// AGPRs) leads the 8-wave tiles by 0.5-1% at 4096^3, with uniform, normal,
-// +-1 and [0.5, 1) inputs alike, once the clock has risen.
-// When that tile count leaves more than a quarter of the last wave's slots
-// idle (288 tiles of 256x128 at 3072^3: 1.125 waves), the candidate with the
-// least estimated time is taken instead: waves x tile area / the tile's
-// relative rate (measured: 128x128x32 runs 3072^3 at 110.9 TFLOP/s against
-// 84.8 for 256x128).
+// Built-in choice when nothing is forced or tuned: the candidate tile with
+// the least estimated time on the chip's 256 CUs of 4 SIMDs each.  With T
+// tiles of bm x bn, the busiest CU holds ceil(T/256) of them, and its matrix
+// cores run at full rate only when those tiles bring at least 4 waves (one
+// per SIMD); so the estimate is
+//     ceil(T/256) * bm * bn / (rate * min(1, ceil(T/256) * waves / 4)),
+// with `rate` the tile's measured rate per CU against the 256x256 tile
+// (a sweep of every candidate over 20 square and skinny shapes from 1152^3
+// to 8192^3: the choice is within 3% of the fastest tile on all but one,
+// 4096 x 4096 x 512, at 4.5%).  The single-wave 32x32 tile, the only one
+// that fills the SIMDs of small products (1024^3: 26 us against 71 us for
+// a 64x64 tile), steps through K 32 deep while its CU holds at most 9 of
+// them and 16 deep beyond that, where more of them fit the LDS at once
+// (3072^3: 117 TFLOP/s against 106); K <= 16 takes it 16 deep.
 int default_entry(int64_t M, int64_t N, int64_t K) {
     struct Pick { int bm, bn, bk, wm, wn; double rate; };
-    static const Pick order[] = {
-        {256, 256, 32, 2, 2, 1.00}, {256, 128, 16, 4, 2, 0.99}, {128, 128, 32, 2, 2, 0.90},
-        {128, 64, 16, 2, 1, 0.75},  {64, 64, 16, 1, 1, 0.50},
+    constexpr int64_t kCUs = 256;
+    auto per_cu = [&](int bm, int bn) {
+        const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+        return (tiles + kCUs - 1) / kCUs;
     };
-    constexpr int kPicks = (int)(sizeof(order) / sizeof(order[0]));
-    const int64_t slots = 256;   // one workgroup per CU for the large tiles
-    auto tiles = [&](const Pick& p) { return ((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn); };
-    int first = -1;
-    for (int i = 0; i < kPicks && first < 0; ++i)
-        if (tiles(order[i]) >= slots) first = i;
-    if (first < 0) {
-        // Too few 64x64 tiles to fill the chip: single-wave 32x32 tiles give
-        // four times the workgroups, each with a quarter of the MFMA work on
-        // its SIMD, and 32-deep chunks halve each one's chain of chunk loads
-        // (256^3: 10.2 us against 22.5 us with 64x64x16).
-        return find_entry({32, 32, K > 16 ? 32 : 16, 1, 1});
-    }
-    const int64_t t0 = tiles(order[first]), w0 = (t0 + slots - 1) / slots;
-    int pick = first;
-    if (4 * (w0 * slots - t0) > w0 * slots) {
-        double best = 0.0;
-        for (int i = 0; i < kPicks; ++i) {
-            const Pick& p = order[i];
-            const double est = (double)((tiles(p) + slots - 1) / slots) * p.bm * p.bn / p.rate;
-            if (i == 0 || est < best) {
-                best = est;
-                pick = i;
-            }
+    const int64_t small_per_cu = per_cu(32, 32);
+    const Pick picks[] = {
+        {256, 256, 32, 2, 2, 1.00},
+        {256, 128, 16, 4, 2, 0.98},
+        {128, 128, 32, 2, 2, 0.90},
+        small_per_cu <= 9 ? Pick{32, 32, 32, 1, 1, 0.60} : Pick{32, 32, 16, 1, 1, 0.70},
+    };
+    int best = 0;
+    double best_est = 0.0;
+    for (int i = 0; i < (int)(sizeof(picks) / sizeof(picks[0])); ++i) {
+        const Pick& p = picks[i];
+        const int64_t per = per_cu(p.bm, p.bn);
+        const double occ = std::min(1.0, (double)(per * p.wm * p.wn) / 4.0);
+        const double est = (double)per * p.bm * p.bn / (p.rate * occ);
+        if (i == 0 || est < best_est) {
+            best = i;
+            best_est = est;
         }
     }
-    const Pick& p = order[pick];
-    return find_entry({p.bm, p.bn, p.bk, p.wm, p.wn});
+    const Pick& p = picks[best];
+    return find_entry({p.bm, p.bn, (p.bm == 32 && K <= 16) ? 16 : p.bk, p.wm, p.wn});
 }
 
 // SGEMM_FORCE_CFG="BMxBNxBKxWMxWN" (e.g. 256x256x32x2x2) forces a compiled

@@ -138,11 +138,15 @@ int sgemm_init_leaf(int64_t M, int64_t N, float beta, float* C, int64_t ldc,
  * `cfg` names no compiled configuration.  Order of precedence: a config set
  * here, then the environment variable SGEMM_FORCE_CFG="BMxBNxBKxWMxWN" (read
  * once per process; ignored with a message on stderr when malformed or not
- * compiled), then a tuned config for the exact shape, then the default: the
- * largest of 256x256, 256x128, 128x128, 128x64 and 64x64 tiles whose count
- * reaches the chip's 256 CUs, unless that count leaves more than a quarter
- * of its last wave idle, in which case the tile with the least estimated
- * time (waves x tile area / the tile's relative rate) is used.
+ * compiled), then a tuned config for the exact shape, then the default:
+ * among the 256x256x32 (2x2 waves), 256x128x16 (4x2), 128x128x32 (2x2) and
+ * single-wave 32x32 tiles (32 deep while a CU holds at most nine of them,
+ * else 16 deep; 16 deep whenever K <= 16), the one with the least estimated
+ * time on 256 CUs of 4 SIMDs: with T tiles the busiest CU holds
+ * ceil(T/256) of them and runs its matrix cores at full rate only with at
+ * least 4 waves, so the estimate is ceil(T/256) * bm * bn / (rate *
+ * min(1, ceil(T/256) * waves / 4)), `rate` being the tile's measured rate
+ * (1.00, 0.98, 0.90, and 0.60 / 0.70 for 32x32 at depth 32 / 16).
  */
 int sgemm_config_count(void);
 int sgemm_config_at(int32_t index, sgemm_config* out);

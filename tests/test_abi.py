@@ -124,22 +124,29 @@ def test_get_config_checks():
 
 
 @pytest.mark.parametrize("shape,want", [
-    # too few 64x64 tiles to fill 256 CUs: single-wave 32x32 tiles, 32 deep
+    # small products: only single-wave 32x32 tiles bring every SIMD work
     ((256, 256, 256), (32, 32, 32, 1, 1)),
     ((960, 960, 960), (32, 32, 32, 1, 1)),
+    ((1024, 1024, 1024), (32, 32, 32, 1, 1)),
     ((960, 960, 16384), (32, 32, 32, 1, 1)),
-    # ... and 16 deep when K fits one such chunk
+    ((1536, 1536, 1536), (32, 32, 32, 1, 1)),
+    # ... 16 deep when K fits one such chunk, or when a CU holds more than 9
     ((200, 200, 8), (32, 32, 16, 1, 1)),
     ((200, 200, 16), (32, 32, 16, 1, 1)),
-    # from 16 x 16 tiles of 64x64 up the 64x64 tile fills the chip
-    ((1008, 1008, 1008), (64, 64, 16, 1, 1)),
-    ((1024, 1024, 1024), (64, 64, 16, 1, 1)),
+    ((3072, 3072, 3072), (32, 32, 16, 1, 1)),
+    # one 128x128 tile per CU beats 13 small ones per CU, and 576 tiles of
+    # 256x256 (2.25 rounds of 256 CUs) lose to 2304 of 128x128 (9 rounds)
+    ((1792, 1792, 1792), (128, 128, 32, 2, 2)),
+    ((2048, 2048, 2048), (128, 128, 32, 2, 2)),
+    ((6144, 6144, 6144), (128, 128, 32, 2, 2)),
+    ((8192, 512, 4096), (128, 128, 32, 2, 2)),
+    # 400 tiles of 256x256 (2 rounds) against 800 of 256x128 on 8 waves
+    ((2560, 2560, 2560), (256, 128, 16, 4, 2)),
     # the five workloads' shapes and the super-tiled step leaf
     ((4096, 4096, 4096), (256, 256, 32, 2, 2)),
     ((65536, 512, 4096), (256, 256, 32, 2, 2)),
-    ((5003, 3001, 2047), (256, 128, 16, 4, 2)),
-    # 3072^3: 256x128 leaves 1.125 waves; the estimate takes 128x128x32
-    ((3072, 3072, 3072), (128, 128, 32, 2, 2)),
+    ((5003, 3001, 2047), (256, 256, 32, 2, 2)),
+    ((16384, 16384, 16384), (256, 256, 32, 2, 2)),
 ])
 def test_default_config_picks(shape, want):
     """The built-in choice at the boundaries of its rule, fixed on the CPU."""
