@@ -126,12 +126,18 @@ __attribute__((format(printf, 1, 2))) void log_line(const char* fmt, ...) {
 // the least estimated time on the chip's 256 CUs of 4 SIMDs each.  With T
 // tiles of bm x bn, the busiest CU holds ceil(T/256) of them, and its matrix
 // cores run at full rate only when those tiles bring at least 4 waves (one
-// per SIMD); so the estimate is
-//     ceil(T/256) * bm * bn / (rate * min(1, ceil(T/256) * waves / 4)),
+// per SIMD); a workgroup alone on its CU (every 256x256 one, whose registers
+// leave room for no other, and any tile when the CU holds just one) also
+// pays its prologue and C traffic with the matrix cores idle, which a
+// second resident workgroup would cover: about 64 k-steps' worth.  So the
+// estimate is
+//     ceil(T/256) * bm * bn * (K + [alone] * 64)
+//         / (rate * min(1, ceil(T/256) * waves / 4)),
 // with `rate` the tile's measured rate per CU against the 256x256 tile
 // (a sweep of every candidate over 20 square and skinny shapes from 1152^3
-// to 8192^3: the choice is within 3% of the fastest tile on all but one,
-// 4096 x 4096 x 512, at 4.5%).  The single-wave 32x32 tile, the only one
+// to 8192^3: the choice is within 2% of the fastest tile on every one, 0.2%
+// on average; 5003 x 3001 x 2047 takes 256x128, 478 us against 503 for
+// 256x256 on the same box).  The single-wave 32x32 tile, the only one
 // that fills the SIMDs of small products (1024^3: 26 us against 71 us for
 // a 64x64 tile), steps through K 32 deep while its CU holds at most 9 of
 // them and 16 deep beyond that, where more of them fit the LDS at once
@@ -156,7 +162,9 @@ int default_entry(int64_t M, int64_t N, int64_t K) {
         const Pick& p = picks[i];
         const int64_t per = per_cu(p.bm, p.bn);
         const double occ = std::min(1.0, (double)(per * p.wm * p.wn) / 4.0);
-        const double est = (double)per * p.bm * p.bn / (p.rate * occ);
+        const bool alone = (p.bm == 256 && p.bn == 256) || per == 1;
+        const double est =
+            (double)per * p.bm * p.bn * (double)(K + (alone ? 64 : 0)) / (p.rate * occ);
         if (i == 0 || est < best_est) {
             best = i;
             best_est = est;

@@ -144,9 +144,12 @@ int sgemm_init_leaf(int64_t M, int64_t N, float beta, float* C, int64_t ldc,
  * else 16 deep; 16 deep whenever K <= 16), the one with the least estimated
  * time on 256 CUs of 4 SIMDs: with T tiles the busiest CU holds
  * ceil(T/256) of them and runs its matrix cores at full rate only with at
- * least 4 waves, so the estimate is ceil(T/256) * bm * bn / (rate *
- * min(1, ceil(T/256) * waves / 4)), `rate` being the tile's measured rate
- * (1.00, 0.98, 0.90, and 0.60 / 0.70 for 32x32 at depth 32 / 16).
+ * least 4 waves, and a workgroup alone on its CU (a 256x256 one, or any
+ * when ceil(T/256) == 1) pays about 64 k-steps of fixed cost that a second
+ * resident one would hide, so the estimate is ceil(T/256) * bm * bn *
+ * (K + [alone] * 64) / (rate * min(1, ceil(T/256) * waves / 4)), `rate`
+ * being the tile's measured rate (1.00, 0.98, 0.90, and 0.60 / 0.70 for
+ * 32x32 at depth 32 / 16).
  */
 int sgemm_config_count(void);
 int sgemm_config_at(int32_t index, sgemm_config* out);

@@ -140,12 +140,15 @@ def test_get_config_checks():
     ((2048, 2048, 2048), (128, 128, 32, 2, 2)),
     ((6144, 6144, 6144), (128, 128, 32, 2, 2)),
     ((8192, 512, 4096), (128, 128, 32, 2, 2)),
-    # 400 tiles of 256x256 (2 rounds) against 800 of 256x128 on 8 waves
+    # 400 tiles of 256x256 (2 rounds) against 800 of 256x128 on 8 waves;
+    # with short K two resident 256x128 tiles per CU hide each other's
+    # fixed cost
     ((2560, 2560, 2560), (256, 128, 16, 4, 2)),
+    ((8192, 8192, 1024), (256, 128, 16, 4, 2)),
     # the five workloads' shapes and the super-tiled step leaf
     ((4096, 4096, 4096), (256, 256, 32, 2, 2)),
     ((65536, 512, 4096), (256, 256, 32, 2, 2)),
-    ((5003, 3001, 2047), (256, 256, 32, 2, 2)),
+    ((5003, 3001, 2047), (256, 128, 16, 4, 2)),
     ((16384, 16384, 16384), (256, 256, 32, 2, 2)),
 ])
 def test_default_config_picks(shape, want):
