@@ -23,7 +23,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libphobos_sgemm.so")
+# PHOBOS_SGEMM_LIB names another build of the library (e.g. the CPU-only
+# sanitizer build of the host code); by default the one built in place here
+LIB_PATH = os.environ.get("PHOBOS_SGEMM_LIB") or os.path.join(HERE, "libphobos_sgemm.so")
 
 SGEMM_OK = 0
 SGEMM_ERR_NO_CONFIG = 2

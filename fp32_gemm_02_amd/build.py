@@ -1,8 +1,11 @@
 """Compile the gfx950 SGEMM library in place (hipcc, no JIT, no torch extension).
 
     python -m fp32_gemm_02_amd.build
+    python -m fp32_gemm_02_amd.build --sanitize DIR
 
-writes fp32_gemm_02_amd/libphobos_sgemm.so next to this file.  Each source is
+writes fp32_gemm_02_amd/libphobos_sgemm.so next to this file (or, with
+--sanitize, DIR/libphobos_sgemm.so with AddressSanitizer and
+UndefinedBehaviorSanitizer in its host code, for CPU-only checks).  Each source is
 compiled to an object of its own, in parallel, then the objects are linked.
 """
 import os
@@ -38,7 +41,39 @@ def _run(cmd):
     return proc.returncode, err
 
 
-def build(extra_flags=(), out=LIB, verbose=False, jobs=None):
+# The CPU-only check of the host code: AddressSanitizer and
+# UndefinedBehaviorSanitizer on the host pass only (the device code is built
+# as usual), the sanitizer runtime shared, to be preloaded into the process.
+SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=undefined", "-shared-libasan", "-g",
+                  "-fno-omit-frame-pointer"]
+
+
+def asan_runtime():
+    """Path of the compiler's shared AddressSanitizer runtime (None if absent)."""
+    import glob
+    hits = sorted(glob.glob(os.path.join(os.path.dirname(os.path.dirname(HIPCC)), "llvm", "lib",
+                                         "clang", "*", "lib", "linux",
+                                         "libclang_rt.asan-x86_64.so")))
+    return hits[-1] if hits else None
+
+
+def build_sanitized(out_dir, verbose=False):
+    """The library with sanitized host code, as out_dir/libphobos_sgemm.so;
+    load it with asan_runtime() preloaded (LD_PRELOAD) and PHOBOS_SGEMM_LIB
+    pointing at it.  For CPU-only runs: no GPU work is meant to go through it."""
+    os.makedirs(out_dir, exist_ok=True)
+    rt = asan_runtime()
+    if rt is None:
+        raise RuntimeError("no shared AddressSanitizer runtime next to the compiler")
+    # linked against the runtime (found through the rpath), so that a plain C
+    # program can link the library too
+    return build(extra_flags=SANITIZE_FLAGS, out=os.path.join(out_dir, "libphobos_sgemm.so"),
+                 verbose=verbose,
+                 link_flags=SANITIZE_FLAGS + ["-Wl,-rpath," + os.path.dirname(rt)])
+
+
+def build(extra_flags=(), out=LIB, verbose=False, jobs=None, link_flags=()):
     inc = ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc")]
     jobs = jobs or min(len(SOURCES), max(1, os.cpu_count() or 1), 8)
     with tempfile.TemporaryDirectory(prefix="phobos_build_") as tmpdir:
@@ -56,7 +91,8 @@ def build(extra_flags=(), out=LIB, verbose=False, jobs=None):
             if err.strip() and verbose:
                 print(err, file=sys.stderr)
         tmp = out + ".tmp"
-        link = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+        link = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *link_flags, *objs, "-o",
+                tmp]
         if verbose:
             print(" ".join(link), flush=True)
         rc, err = _run(link)
@@ -67,4 +103,7 @@ def build(extra_flags=(), out=LIB, verbose=False, jobs=None):
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    if len(sys.argv) > 2 and sys.argv[1] == "--sanitize":
+        print(build_sanitized(sys.argv[2], verbose=True))
+    else:
+        print(build(verbose=True))
