@@ -12,7 +12,7 @@ events, and before each step C is restored from a device copy of its initial
 values, outside the events (beta = 1 would otherwise let it accumulate);
 ms_per_step is the mean of the step times.  --warmup W runs exactly W
 untimed steps first; without it, untimed steps run until at least 2 have run
-and at least 0.2 s has passed (the count is reported).
+and at least 1 s has passed (the count is reported).
 
 Printed: one JSON line with the metric (GFLOP/s = 2*M*N*K / time per step),
 the roofline of the dominant kernel (the step leaf; its duration per launch
@@ -96,14 +96,15 @@ def device_fp32_matrix_peak(device=0):
             "tflops": round(cus * khz * 1e3 * FP32_MFMA_FLOP_PER_CLK_PER_CU / 1e12, 2)}
 
 
-MIN_WARMUP_S = 0.2
+MIN_WARMUP_S = 1.0
 
 
 def warm_up(step, warmup, stream):
     """Untimed steps before the timed region: exactly `warmup` when it is
     given; otherwise at least 2 steps and at least MIN_WARMUP_S seconds of them
-    (each waited for), since the shader clock rises over tens of ms of load
-    and short steps timed after a few calls measure up to 12% slow.
+    (each waited for).  The shader clock rises over hundreds of ms of load:
+    after 0.15 s of the unaligned 5003x3001x2047 product the clock sampled
+    during the timed steps was still about 2.0 GHz of its 2.4.
     Returns the number of steps run."""
     if warmup is not None:
         for _ in range(warmup):
@@ -380,7 +381,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=None,
-                    help="untimed steps first (default: at least 2 and at least 0.2 s)")
+                    help="untimed steps first (default: at least 2 and at least 1 s)")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--tune", action="store_true")
     ap.add_argument("--host-resident", type=int, default=None, metavar="MIB")
@@ -479,6 +480,10 @@ def main():
     # of a step are all alike, so one in TRACE_EVERY is traced (7, prime to
     # the 4 K steps of a super-tile, so every K position is sampled).
     every = TRACE_EVERY if launches_per_step > 1 else 1
+    # a step of one launch is timed by the step's own event pair, so the
+    # library traces nothing then (a second pair per launch would only add
+    # stream time)
+    single = launches_per_step == 1 and tc is None and not host
     restore = None
     if w.beta != 0:
         # every timed step starts from the initial C (restored outside the
@@ -490,10 +495,14 @@ def main():
             with torch.cuda.stream(stream):
                 dC.copy_(c0, non_blocking=not host)
     cap = args.steps * launches_per_step * 2 + 16
-    g.sgemm_trace_begin(cap, every=every)
+    if not single:
+        g.sgemm_trace_begin(cap, every=every)
     with ClockSampler() as clock:
         ms_total, per_step, wall = timed_steps(step, args.steps, stream, restore)
-    ms_kern, kinds, n = g.sgemm_trace_end(cap=cap)
+    if not single:
+        ms_kern, kinds, n = g.sgemm_trace_end(cap=cap)
+    else:
+        ms_kern, kinds = per_step, [g.SGEMM_KIND_GEMM] * len(per_step)
     ms_per_step = ms_total / args.steps
     value = gflops(w.M, w.N, w.K, ms_per_step)
 
@@ -544,7 +553,8 @@ def main():
                        g.sgemm_get_config(*step_shape, w.lda, w.ldb, w.ldc).as_tuple()),
                    "tuned": tuned is not None,
                    "c_restored_each_step": restore is not None,
-                   "traced_launches": {"every": every, "count": len(step_ms)},
+                   "traced_launches": ({"every": every, "count": len(step_ms)} if not single
+                                       else "the step's own event pair (one launch per step)"),
                    "sclk_during_timed_region": clock.summary(),
                    "step_ms": step_stats(per_step),
                    "device": device_info(),
@@ -572,9 +582,11 @@ def main():
         out["cpu_baseline"] = cpu_baseline(x, w, fmt=tc)
     if tuned is not None:
         g.sgemm_set_config(None)
+    traced = (f"{len(step_ms)} step-leaf launches traced (one in {every})" if not single else
+              f"{len(step_ms)} launches timed by their step's events")
     print(f"# timed {args.steps} steps: {ms_total:.2f} ms on the stream ({wall * 1e3:.2f} ms "
-          f"wall, C restores included); {len(step_ms)} step-leaf launches traced (one in "
-          f"{every}), mean {avg_launch_ms:.4f} ms", file=sys.stderr, flush=True)
+          f"wall, C restores included); {traced}, mean {avg_launch_ms:.4f} ms", file=sys.stderr,
+          flush=True)
     print(json.dumps(out), flush=True)
 
 

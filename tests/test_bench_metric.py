@@ -55,7 +55,7 @@ def test_warm_up_default_runs_two_steps_and_the_minimum_time():
     assert ran == len(n) >= 2
     assert time.perf_counter() - t0 >= bench.MIN_WARMUP_S
     slow = []
-    assert bench.warm_up(lambda: (slow.append(1), time.sleep(0.15)), None, _Stream()) == 2
+    assert bench.warm_up(lambda: (slow.append(1), time.sleep(0.6)), None, _Stream()) == 2
 
 
 def test_traffic_only_for_the_counted_kernel_source(tmp_path, monkeypatch):
