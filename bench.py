@@ -221,11 +221,12 @@ def kernel_source_hash(sources=None):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload, tc=None):
+def measured_traffic(workload, tc=None, config=None):
     """HBM bytes per launch of the dominant kernel from the committed counter
     summary, if it was taken on the current kernel source for this workload
     (the fp32 step leaf of the default workload, or the fp16 GEMM of the
-    matrix-core variant); else None."""
+    matrix-core variant) and, when `config` (e.g. "256x256x32x4x2") is given
+    and the summary names its tile, on that tile; else None."""
     if workload != DEFAULT_WORKLOAD:
         return None
     if tc is None:
@@ -239,7 +240,10 @@ def measured_traffic(workload, tc=None):
     text = open(path).read()
     m_hash = re.search(r"^kernel_source_sha256_16:\s*(\S+)", text, re.M)
     m_bytes = re.search(r"^hbm_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
+    m_cfg = re.search(r"^kernel_config:\s*(\S+)", text, re.M)
     if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash(sources):
+        return None
+    if config is not None and m_cfg is not None and m_cfg.group(1) != config:
         return None
     return float(m_bytes.group(1))
 
@@ -512,7 +516,10 @@ def main():
     avg_launch_ms = float(np.mean(step_ms))
     step_flops = 2.0 * step_shape[0] * step_shape[1] * step_shape[2]
     achieved_tflops = step_flops / (avg_launch_ms * 1e-3) / 1e12
-    traffic = None if host else measured_traffic(args.workload, tc)
+    kcfg = (g.sgemm_tc_get_config(tc, w.M, w.N, w.K).as_tuple()[:5] if tc is not None else
+            g.sgemm_get_config(*step_shape, w.lda, w.ldb, w.ldc).as_tuple())
+    traffic = None if host else measured_traffic(args.workload, args.tc,
+                                                 "x".join(str(v) for v in kcfg))
     peak = PEAK_FP32_MFMA_TFLOPS if tc is None else PEAK_F16_MFMA_TFLOPS
 
     dev_peak = device_fp32_matrix_peak() if tc is None else None

@@ -139,7 +139,7 @@ int sgemm_init_leaf(int64_t M, int64_t N, float beta, float* C, int64_t ldc,
  * here, then the environment variable SGEMM_FORCE_CFG="BMxBNxBKxWMxWN" (read
  * once per process; ignored with a message on stderr when malformed or not
  * compiled), then a tuned config for the exact shape, then the default:
- * among the 256x256x32 (2x2 waves), 256x128x16 (4x2), 128x128x32 (2x2) and
+ * among the 256x256x32 (4x2 waves), 256x128x16 (4x2), 128x128x32 (2x2) and
  * single-wave 32x32 tiles (32 deep while a CU holds at most nine of them,
  * else 16 deep; 16 deep whenever K <= 16), the one with the least estimated
  * time on 256 CUs of 4 SIMDs: with T tiles the busiest CU holds

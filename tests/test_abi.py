@@ -146,10 +146,10 @@ def test_get_config_checks():
     ((2560, 2560, 2560), (256, 128, 16, 4, 2)),
     ((8192, 8192, 1024), (256, 128, 16, 4, 2)),
     # the five workloads' shapes and the super-tiled step leaf
-    ((4096, 4096, 4096), (256, 256, 32, 2, 2)),
-    ((65536, 512, 4096), (256, 256, 32, 2, 2)),
+    ((4096, 4096, 4096), (256, 256, 32, 4, 2)),
+    ((65536, 512, 4096), (256, 256, 32, 4, 2)),
     ((5003, 3001, 2047), (256, 128, 16, 4, 2)),
-    ((16384, 16384, 16384), (256, 256, 32, 2, 2)),
+    ((16384, 16384, 16384), (256, 256, 32, 4, 2)),
 ])
 def test_default_config_picks(shape, want):
     """The built-in choice at the boundaries of its rule, fixed on the CPU."""

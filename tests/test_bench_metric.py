@@ -85,3 +85,13 @@ def test_clock_sampler_reads_the_marked_level(tmp_path):
     with empty:
         pass
     assert empty.summary() is None
+
+
+def test_traffic_only_for_the_counted_tile(tmp_path, monkeypatch):
+    f = tmp_path / "traffic.txt"
+    f.write_text("hbm_bytes_per_launch: 99\nkernel_config: 256x256x32x4x2\n"
+                 "kernel_source_sha256_16: %s\n" % bench.kernel_source_hash())
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
+    assert bench.measured_traffic(bench.DEFAULT_WORKLOAD, config="256x256x32x4x2") == 99.0
+    assert bench.measured_traffic(bench.DEFAULT_WORKLOAD, config="256x256x32x2x2") is None
+    assert bench.measured_traffic(bench.DEFAULT_WORKLOAD) == 99.0

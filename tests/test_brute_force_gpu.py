@@ -52,11 +52,11 @@ def _all_cfgs():
 
 
 def test_brute_force_default_tile():
-    """The full set for the tile large shapes use (256x256x32 on 4 waves):
+    """The full set for the tile large shapes use (256x256x32 on 8 waves):
     M, N in 1..9, BM-1..BM+1, 2BM+-1 and K in 1..9, BK-1..BK+1, 2BK-1..2BK+1.
     K = BK and 2BK are whole chunks: with a tile inside N every chunk,
     the last one included, takes the direct loads."""
-    cfg = g.sgemm_config(256, 256, 32, 2, 2)
+    cfg = g.sgemm_config(256, 256, 32, 4, 2)
     bm, bn, bk = cfg.bm, cfg.bn, cfg.bk
     ms = list(range(1, 10)) + [bm - 1, bm, bm + 1, 2 * bm - 1, 2 * bm + 1]
     ns = list(range(1, 10)) + [bn - 1, bn, bn + 1, 2 * bn - 1, 2 * bn + 1]

@@ -44,7 +44,7 @@ int main(int argc, char** argv) {
     EXPECT(k > 0);
     for (i = 0; i < k; ++i) EXPECT(sgemm_config_at(i, &c) == SGEMM_OK && c.bm >= 32);
     EXPECT(sgemm_get_config(4096, 4096, 4096, 4096, 4096, 4096, &c) == SGEMM_OK);
-    EXPECT(c.bm == 256 && c.bn == 256 && c.bk == 32 && c.wm == 2 && c.wn == 2);
+    EXPECT(c.bm == 256 && c.bn == 256 && c.bk == 32 && c.wm == 4 && c.wn == 2);
     EXPECT(sgemm_tune_candidates(4096, 4096, 4096, cands, 64) > 0);
     /* the tuning cache: one entry in, the choice follows it, saved back out */
     f = fopen(cache, "w");
