@@ -400,32 +400,59 @@ __global__ __launch_bounds__(256) void tc_cast_rows_kernel(const float* A, int64
 // a row of B16, both 16 bytes per lane.  (64 x 64 tiles ran 12% slower at
 // 16384 x 16384; taller tiles or banded tile orders did not help either.)
 // The tile sits in LDS unpadded, as 16-byte pieces; piece q of row r is kept
-// at q ^ 2*((r >> 3) & 7).  A row is stored with one 16-byte write per lane,
-// each 16 lanes filling the 16 pieces of a 256-byte window; in a column read
-// (8 rows o..o+7 of one n per lane, o a multiple of 8, 8 n per wave) the 8
-// row groups take 8 different even offsets, so the wave's 64 lanes read 64
-// different 4-byte words modulo 256 bytes.
+// at q ^ ((r >> 3) & 7).  A column read (8 rows o..o+7 of one n per lane, o
+// a multiple of 8, 8 n per wave, 4-byte reads) is served 32 lanes at a time
+// from 32 banks of 4 bytes, as the counters show: the 32 lanes of a half
+// wave (rows 8m+i for m = 0..7, four consecutive n) then take 8 different
+// pieces mod 8 and 4 words of each, 32 different banks.  (The swizzle
+// 2*((r >> 3) & 7) gave 64 different words mod 256 bytes per wave but put
+// rows m and m ^ 4 of a half wave on the same banks: half of the read cycles
+// were conflicts.)  A tile wholly inside B (16-byte aligned rows, offsets in 32
+// bits) comes in by direct global-to-LDS loads: each wave's load fills 64
+// consecutive 16-byte slots, two rows, the swizzle applied to the global
+// address of each slot.  Edge tiles go through registers with bounds checks
+// and zero fill and are stored with one 16-byte write per lane.  (Stored
+// through registers, every tile spent a third of its LDS cycles in bank
+// conflicts on those writes, at 8 conflict cycles per 16-byte write of a
+// wave; the direct loads write no LDS through the LDS pipe.)
 template <int FMT, bool VEC>
 __global__ __launch_bounds__(256) void tc_cast_cols_kernel(const float* B, int64_t ldb, int K,
                                                            int N, uint16_t* out, int Np, int Kp) {
     using F = TcFmt<FMT>;
     constexpr int TK = 64, TN = 128;
     constexpr int LPR = TN / 4, RPP = 256 / LPR, UPR = TK / 8;   // lanes per row, rows per pass
+    constexpr int DL = TK * LPR / 256;                           // direct loads per wave
     static_assert(kTcPadMN % TN == 0 && kTcPadK % TK == 0, "whole tiles of the padded B16");
-    __shared__ f32x4 t[TK][TN / 4];
+    static_assert(DL * 256 == TK * LPR, "whole direct loads per wave");
+    __shared__ __attribute__((aligned(16))) f32x4 t[TK][TN / 4];
     const float* tf = reinterpret_cast<const float*>(&t[0][0]);
-    auto piece = [](int r, int q) { return q ^ (2 * ((r >> 3) & 7)); };
+    auto piece = [](int r, int q) { return q ^ ((r >> 3) & 7); };
     auto at = [&](int r, int n) { return tf[r * TN + 4 * piece(r, n >> 2) + (n & 3)]; };
     const int tn = Np / TN, tk = Kp / TK;
     const int64_t tiles = (int64_t)tn * tk;
+    const int wave = (int)threadIdx.x >> 6, lane = (int)threadIdx.x & 63;
+    const bool narrow = ((int64_t)(TK - 1) * ldb + TN) * 4 <= (int64_t)UINT32_MAX;
     for (int64_t b = blockIdx.x; b < tiles; b += gridDim.x) {
         const int n0 = (int)(b % tn) * TN, k0 = (int)(b / tn) * TK;
+        if (VEC && narrow && k0 + TK <= K && n0 + TN <= N) {
+            // slot u = (j*4 + wave)*64 + lane holds row u / LPR, stored piece
+            // u % LPR, i.e. logical piece (u % LPR) ^ swizzle(row)
+            const float* base = B + (int64_t)k0 * ldb + n0;
 #pragma unroll
-        for (int pass = 0; pass < TK / RPP; ++pass) {
-            const int kr = RPP * pass + (int)threadIdx.x / LPR, q = (int)threadIdx.x % LPR;
-            const int k = k0 + kr, n = n0 + 4 * q;
-            t[kr][piece(kr, q)] = (k < K) ? load4<VEC>(B + (int64_t)k * ldb + n, N - n)
-                                          : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            for (int j = 0; j < DL; ++j) {
+                const int u = (j * 4 + wave) * 64 + lane, r = u / LPR;
+                const uint32_t off = ((uint32_t)r * (uint32_t)ldb + 4u * (uint32_t)piece(r, u % LPR)) * 4u;
+                dma16s(base, off, reinterpret_cast<char*>(&t[0][0]) + (j * 4 + wave) * 1024);
+            }
+            __builtin_amdgcn_s_waitcnt(kWaitVm<0>);
+        } else {
+#pragma unroll
+            for (int pass = 0; pass < TK / RPP; ++pass) {
+                const int kr = RPP * pass + (int)threadIdx.x / LPR, q = (int)threadIdx.x % LPR;
+                const int k = k0 + kr, n = n0 + 4 * q;
+                t[kr][piece(kr, q)] = (k < K) ? load4<VEC>(B + (int64_t)k * ldb + n, N - n)
+                                              : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            }
         }
         __syncthreads();
 #pragma unroll
