@@ -481,9 +481,10 @@ def main():
         launches_per_step = 1
     # A pair of HIP events around a launch costs the stream about 10 us; on the
     # 64 launches of a super-tiled step that is 1% of the step.  The launches
-    # of a step are all alike, so one in TRACE_EVERY is traced (7, prime to
-    # the 4 K steps of a super-tile, so every K position is sampled).
-    every = TRACE_EVERY if launches_per_step > 1 else 1
+    # of such a step are all alike, so one in TRACE_EVERY is traced (7, prime
+    # to the 4 K steps of a super-tile, so every K position is sampled); steps
+    # of a few unlike launches (the 16-bit form's cast pass and GEMM) trace all.
+    every = TRACE_EVERY if launches_per_step >= 16 else 1
     # a step of one launch is timed by the step's own event pair, so the
     # library traces nothing then (a second pair per launch would only add
     # stream time)
