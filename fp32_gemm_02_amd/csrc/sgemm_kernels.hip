@@ -21,7 +21,11 @@
 //   - the A tile is stored row-major without padding, its 16-byte pieces
 //     XOR-swizzled within each row, so that the MFMA operand reads are free of
 //     LDS bank conflicts (the swizzle is applied to the global addresses of
-//     the direct loads, since those write LDS in lane order).
+//     the direct loads, since those write LDS in lane order);
+//   - with beta != 0, part of the C tile is loaded into LDS during the last
+//     K chunk, while the matrix cores still run, so that less of C is read
+//     in the burst at the end, when every workgroup of a launch reads and
+//     writes its tile at once.
 //
 // MFMA 32x32x2 f32 operand layout (one block, 64 lanes, l = lane):
 //   src A: lane l holds A'[l % 32][l / 32]      (32 x 2)
@@ -111,12 +115,30 @@ struct TileShape {
     static_assert(DA * 64 * NW == BM * QA && DB * 64 * NW == BK * QB,
                   "whole direct loads per wave");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS of one CU");
+    // C prefetch for beta != 0 (8-wave tiles whose waves write 4 consecutive
+    // columns per lane and hold at least 128 accumulators, so that one
+    // workgroup fills its CU whatever its LDS): during the last K chunk, rows
+    // of each wave's first 32-row block of C are loaded straight into LDS,
+    // CPF_FREE of them into the stage buffer that chunk leaves free and
+    // CPF_SPARE more into LDS beyond the ring; the epilogue takes them from
+    // there instead of from memory.  Every row is 1 KiB per wave: lane l
+    // holds its own 16 bytes at offset 16*l.
+    static constexpr bool CPF_OK = NB == 4 && NW == 8 && MB * NB * 16 >= 128;
+    static constexpr int CPF_ROW_BYTES = 64 * 16;
+    static constexpr int CPF_FREE =
+        CPF_OK ? (STAGE * 4 / (NW * CPF_ROW_BYTES) < 16 ? STAGE * 4 / (NW * CPF_ROW_BYTES) : 16) : 0;
+    static constexpr int CPF_SPARE_MAX = (160 * 1024 - LDS_BYTES) / (NW * CPF_ROW_BYTES);
+    static constexpr int CPF_SPARE =
+        CPF_OK ? (CPF_SPARE_MAX < 16 - CPF_FREE ? CPF_SPARE_MAX : 16 - CPF_FREE) : 0;
+    static constexpr int CPF = CPF_FREE + CPF_SPARE;   // prefetched rows per lane, <= 16
+    static constexpr int SMEM_FLOATS = NS * STAGE + CPF_SPARE * NW * CPF_ROW_BYTES / 4;
+    static_assert(SMEM_FLOATS * 4 <= 160 * 1024, "LDS of one CU");
 };
 
 template <int BM, int BN, int BK, int WM, int WN, bool VEC>
 __global__ __launch_bounds__(64 * WM * WN) void sgemm_mfma_kernel(GemmArgs p) {
     using T = TileShape<BM, BN, BK, WM, WN>;
-    __shared__ __attribute__((aligned(16))) float smem[T::NS * T::STAGE];
+    __shared__ __attribute__((aligned(16))) float smem[T::SMEM_FLOATS];
 
     int tm, tn;
     tile_of(p, tm, tn);
@@ -320,10 +342,22 @@ __global__ __launch_bounds__(64 * WM * WN) void sgemm_mfma_kernel(GemmArgs p) {
     // barrier.  Every chunk loads directly except, on a tile at the N edge or
     // when K is not a whole number of chunks, the last one, which holds row
     // K-1 of B: that one comes through registers with bounds checks.
+    // C prefetch: whole tile, beta != 0, every chunk direct, and the lane
+    // offsets of four rows of C fit in 32 bits.
+    const bool whole = VEC && m0 + BM <= p.M && n_inside;
+    const uint32_t c_off = (uint32_t)((4 * h * p.ldc + 4 * l32) * 4);
+    auto cpf_dst = [&](int nb, int r) -> float* {
+        if (r < T::CPF_FREE) return smem + nb * T::STAGE + (wave * T::CPF_FREE + r) * 256;
+        return smem + NS * T::STAGE + (wave * T::CPF_SPARE + (r - T::CPF_FREE)) * 256;
+    };
+    int cpf_buf = 0;
     constexpr int MFMAS = T::MB * T::NB;                // MFMAs per k-step
     constexpr int DMA_AT = (MFMAS >= 10) ? 6 : MFMAS - DMA_PER_STEP;
     const bool reg_last = !n_inside || p.K % BK != 0;
     const int nk_direct = reg_last ? (p.K - 1) / BK : p.K / BK;   // chunks loaded directly
+    const bool cpf = T::CPF > 0 && whole && p.beta != 0.0f && !reg_last && narrow &&
+                     (4 * p.ldc + 4 * 32) * 4 <= (int64_t)UINT32_MAX;
+    bool cpf_done = false;
     bool done = false;
     if constexpr (NS == 2 && T::MB + 2 <= MFMAS && DMA_AT >= 0) {
         if (VEC && narrow && nk_direct >= 1) {
@@ -336,10 +370,20 @@ __global__ __launch_bounds__(64 * WM * WN) void sgemm_mfma_kernel(GemmArgs p) {
             read_a(smem, 0, fa[0]);
             fb[0] = read_b(smem, 0);
             int cur = 0;
+            // Prefetch load r (0 .. CPF-1) of C: the lane's row r of its
+            // wave's first 32-row block (what the epilogue reads as cv[r]),
+            // into the free stage buffer nb (r < CPF_FREE) or beyond the
+            // ring.  The whole tile lies inside C, so every address is.
+            auto load_c_one = [&](int nb, int r) {
+                const float* row = p.C + (int64_t)(m0 + wm * T::TWM + 8 * (r >> 2) + (r & 3)) * p.ldc +
+                                   n0 + wn * T::TWN;
+                dma16s(row, c_off, cpf_dst(nb, r));
+            };
             // One stage: the k-steps of chunk kt from buffer cur, while chunk
             // kt+1 is loaded directly into the other buffer (NEXT 1; 0: no
-            // next chunk here); at the last k-step, the barrier and the first
-            // reads of chunk kt+1.
+            // next chunk here, and with the C prefetch its rows are loaded
+            // into the other buffer instead); at the last k-step, the barrier
+            // and the first reads of chunk kt+1.
             auto stage = [&](int kt, auto next_tag) {
                 constexpr int NEXT = decltype(next_tag)::value;
                 const float* base = smem + cur * T::STAGE;
@@ -359,7 +403,7 @@ __global__ __launch_bounds__(64 * WM * WN) void sgemm_mfma_kernel(GemmArgs p) {
                             if (m == 0) fb[(kk + 1) & 1] = read_b(base, kk + 1);
                             if ((kk + 1) % 4 == 0 && m >= 1 && m <= T::MB)
                                 read_a_one(base, (kk + 1) / 4, fa[((kk + 1) / 4) & 1], m - 1);
-                        } else if (NEXT != 0) {
+                        } else if (NEXT == 1) {
                             // chunk kt+1 has landed (and its register-path
                             // stores are done) everywhere, and every wave has
                             // read chunk kt's buffer for the last time (its
@@ -375,6 +419,10 @@ __global__ __launch_bounds__(64 * WM * WN) void sgemm_mfma_kernel(GemmArgs p) {
                             const int j = kk * DMA_PER_STEP + (m - DMA_AT);
                             if (j < DIRECT_LOADS) load_direct_one(lk0, nb, j);
                         }
+                        if (NEXT == 0 && m >= DMA_AT && m < DMA_AT + DMA_PER_STEP) {
+                            const int r = kk * DMA_PER_STEP + (m - DMA_AT);
+                            if (r < T::CPF && cpf) load_c_one(nb, r);
+                        }
                         __builtin_amdgcn_sched_barrier(0);
                     }
                 }
@@ -383,6 +431,7 @@ __global__ __launch_bounds__(64 * WM * WN) void sgemm_mfma_kernel(GemmArgs p) {
             using Direct = std::integral_constant<int, 1>;
             using Last = std::integral_constant<int, 0>;
             for (int kt = 0; kt + 1 < nk_direct; ++kt) stage(kt, Direct{});
+            cpf_buf = cur ^ 1;
             stage(nk_direct - 1, Last{});
             if (reg_last) {
                 // The last chunk through registers, into the buffer chunk
@@ -396,6 +445,7 @@ __global__ __launch_bounds__(64 * WM * WN) void sgemm_mfma_kernel(GemmArgs p) {
                 fb[0] = read_b(smem + cur * T::STAGE, 0);
                 stage(nk_direct, Last{});
             }
+            cpf_done = cpf;
             done = true;
         }
     }
@@ -450,18 +500,29 @@ __global__ __launch_bounds__(64 * WM * WN) void sgemm_mfma_kernel(GemmArgs p) {
     const int col = n0 + wn * T::TWN + T::NB * l32;
     const int ncols = p.N - col;
     using CV = typename BVec<T::NB>::type;
-    if (VEC && m0 + BM <= p.M && n_inside) {
+    if (whole) {
         // Whole tile inside C: the 16 rows of a 32-row block are read before
         // any is written, so a lane waits for one memory round trip per block
-        // rather than one per row.
+        // rather than one per row.  With the C prefetch, the first CPF rows
+        // of block 0 come from LDS, where the wave's own loads put them
+        // during the last chunk (its vmcnt wait covers those loads).
 #pragma unroll
         for (int i = 0; i < T::MB; ++i) {
             float* base = p.C + (int64_t)(m0 + wm * T::TWM + i * 32 + 4 * h) * p.ldc + col;
             auto row_ptr = [&](int r) { return base + (int64_t)(8 * (r >> 2) + (r & 3)) * p.ldc; };
             CV cv[16];
             if (beta != 0.0f) {
+                if (i == 0 && T::CPF > 0 && cpf_done) {
+                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
-                for (int r = 0; r < 16; ++r) cv[r] = *reinterpret_cast<const CV*>(row_ptr(r));
+                    for (int r = 0; r < T::CPF; ++r)
+                        cv[r] = *reinterpret_cast<const CV*>(cpf_dst(cpf_buf, r) + 4 * lane);
+                } else {
+#pragma unroll
+                    for (int r = 0; r < T::CPF; ++r) cv[r] = *reinterpret_cast<const CV*>(row_ptr(r));
+                }
+#pragma unroll
+                for (int r = T::CPF; r < 16; ++r) cv[r] = *reinterpret_cast<const CV*>(row_ptr(r));
             }
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -533,7 +594,7 @@ hipError_t launch_gemm(const GemmArgs& p, hipStream_t stream) {
 
 #define PHOBOS_CFG(BM, BN, BK, WM, WN)                                                  \
     KernelEntry{sgemm_config{BM, BN, BK, WM, WN}, 64 * WM * WN,                        \
-                TileShape<BM, BN, BK, WM, WN>::LDS_BYTES,                               \
+                TileShape<BM, BN, BK, WM, WN>::SMEM_FLOATS * 4,                         \
                 &launch_gemm<BM, BN, BK, WM, WN, true>,                                 \
                 &launch_gemm<BM, BN, BK, WM, WN, false>}
 
