@@ -17,7 +17,7 @@ and at least 1 s has passed (the count is reported).
 Printed: one JSON line with the metric (GFLOP/s = 2*M*N*K / time per step),
 the roofline of the dominant kernel (the step leaf; its duration per launch
 from HIP events the library records on the launch stream during the timed
-region, around one launch in seven) and the CPU oracle's rate on a bounded
+region, around one launch in 31) and the CPU oracle's rate on a bounded
 slab of the same product.  The shader clock is sampled from the driver's
 sysfs clock table by a host thread during the timed region.
 The timed region records one more event after each step, so the config also
@@ -63,7 +63,7 @@ HIP_ATTR_MULTIPROCESSOR_COUNT = 63
 PEAK_HBM_GBS = 8000.0             # MI355X published HBM3E bandwidth
 PEAK_F16_MFMA_TFLOPS = 2500.0     # MI355X published dense fp16 / bf16 matrix peak
 DEFAULT_WORKLOAD = "supertiled_16384_t4096"
-TRACE_EVERY = 7
+TRACE_EVERY = 31
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sgemm_step_4096_ld16384.txt")
 TC_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "tc16_gemm_f16_16384_counters.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "fp32_gemm_02_amd", "csrc", f)
@@ -467,6 +467,20 @@ def main():
             g.sgemm(w.M, w.N, w.K, w.alpha, dA, w.lda, dB, w.ldb, w.beta, dC, w.ldc,
                     stream=stream)
 
+    restore = None
+    if w.beta != 0:
+        # every timed step starts from the initial C (restored outside the
+        # step's events); the copy lives on the device, or in host memory for
+        # the host-resident form.  It is made before the warm-up: a step that
+        # followed the 1 GiB allocation at once ran 2% slower than the rest.
+        with torch.cuda.stream(stream):
+            c0 = dC.clone()
+        stream.synchronize()
+
+        def restore():
+            with torch.cuda.stream(stream):
+                dC.copy_(c0, non_blocking=not host)
+
     tuned = None
     if args.tune and tc is None:
         tuned, _ = g.sgemm_tune(*step_shape, w.lda, w.ldb, w.ldc, reps=10, stream=stream)
@@ -479,26 +493,18 @@ def main():
         launches_per_step = 1 + g.sgemm_tc_get_config(tc, w.M, w.N, w.K).staged   # cast pass
     else:
         launches_per_step = 1
-    # A pair of HIP events around a launch costs the stream about 10 us; on the
-    # 64 launches of a super-tiled step that is 1% of the step.  The launches
-    # of such a step are all alike, so one in TRACE_EVERY is traced (7, prime
-    # to the 4 K steps of a super-tile, so every K position is sampled); steps
-    # of a few unlike launches (the 16-bit form's cast pass and GEMM) trace all.
+    # A pair of the library's trace events around a launch costs the stream
+    # about 4.5 us (timing-only events, no system-scope fence); on the 64
+    # launches of a super-tiled step, tracing each costs 0.5% of the step and
+    # one in seven 0.1%.  The launches of such a step are all alike, so one in
+    # TRACE_EVERY is traced (31, prime to the 4 K steps of a super-tile, so
+    # every K position is sampled: 41 launches over 20 steps); steps of a few
+    # unlike launches (the 16-bit form's cast pass and GEMM) trace all.
     every = TRACE_EVERY if launches_per_step >= 16 else 1
     # a step of one launch is timed by the step's own event pair, so the
     # library traces nothing then (a second pair per launch would only add
     # stream time)
     single = launches_per_step == 1 and tc is None and not host
-    restore = None
-    if w.beta != 0:
-        # every timed step starts from the initial C (restored outside the
-        # step's events); the copy lives on the device, or in pinned memory
-        # for the host-resident form
-        c0 = dC.clone()
-
-        def restore():
-            with torch.cuda.stream(stream):
-                dC.copy_(c0, non_blocking=not host)
     cap = args.steps * launches_per_step * 2 + 16
     if not single:
         g.sgemm_trace_begin(cap, every=every)
@@ -595,6 +601,7 @@ def main():
     print(f"# timed {args.steps} steps: {ms_total:.2f} ms on the stream ({wall * 1e3:.2f} ms "
           f"wall, C restores included); {traced}, mean {avg_launch_ms:.4f} ms", file=sys.stderr,
           flush=True)
+    print("# step times (ms): " + " ".join(f"{t:.3f}" for t in per_step), file=sys.stderr, flush=True)
     print(json.dumps(out), flush=True)
 
 

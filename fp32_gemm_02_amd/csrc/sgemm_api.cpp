@@ -353,8 +353,11 @@ struct TraceScope {
         if (g_trace_seen++ % g_trace_every != 0) return;
         if ((int64_t)g_trace.size() >= g_trace_cap) return;
         TraceRec r{};
-        if (hipEventCreate(&r.start) != hipSuccess) return;
-        if (hipEventCreate(&r.stop) != hipSuccess) {
+        // Timing-only events: no system-scope fence (cache writeback and
+        // invalidate) when they are recorded, so the traced launch and the
+        // ones after it run as they would untraced.
+        if (hipEventCreateWithFlags(&r.start, hipEventDisableSystemFence) != hipSuccess) return;
+        if (hipEventCreateWithFlags(&r.stop, hipEventDisableSystemFence) != hipSuccess) {
             (void)hipEventDestroy(r.start);
             return;
         }

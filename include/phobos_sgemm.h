@@ -420,7 +420,9 @@ int sgemm_supertiled_host(int64_t M, int64_t N, int64_t K, float alpha,
  * Launch trace.  Between sgemm_trace_begin(capacity) and sgemm_trace_end,
  * every kernel the library enqueues is bracketed by a pair of HIP events
  * recorded on the launch's own stream (up to `capacity` launches; later ones
- * are not traced).  sgemm_trace_end waits for those events, writes each
+ * are not traced).  The events are for timing only: they are created without
+ * the system-scope fence (hipEventDisableSystemFence), so recording them
+ * writes back and invalidates no cache.  sgemm_trace_end waits for those events, writes each
  * launch's duration in milliseconds to ms_out[i] and its kind to kind_out[i]
  * (SGEMM_KIND_*), for i < min(count, cap), stores the count in *n_out and
  * frees the events.  Arguments of begin: 1 capacity (>= 1).  Of end:
