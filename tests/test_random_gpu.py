@@ -49,6 +49,42 @@ def test_random_sgemm_and_supertiled(seed):
         gu.check_full(w, x, out, steps=steps, exact=integer, relaxed=not integer)
 
 
+def test_random_whole_tiles_with_c_prefetch():
+    """Shapes where the 8-wave 256x256 tiles take their C prefetch: beta != 0,
+    16-byte aligned operands, K a whole number of chunks, so every tile wholly
+    inside C loads 12 (BK = 32) or all 16 (BK = 16) of its lanes' rows of a
+    32-row block of C into LDS during the last chunk.  Edge tiles of the same
+    launches take the plain epilogue beside them.  The super-tiled walk runs
+    the same leaves with beta = 1 on its step launches."""
+    rng = np.random.default_rng(5)
+    for i in range(40):
+        cfg = [(256, 256, 32, 4, 2), (256, 256, 16, 4, 2)][i % 2]
+        bk = cfg[2]
+        M, N = (int(rng.integers(256, 1100)) for _ in range(2))
+        K = bk * int(rng.integers(1, 48))
+        lda, ldb, ldc = (-(-v // 4) * 4 + 4 * int(rng.choice([0, 0, 1, 5])) for v in (K, N, N))
+        alpha = float(rng.choice([1.0, -1.0, 0.5, 1.5]))
+        beta = float(rng.choice([1.0, 0.5, -0.25, 2.0]))
+        integer = bool(rng.integers(0, 2))
+        supertiled = rng.integers(0, 3) == 0
+        tiles = ((int(rng.integers(256, 700)), int(rng.integers(256, 700)),
+                  bk * int(rng.integers(1, 20))) if supertiled else (None,) * 3)
+        c = "I7" if integer else "U"
+        w = wl.custom(M, N, K, alpha, beta, (c, c, c), seed=9000 + i, lda=lda, ldb=ldb, ldc=ldc,
+                      entry="sgemm_supertiled" if supertiled else "sgemm", TM=tiles[0],
+                      TN=tiles[1], TK=tiles[2], name=f"random_cpf_{i}")
+        print(f"case {i}: {w.entry} {M}x{N}x{K} ld {lda},{ldb},{ldc} alpha {alpha} beta {beta} "
+              f"tiles {tiles} cfg {cfg}", flush=True)
+        g.sgemm_set_config(cfg)
+        try:
+            x = wl.make_inputs(w)
+            out = gu.run(w, x)
+        finally:
+            g.sgemm_set_config(None)
+        steps = -(-K // min(tiles[2], K)) if supertiled else 1
+        gu.check_full(w, x, out, steps=steps, exact=integer, relaxed=not integer)
+
+
 def test_random_matrix_core_variant():
     rng = np.random.default_rng(3)
     for i in range(60):
