@@ -9,10 +9,10 @@
 // Query rows come in super-tiles of br rows (the pages' @cluster row block;
 // br = Nq for the monolithic form), each worked by ceil(br/64) workgroups of
 // one launch.  One workgroup owns 64 query rows of its super-tile, 16 per
-// query group; each group has two waves that take alternate blocks of 64
-// keys (the workgroup stages 128 keys of K and V per step in rings of LDS
-// stages, loaded one step ahead by direct global-to-LDS loads) and merge
-// their running statistics at the end.  Both products run on the FP32 matrix cores
+// query group; the workgroup stages 128 keys of K and V per step in rings of
+// LDS stages, loaded ahead by direct global-to-LDS loads, and each group has
+// four waves that take a quarter of each step's keys (two waves and halves
+// on the register path) and merge their running statistics at the end.  Both products run on the FP32 matrix cores
 // (v_mfma_f32_16x16x4_f32, lane layout checked on the GPU with an in-bounds
 // probe; l = lane, g = l / 16, q = l % 16):
 //   src A: lane l holds A'[q][g]   (16 x 4)
@@ -37,16 +37,19 @@
 #include "sgemm_device.h"
 #include "sgemm_internal.h"
 
+// Waves per query group on the direct-load path (2 or 4).
+#ifndef PHOBOS_ATT_KSPLIT
+#define PHOBOS_ATT_KSPLIT 4
+#endif
+
 namespace phobos {
 
 namespace {
 
 constexpr int kD = 64;      // head dimension
 constexpr int kBQ = 64;     // query rows per workgroup (16 per wave)
-constexpr int kBC = 64;     // keys per block
+constexpr int kKI = 128;    // keys per step of the key loop
 constexpr int kRowB = kD * 4;                      // bytes of one K or V row in LDS
-constexpr int kTile = kBC * kRowB;                 // bytes of one K or V tile
-constexpr int kStage = 2 * kTile;                  // K and V
 constexpr float kLog2e = 1.4426950408889634f;
 
 // K rows are stored with their 16-byte pieces XOR-swizzled by row.  The LDS
@@ -76,13 +79,15 @@ __device__ __forceinline__ float quad_sum(float x) {
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// KSPLIT = 2: two waves per group of 16 queries, each taking every other
-// block of 64 keys (128 keys per step), two waves per SIMD in all; their
-// running (maximum, weight sum, weighted sum) are merged at the end.
+// KSPLIT waves per group of 16 queries, each taking its own 128/KSPLIT keys
+// of every step of 128 (KSPLIT waves per SIMD in all); their running
+// (maximum, weight sum, weighted sum) are merged at the end.  With four
+// waves per SIMD instead of two (and 97 instead of 169 registers), one
+// wave's softmax overlaps the others' MFMAs better: 0.5% faster.
 //
-// With direct loads, K and V have rings of two LDS stages, and each wave
-// forms the scores of the next step before the softmax of the current one
-// (see the loop).  With the register path, K has two stages and V three: K
+// With direct loads, K has a ring of three LDS stages and V of two, and
+// each wave forms the scores of the next step before the softmax of the
+// current one (see the loop).  With the register path, K has two stages and V three: K
 // stage it & 1 and V stage it % 3 hold the rows of step it while those of
 // step it+1 are in flight.  The two waves of a query group share a SIMD
 // (waves w and w+4), and the barrier that ends each step would keep them in
@@ -94,16 +99,21 @@ __device__ __forceinline__ float quad_sum(float x) {
 template <bool VEC, bool DMA, int KSPLIT>
 __global__ __launch_bounds__(256 * KSPLIT) void attention_kernel(AttnArgs p) {
     constexpr int NT = 256 * KSPLIT;           // threads
-    constexpr int KI = kBC * KSPLIT;           // keys per step
+    constexpr int KI = kKI;                    // keys per step
+    constexpr int KW = KI / KSPLIT;            // keys per wave per step
+    constexpr int NSB = KW / 16;               // sub-blocks of 16 keys per wave
+    static_assert(KSPLIT == 2 || (KSPLIT == 4 && DMA), "key splits: 2, or 4 with direct loads");
     constexpr int TILE = KI * kRowB;           // bytes of the K (or V) rows of one step
     constexpr int LD = KI * 16 / NT;           // 16-byte pieces per thread per tensor
     static_assert(LD * NT == KI * 16, "whole pieces per thread");
     __shared__ __attribute__((aligned(16))) char lds[5 * TILE];
-    char* const kring = lds;                   // K stages 0, 1
-    char* const vring = lds + 2 * TILE;        // V stages 0, 1, 2
+    // direct loads: K stages 0, 1, 2 and V stages 0, 1; register path: K
+    // stages 0, 1 and V stages 0, 1, 2
+    char* const kring = lds;
+    char* const vring = lds + (DMA ? 3 : 2) * TILE;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int q = lane & 15, g = lane >> 4;
-    const int wq = wave & 3, half = wave >> 2;   // query group, key half
+    const int wq = wave & 3, half = wave >> 2;   // query group, key part
     // super-tile of this workgroup and its rows; one launch holds the leaves
     // of every super-tile
     const int st = blockIdx.x / p.blocks_per_tile, lb = blockIdx.x - st * p.blocks_per_tile;
@@ -191,27 +201,27 @@ __global__ __launch_bounds__(256 * KSPLIT) void attention_kernel(AttnArgs p) {
             *reinterpret_cast<f32x4*>(vs + (u >> 4) * kRowB + 16 * (u & 15)) = sv[i];
         }
     };
-    // S^T for this wave's 64 keys of a step (rows 64*half .. +63 of the
-    // stage), in 4 sub-blocks of 16: s[kb][r] = S[qrow][kbase + 16kb + r]
-    // The four sub-blocks' accumulations are interleaved, so that an MFMA
-    // never waits for the result of the one just before it.
+    // S^T for this wave's KW keys of a step (rows KW*half .. +KW-1 of the
+    // stage), in NSB sub-blocks of 16: s[kb][r] = S[qrow][kbase + 16kb + r]
+    // The sub-blocks' accumulations are interleaved, so that an MFMA never
+    // waits for the result of the one just before it.
     auto scores = [&](int buf, f32x4* s) {
-        const char* ks = kring + buf * TILE + half * (kBC * kRowB);
+        const char* ks = kring + buf * TILE + half * (KW * kRowB);
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int kb = 0; kb < NSB; ++kb) s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc) {
-            f32x4 a[4];
+            f32x4 a[NSB];
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
+            for (int kb = 0; kb < NSB; ++kb) {
                 const int krow = 16 * kb + q;             // A' row of this lane
-                // the swizzle of row 64*half + krow is that of krow (64 = 0 mod 16)
+                // the swizzle of row KW*half + krow is that of krow (KW = 0 mod 16)
                 a[kb] = *reinterpret_cast<const f32x4*>(ks + krow * kRowB + 16 * kswz(krow, 4 * g + cc));
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e)
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb)
+                for (int kb = 0; kb < NSB; ++kb)
                     s[kb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[kb][e], qv[4 * cc + e], s[kb], 0, 0, 0);
         }
     };
@@ -228,15 +238,15 @@ __global__ __launch_bounds__(256 * KSPLIT) void attention_kernel(AttnArgs p) {
         // last step can hold any)
         float bm = -INFINITY;
         if ((it + 1) * KI > p.Nk) {
-            const int kbase = it * KI + half * kBC + 4 * g;
+            const int kbase = it * KI + half * KW + 4 * g;
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
+            for (int kb = 0; kb < NSB; ++kb)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     if (kbase + 16 * kb + r >= p.Nk) s[kb][r] = -INFINITY;
         }
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < NSB; ++kb)
 #pragma unroll
             for (int r = 0; r < 4; ++r) bm = fmaxf(bm, s[kb][r]);
         bm = quad_max(bm);
@@ -247,7 +257,7 @@ __global__ __launch_bounds__(256 * KSPLIT) void attention_kernel(AttnArgs p) {
         m = mn;
         float bl = 0.0f;
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < NSB; ++kb)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const float w = __builtin_amdgcn_exp2f(s[kb][r] - base);
@@ -259,9 +269,9 @@ __global__ __launch_bounds__(256 * KSPLIT) void attention_kernel(AttnArgs p) {
         for (int db = 0; db < 4; ++db) o[db] *= alpha;
 
         // O^T += V^T P^T: step ts uses keys 16(ts/4) + 4g + ts%4 (lane group g)
-        const char* vs = vring + vstage * TILE + half * (kBC * kRowB);
+        const char* vs = vring + vstage * TILE + half * (KW * kRowB);
 #pragma unroll
-        for (int ts = 0; ts < 16; ++ts) {
+        for (int ts = 0; ts < 4 * NSB; ++ts) {
             const int vrow = 16 * (ts >> 2) + 4 * g + (ts & 3);
             const f32x4 a = *reinterpret_cast<const f32x4*>(vs + vrow * kRowB + 16 * q);
             const float w = s[ts >> 2][ts & 3];
@@ -273,30 +283,36 @@ __global__ __launch_bounds__(256 * KSPLIT) void attention_kernel(AttnArgs p) {
 
   if constexpr (DMA) {
     // Scores one step ahead: in step it the wave forms the scores of step
-    // it+1 (K stage (it+1) & 1) before the softmax and output products of
+    // it+1 (K stage (it+1) % 3) before the softmax and output products of
     // step it (V stage it & 1), so its exponentials of step it can overlap
-    // its own MFMAs.  K(it+2) and V(it+1) are loaded meanwhile.
+    // its own MFMAs.  K(it+2) and V(it+1) are loaded meanwhile.  K needs three
+    // stages: K(it+2) is issued at the start of step it, when K(it+1) is
+    // about to be read and a wave may still be reading K(it) (the scores of
+    // step 0 run before the loop, with no barrier after them).
     issue_dma(p.K, p.ldk, 0, kring, true);
     issue_dma(p.V, p.ldv, 0, vring, false);
     if (ni > 1) issue_dma(p.K, p.ldk, 1, kring + TILE, true);
     __builtin_amdgcn_s_waitcnt(kWaitVm<0>);
     __syncthreads();
-    f32x4 s[4];
+    f32x4 s[NSB];
     scores(0, s);
+    int k1 = 1, k2 = 2;                  // K stages of steps it+1 and it+2
     for (int it = 0; it < ni; ++it) {
-        // K stage it & 1 held K(it), read in step it-1; V stage (it+1) & 1
-        // held V(it-1), read in step it-1
-        if (it + 2 < ni) issue_dma(p.K, p.ldk, it + 2, kring + (it & 1) * TILE, true);
+        // K stage k2 held K(it-1), read in step it-2 (or never, for it = 0);
+        // V stage (it+1) & 1 held V(it-1), read in step it-1
+        if (it + 2 < ni) issue_dma(p.K, p.ldk, it + 2, kring + k2 * TILE, true);
         if (it + 1 < ni) issue_dma(p.V, p.ldv, it + 1, vring + ((it + 1) & 1) * TILE, false);
-        f32x4 sn[4];
+        f32x4 sn[NSB];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) sn[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (it + 1 < ni) scores((it + 1) & 1, sn);
+        for (int kb = 0; kb < NSB; ++kb) sn[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (it + 1 < ni) scores(k1, sn);
         consume(it, s, it & 1);
+        k1 = k2;
+        k2 = (k2 == 2) ? 0 : k2 + 1;
         __builtin_amdgcn_s_waitcnt(kWaitVm<0>);
         __syncthreads();
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) s[kb] = sn[kb];
+        for (int kb = 0; kb < NSB; ++kb) s[kb] = sn[kb];
     }
   } else {
     fetch(0);
@@ -304,11 +320,11 @@ __global__ __launch_bounds__(256 * KSPLIT) void attention_kernel(AttnArgs p) {
     store_v(0);
     __builtin_amdgcn_s_waitcnt(kWaitVm<0>);
     __syncthreads();
-    f32x4 s[4];
+    f32x4 s[NSB];
     for (int it = 0; it < ni; ++it) {
         const bool more = it + 1 < ni;
         if (more) fetch(it + 1);
-        if (KSPLIT == 1 || half == 0) {
+        if (half == 0) {
             scores(it & 1, s);
             consume(it, s, it % 3);
         } else {
@@ -326,15 +342,18 @@ __global__ __launch_bounds__(256 * KSPLIT) void attention_kernel(AttnArgs p) {
         __builtin_amdgcn_s_waitcnt(kWaitVm<0>);   // this wave's loads of step it+1
         __syncthreads();
     }
-    if (KSPLIT == 2 && half == 1) consume(ni - 1, s, (ni - 1) % 3);
+    if (half == 1) consume(ni - 1, s, (ni - 1) % 3);
   }
 
-    if constexpr (KSPLIT == 2) {
-        // merge the second key half into the first: both hold the same lanes'
-        // queries and output columns; the K ring is free after the last
-        // barrier (the second half's last output products read the V ring)
-        float* x = reinterpret_cast<float*>(lds) + (wq * 64 + lane) * 18;
-        if (half == 1) {
+    {
+        // merge the other key parts into the first: all hold the same lanes'
+        // queries and output columns; the K ring (2 * TILE bytes, room for
+        // 3 parts x 4 groups x 64 lanes x 18 floats) is free after the last
+        // barrier (the last output products read the V ring).  Parts are
+        // added in order 1, 2, 3, each rescaled to the larger maximum.
+        static_assert((KSPLIT - 1) * 4 * 64 * 18 * 4 <= 2 * TILE, "merge area in the K ring");
+        float* x = reinterpret_cast<float*>(lds) + (((half - 1) * 4 + wq) * 64 + lane) * 18;
+        if (half != 0) {
             x[0] = m;
             x[1] = l;
 #pragma unroll
@@ -343,14 +362,21 @@ __global__ __launch_bounds__(256 * KSPLIT) void attention_kernel(AttnArgs p) {
                 for (int r = 0; r < 4; ++r) x[2 + 4 * db + r] = o[db][r];
         }
         __syncthreads();
-        if (half == 1) return;
-        const float m2 = x[0], mm = fmaxf(m, m2);
-        const float f1 = __builtin_amdgcn_exp2f(m - mm), f2 = __builtin_amdgcn_exp2f(m2 - mm);
-        l = l * f1 + x[1] * f2;
+        if (half != 0) return;
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
+        for (int part = 1; part < KSPLIT; ++part) {
+            const float* y = reinterpret_cast<const float*>(lds) + (((part - 1) * 4 + wq) * 64 + lane) * 18;
+            const float m2 = y[0], mm = fmaxf(m, m2);
+            // a part that has met no key keeps weight 0 (not exp2(-inf + inf))
+            const float f1 = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - mm);
+            const float f2 = (m2 == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m2 - mm);
+            m = mm;
+            l = l * f1 + y[1] * f2;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) o[db][r] = o[db][r] * f1 + x[2 + 4 * db + r] * f2;
+            for (int db = 0; db < 4; ++db)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) o[db][r] = o[db][r] * f1 + y[2 + 4 * db + r] * f2;
+        }
     }
 
     // ---- epilogue: the weight sum over all keys, O = o / l ----
@@ -375,20 +401,22 @@ __global__ __launch_bounds__(256 * KSPLIT) void attention_kernel(AttnArgs p) {
 }  // namespace
 
 hipError_t launch_attention(const AttnArgs& p, bool vec, hipStream_t stream) {
-    // two waves per query group: at 16384 queries one 16-query wave per SIMD
-    // left latency exposed (87-92 TFLOP/s); two per SIMD reach 103-107
+    // KS waves per query group: at 16384 queries one 16-query wave per SIMD
+    // left latency exposed (87-92 TFLOP/s); two per SIMD reached 103-107
     constexpr int KS = 2;
+    constexpr int KS_DMA = PHOBOS_ATT_KSPLIT;
     const int64_t tiles = (p.Nq + (int64_t)p.br - 1) / p.br;
-    const dim3 grid((unsigned)(tiles * p.blocks_per_tile)), block(256 * KS);
+    const dim3 grid((unsigned)(tiles * p.blocks_per_tile));
     // direct loads when 32-bit byte offsets cover the rows of one step of K
     // and of V, and the rows are 16-byte aligned
-    const int64_t span = ((int64_t)(kBC * KS - 1) * std::max(p.ldk, p.ldv) + kD) * 4;
+    const int64_t span = ((int64_t)(kKI - 1) * std::max(p.ldk, p.ldv) + kD) * 4;
     if (vec && span <= (int64_t)UINT32_MAX)
-        hipLaunchKernelGGL((attention_kernel<true, true, KS>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((attention_kernel<true, true, KS_DMA>), grid, dim3(256 * KS_DMA), 0,
+                           stream, p);
     else if (vec)
-        hipLaunchKernelGGL((attention_kernel<true, false, KS>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((attention_kernel<true, false, KS>), grid, dim3(256 * KS), 0, stream, p);
     else
-        hipLaunchKernelGGL((attention_kernel<false, false, KS>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((attention_kernel<false, false, KS>), grid, dim3(256 * KS), 0, stream, p);
     return hipGetLastError();
 }
 
