@@ -145,6 +145,9 @@ __attribute__((format(printf, 1, 2))) void log_line(const char* fmt, ...) {
 // 256x256 tile runs on 8 waves (4 x 2, two per SIMD): against 4 waves it
 // measured 0.3% faster on the super-tiled 16384^3 walk, 4096^3 and the
 // tall-skinny product alike (five alternating runs, no overlap).
+// A split-K entry: the 32 x 32 tile with more waves than its one block.
+bool is_splitk(const sgemm_config& c) { return c.bm == 32 && c.bn == 32 && c.wm * c.wn > 1; }
+
 int default_entry(int64_t M, int64_t N, int64_t K) {
     struct Pick { int bm, bn, bk, wm, wn; double rate; };
     constexpr int64_t kCUs = 256;
@@ -174,6 +177,22 @@ int default_entry(int64_t M, int64_t N, int64_t K) {
         }
     }
     const Pick& p = picks[best];
+    if (p.bm == 32) {
+        // Split-K inside the workgroup where single-wave 32x32 tiles leave
+        // SIMDs idle or wait out their loads alone (a sweep of 40 shapes up to
+        // 3072^3 on one box: with it the built-in choice is within 3.3% of the
+        // fastest entry on every shape, 0.5% on average): eight waves per tile
+        // for at most 512 tiles or K of 16384 and more, else four waves of
+        // 16-deep chunks.
+        // Not where exactly two single-wave tiles per SIMD run already and K
+        // is short (1024 x 2048 x 1024: 101.8 against 95.2 TFLOP/s).
+        const int64_t tiles = ((M + 31) / 32) * ((N + 31) / 32);
+        const bool two_per_simd = tiles % 1024 == 0 && tiles >= 2048 && K < 4096;
+        if (K >= 512 && tiles <= 2560 && !two_per_simd)
+            return find_entry(tiles <= 512 || K >= 16384 ? sgemm_config{32, 32, 32, 4, 2}
+                                                         : sgemm_config{32, 32, 16, 2, 2});
+        if (K >= 64 && K < 512 && tiles <= 576) return find_entry({32, 32, 16, 2, 2});
+    }
     return find_entry({p.bm, p.bn, (p.bm == 32 && K <= 16) ? 16 : p.bk, p.wm, p.wn});
 }
 
@@ -989,6 +1008,8 @@ int sgemm_tune_candidates(int64_t M, int64_t N, int64_t K, sgemm_config* out, in
         // no tile larger than the problem needs
         if (c.bm > mneed || c.bn > nneed) continue;
         if (kKernelTable[i].lds_bytes > 160 * 1024) continue;
+        // a split-K entry only where every wave gets a chunk of K
+        if (is_splitk(c) && (K + c.bk - 1) / c.bk < (int64_t)c.wm * c.wn) continue;
         if (n < cap) out[n] = c;
         ++n;
     }

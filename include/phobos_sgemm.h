@@ -74,6 +74,10 @@ extern "C" {
  * wm x wn wavefronts of 64 lanes (workgroup = 64*wm*wn threads).  These are
  * the TILE_M / TILE_N / TILE_K of the pages' @autotune attribute ("Show HN:
  * Phobos", sections "Introducing the Phobos Language" and "Runtime").
+ * A 32x32 tile with more than one wave (wm*wn = 4 or 8) is a split-K entry:
+ * its waves share the one 32x32 block of C, each taking every (wm*wn)-th
+ * chunk of bk of K, and their partial sums are added in wave order before
+ * the store (a fixed order, so results repeat bit for bit).
  */
 typedef struct sgemm_config {
     int32_t bm, bn, bk, wm, wn;
@@ -149,7 +153,11 @@ int sgemm_init_leaf(int64_t M, int64_t N, float beta, float* C, int64_t ldc,
  * resident one would hide, so the estimate is ceil(T/256) * bm * bn *
  * (K + [alone] * 64) / (rate * min(1, ceil(T/256) * waves / 4)), `rate`
  * being the tile's measured rate (1.00, 0.98, 0.90, and 0.60 / 0.70 for
- * 32x32 at depth 32 / 16).
+ * 32x32 at depth 32 / 16).  When that is a 32x32 tile, with T 32x32 tiles:
+ * for K >= 512 and T <= 2560 (except T a multiple of 1024 from 2048 on with
+ * K < 4096, where two single-wave tiles per SIMD already run) the split-K
+ * entry 32x32x32 on 4x2 waves if T <= 512 or K >= 16384, else 32x32x16 on
+ * 2x2 waves; for 64 <= K < 512 and T <= 576 the 32x32x16 2x2 entry.
  */
 int sgemm_config_count(void);
 int sgemm_config_at(int32_t index, sgemm_config* out);
@@ -170,7 +178,8 @@ int sgemm_set_config(const sgemm_config* cfg);
  * `cap`) the compiled configurations that survive pruning for this shape:
  * tile extents inside the @autotune ranges of the "@cluster" page's matmul
  * (TILE_M, TILE_N in [32, 256], TILE_K in [4, 32]) and no tile larger than the
- * problem needs (bm <= max(32, roundup32(M)), bn <= max(32, roundup32(N))).
+ * problem needs (bm <= max(32, roundup32(M)), bn <= max(32, roundup32(N))),
+ * and split-K entries only when every wave gets a chunk (ceil(K/bk) >= wm*wn).
  * Returns the number of candidates, or a negative argument error
  * (1 M, 2 N, 3 K, 4 out, 5 cap).
  * sgemm_tune times the candidates on scratch buffers it allocates and frees

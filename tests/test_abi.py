@@ -95,6 +95,10 @@ def test_config_table_and_forcing():
     cfgs = g.configs()
     assert len(cfgs) >= 4
     for c in cfgs:
+        if c.bm == 32 and c.bn == 32 and c.wm * c.wn > 1:
+            # a split-K entry: more waves than the tile's one 32x32 block
+            assert c.wm * c.wn in (4, 8) and c.bk in (16, 32)
+            continue
         # each tile is whole 32x32 MFMA blocks per wave, B reads 1, 2 or 4 wide
         assert c.bm % (32 * c.wm) == 0 and c.bn % (32 * c.wn) == 0
         assert (c.bn // c.wn // 32) in (1, 2, 4)
@@ -124,12 +128,25 @@ def test_get_config_checks():
 
 
 @pytest.mark.parametrize("shape,want", [
-    # small products: only single-wave 32x32 tiles bring every SIMD work
-    ((256, 256, 256), (32, 32, 32, 1, 1)),
-    ((960, 960, 960), (32, 32, 32, 1, 1)),
-    ((1024, 1024, 1024), (32, 32, 32, 1, 1)),
-    ((960, 960, 16384), (32, 32, 32, 1, 1)),
-    ((1536, 1536, 1536), (32, 32, 32, 1, 1)),
+    # small products: 32x32 tiles, their K split over the waves of a
+    # workgroup: eight waves for at most 512 tiles or K of 16384 and more ...
+    ((512, 512, 512), (32, 32, 32, 4, 2)),
+    ((128, 128, 16384), (32, 32, 32, 4, 2)),
+    ((960, 960, 16384), (32, 32, 32, 4, 2)),
+    # ... four waves of 16-deep chunks up to 2560 tiles ...
+    ((256, 256, 256), (32, 32, 16, 2, 2)),
+    ((768, 768, 256), (32, 32, 16, 2, 2)),
+    ((960, 960, 960), (32, 32, 16, 2, 2)),
+    ((1024, 1024, 1024), (32, 32, 16, 2, 2)),
+    ((1536, 1536, 1536), (32, 32, 16, 2, 2)),
+    ((8192, 128, 2048), (32, 32, 16, 2, 2)),
+    # ... and one wave per tile with short K beyond 576 tiles, with 2048
+    # tiles (two per SIMD) and K below 4096, with K below 64, or beyond
+    # 2560 tiles
+    ((1024, 1024, 256), (32, 32, 32, 1, 1)),
+    ((1024, 2048, 1024), (32, 32, 32, 1, 1)),
+    ((1024, 2048, 4096), (32, 32, 16, 2, 2)),
+    ((256, 256, 40), (32, 32, 32, 1, 1)),
     # ... 16 deep when K fits one such chunk, or when a CU holds more than 9
     ((200, 200, 8), (32, 32, 16, 1, 1)),
     ((200, 200, 16), (32, 32, 16, 1, 1)),
