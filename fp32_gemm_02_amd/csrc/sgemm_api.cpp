@@ -161,11 +161,16 @@ int default_entry(int64_t M, int64_t N, int64_t K) {
         {256, 128, 16, 4, 2, 0.98},
         {128, 128, 32, 2, 2, 0.90},
         small_per_cu <= 9 ? Pick{32, 32, 32, 1, 1, 0.60} : Pick{32, 32, 16, 1, 1, 0.70},
+        {32, 32, 16, 2, 2, 0.79},   // split-K: four waves share each 32x32 tile
     };
     int best = 0;
     double best_est = 0.0;
     for (int i = 0; i < (int)(sizeof(picks) / sizeof(picks[0])); ++i) {
         const Pick& p = picks[i];
+        // split-K as an estimate only from K = 2048 on (below it, it lost to
+        // the tile the estimate picked otherwise at 1664^3, 1792^3 and
+        // 2560 x 2560 x 1024 by 1-2%)
+        if (p.wm * p.wn > 1 && p.bm == 32 && K < 2048) continue;
         const int64_t per = per_cu(p.bm, p.bn);
         const double occ = std::min(1.0, (double)(per * p.wm * p.wn) / 4.0);
         const bool alone = (p.bm == 256 && p.bn == 256) || per == 1;
@@ -183,17 +188,26 @@ int default_entry(int64_t M, int64_t N, int64_t K) {
         // 3072^3 on one box: with it the built-in choice is within 3.3% of the
         // fastest entry on every shape, 0.5% on average): eight waves per tile
         // for at most 512 tiles or K of 16384 and more, else four waves of
-        // 16-deep chunks.
-        // Not where exactly two single-wave tiles per SIMD run already and K
-        // is short (1024 x 2048 x 1024: 101.8 against 95.2 TFLOP/s).
+        // 16-deep chunks.  Not where exactly two single-wave tiles per SIMD run
+        // already and K is short (1024 x 2048 x 1024: 101.8 against 95.2
+        // TFLOP/s).  Beyond 2560 tiles the estimate above decides between four
+        // split-K waves (rate 0.79: 114-123 TFLOP/s from 2304^3 to 3584^3 and
+        // at 8192 deep, against 80-117 for the tiles picked before) and the
+        // other tiles.
         const int64_t tiles = ((M + 31) / 32) * ((N + 31) / 32);
         const bool two_per_simd = tiles % 1024 == 0 && tiles >= 2048 && K < 4096;
-        if (K >= 512 && tiles <= 2560 && !two_per_simd)
-            return find_entry(tiles <= 512 || K >= 16384 ? sgemm_config{32, 32, 32, 4, 2}
-                                                         : sgemm_config{32, 32, 16, 2, 2});
-        if (K >= 64 && K < 512 && tiles <= 576) return find_entry({32, 32, 16, 2, 2});
+        if (tiles <= 2560) {
+            if (K >= 512 && !two_per_simd)
+                return find_entry(tiles <= 512 || K >= 16384 ? sgemm_config{32, 32, 32, 4, 2}
+                                                             : sgemm_config{32, 32, 16, 2, 2});
+            if (K >= 64 && K < 512 && tiles <= 576) return find_entry({32, 32, 16, 2, 2});
+        } else if (p.wm * p.wn > 1) {
+            return find_entry({32, 32, 16, 2, 2});
+        }
+        // one wave per 32x32 tile
+        return find_entry({32, 32, K <= 16 ? 16 : picks[3].bk, 1, 1});
     }
-    return find_entry({p.bm, p.bn, (p.bm == 32 && K <= 16) ? 16 : p.bk, p.wm, p.wn});
+    return find_entry({p.bm, p.bn, p.bk, p.wm, p.wn});
 }
 
 // SGEMM_FORCE_CFG="BMxBNxBKxWMxWN" (e.g. 256x256x32x4x2) forces a compiled

@@ -153,11 +153,14 @@ int sgemm_init_leaf(int64_t M, int64_t N, float beta, float* C, int64_t ldc,
  * resident one would hide, so the estimate is ceil(T/256) * bm * bn *
  * (K + [alone] * 64) / (rate * min(1, ceil(T/256) * waves / 4)), `rate`
  * being the tile's measured rate (1.00, 0.98, 0.90, and 0.60 / 0.70 for
- * 32x32 at depth 32 / 16).  When that is a 32x32 tile, with T 32x32 tiles:
- * for K >= 512 and T <= 2560 (except T a multiple of 1024 from 2048 on with
- * K < 4096, where two single-wave tiles per SIMD already run) the split-K
- * entry 32x32x32 on 4x2 waves if T <= 512 or K >= 16384, else 32x32x16 on
- * 2x2 waves; for 64 <= K < 512 and T <= 576 the 32x32x16 2x2 entry.
+ * 32x32 at depth 32 / 16), and from K = 2048 on also the split-K entry
+ * 32x32x16 on 2x2 waves (4 waves per tile, rate 0.79).  When the least is a
+ * 32x32 tile, with T 32x32 tiles: for T <= 2560, K >= 512 (except T a
+ * multiple of 1024 from 2048 on with K < 4096, where two single-wave tiles
+ * per SIMD already run) the split-K entry 32x32x32 on 4x2 waves if T <= 512
+ * or K >= 16384, else 32x32x16 on 2x2 waves, and for 64 <= K < 512 with
+ * T <= 576 the 32x32x16 2x2 entry; for T > 2560 the split-K entry when the
+ * estimate picked it; otherwise one wave per tile.
  */
 int sgemm_config_count(void);
 int sgemm_config_at(int32_t index, sgemm_config* out);

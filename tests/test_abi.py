@@ -150,17 +150,23 @@ def test_get_config_checks():
     # ... 16 deep when K fits one such chunk, or when a CU holds more than 9
     ((200, 200, 8), (32, 32, 16, 1, 1)),
     ((200, 200, 16), (32, 32, 16, 1, 1)),
-    ((3072, 3072, 3072), (32, 32, 16, 1, 1)),
+    ((1664, 1664, 1664), (32, 32, 16, 1, 1)),
+    # beyond 2560 such tiles, from K = 2048 on, the estimate weighs split-K
+    # (four waves, rate 0.79) against the other tiles
+    ((2304, 2304, 2304), (32, 32, 16, 2, 2)),
+    ((3072, 3072, 3072), (32, 32, 16, 2, 2)),
+    ((3584, 3584, 3584), (32, 32, 16, 2, 2)),
+    ((2560, 2560, 2560), (32, 32, 16, 2, 2)),
+    ((1792, 1792, 8192), (32, 32, 16, 2, 2)),
     # one 128x128 tile per CU beats 13 small ones per CU, and 576 tiles of
     # 256x256 (2.25 rounds of 256 CUs) lose to 2304 of 128x128 (9 rounds)
     ((1792, 1792, 1792), (128, 128, 32, 2, 2)),
     ((2048, 2048, 2048), (128, 128, 32, 2, 2)),
     ((6144, 6144, 6144), (128, 128, 32, 2, 2)),
     ((8192, 512, 4096), (128, 128, 32, 2, 2)),
-    # 400 tiles of 256x256 (2 rounds) against 800 of 256x128 on 8 waves;
-    # with short K two resident 256x128 tiles per CU hide each other's
-    # fixed cost
-    ((2560, 2560, 2560), (256, 128, 16, 4, 2)),
+    # 100 tiles of 256x256 against 200 of 256x128 on 8 waves; with short K
+    # two resident 256x128 tiles per CU hide each other's fixed cost
+    ((2560, 2560, 1024), (256, 128, 16, 4, 2)),
     ((8192, 8192, 1024), (256, 128, 16, 4, 2)),
     # the five workloads' shapes and the super-tiled step leaf
     ((4096, 4096, 4096), (256, 256, 32, 4, 2)),
