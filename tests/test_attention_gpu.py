@@ -110,3 +110,14 @@ def test_attention_16384():
     gu.report("attention_16384", worst)
     st = run_attn(w, x, BR=w.BR)
     assert np.array_equal(logical_o(w, mono).view(np.int32), logical_o(w, st).view(np.int32))
+
+
+def test_attention_repeats_bit_for_bit():
+    """The four key parts of a query group are merged in a fixed order: two
+    calls give the same bits."""
+    w = wl.AttnWorkload("repeat", 700, 3000, 64, 0.125, ("N", "N", "N"), seed=77, ldq=64,
+                        ldk=64, ldv=64, ldo=64)
+    x = wl.make_attn_inputs(w)
+    first, second = run_attn(w, x), run_attn(w, x)
+    assert np.array_equal(first.view(np.int32), second.view(np.int32))
+    check_attn(w, x, first)

@@ -318,3 +318,26 @@ def test_subnormals_are_kept(cfg, a_val, b_val):
     ref, _ = gu.oracle.sgemm(M, N, K, 1.0, A, B, 0.0, np.zeros((M, N), np.float32))
     assert np.array_equal(out, ref)
     assert out[5, 5] == np.float32(2.0 ** -140) and out[5, 5] != 0
+
+
+@pytest.mark.parametrize("M,N,K,want", [
+    (512, 512, 2048, (32, 32, 32, 4, 2)),      # split K over eight waves
+    (1024, 1024, 1024, (32, 32, 16, 2, 2)),    # split K over four waves
+    (1024, 2048, 1024, (32, 32, 32, 1, 1)),    # one wave per tile
+    (1024, 1024, 4096, (32, 32, 16, 2, 2)),
+    (768, 1280, 1536, (32, 32, 16, 2, 2)),
+    (2048, 2048, 2048, (128, 128, 32, 2, 2)),
+    (4096, 4096, 4096, (256, 256, 32, 4, 2)),  # 256x256 tiles with the C prefetch
+])
+def test_results_repeat_bit_for_bit(M, N, K, want):
+    """The split-K entries add their waves' partial sums in a fixed order and
+    the C prefetch only moves where C is read from: two calls on the same
+    fractional inputs give the same bits, and the result is within the bound."""
+    w = wl.custom(M, N, K, 1.25, 0.75, ("U", "U", "U"), seed=M + N + K)
+    if want is not None:
+        assert g.sgemm_get_config(M, N, K, w.lda, w.ldb, w.ldc).as_tuple() == want
+    x = wl.make_inputs(w)
+    first = gu.run(w, x)
+    second = gu.run(w, x)
+    assert np.array_equal(first.view(np.int32), second.view(np.int32))
+    gu.check_full(w, x, first, relaxed=True)
