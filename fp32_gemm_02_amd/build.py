@@ -18,6 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libphobos_sgemm.so")
 SOURCES = [os.path.join(HERE, "csrc", "sgemm_kernels.hip"),
+           os.path.join(HERE, "csrc", "sgemm_splitk.hip"),
            os.path.join(HERE, "csrc", "sgemm_tc.hip"),
            os.path.join(HERE, "csrc", "attention.hip"),
            os.path.join(HERE, "csrc", "sgemm_api.cpp"),

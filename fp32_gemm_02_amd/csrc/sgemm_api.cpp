@@ -33,10 +33,20 @@ namespace {
 constexpr int64_t kMaxDim = int64_t(1) << 30;
 constexpr int64_t kMaxGridItems = 0xffffffffLL;
 
+// The main kernel's configurations, then the split-K ones.
 struct Table {
+    std::vector<KernelEntry> all;
     const KernelEntry* entries;
     int count;
-    Table() { entries = phobos::kernel_table(&count); }
+    Table() {
+        int n = 0, ns = 0;
+        const KernelEntry* main = phobos::kernel_table(&n);
+        const KernelEntry* split = phobos::splitk_kernel_table(&ns);
+        all.assign(main, main + n);
+        all.insert(all.end(), split, split + ns);
+        entries = all.data();
+        count = (int)all.size();
+    }
 };
 const Table& table() {
     static const Table t;
@@ -145,8 +155,8 @@ __attribute__((format(printf, 1, 2))) void log_line(const char* fmt, ...) {
 // 256x256 tile runs on 8 waves (4 x 2, two per SIMD): against 4 waves it
 // measured 0.3% faster on the super-tiled 16384^3 walk, 4096^3 and the
 // tall-skinny product alike (five alternating runs, no overlap).
-// A split-K entry: the 32 x 32 tile with more waves than its one block.
-bool is_splitk(const sgemm_config& c) { return c.bm == 32 && c.bn == 32 && c.wm * c.wn > 1; }
+// A split-K entry: a wave grid larger than the tile's 32 x 32 blocks.
+bool is_splitk(const sgemm_config& c) { return 32 * c.wm > c.bm || 32 * c.wn > c.bn; }
 
 int default_entry(int64_t M, int64_t N, int64_t K) {
     struct Pick { int bm, bn, bk, wm, wn; double rate; };
@@ -156,12 +166,14 @@ int default_entry(int64_t M, int64_t N, int64_t K) {
         return (tiles + kCUs - 1) / kCUs;
     };
     const int64_t small_per_cu = per_cu(32, 32);
+    const int64_t tiles32 = ((M + 31) / 32) * ((N + 31) / 32);
     const Pick picks[] = {
         {256, 256, 32, 4, 2, 1.00},
         {256, 128, 16, 4, 2, 0.98},
         {128, 128, 32, 2, 2, 0.90},
         small_per_cu <= 9 ? Pick{32, 32, 32, 1, 1, 0.60} : Pick{32, 32, 16, 1, 1, 0.70},
         {32, 32, 16, 2, 2, 0.79},   // split-K: four waves share each 32x32 tile
+        {64, 64, 16, 4, 1, 0.85},   // split-K: four waves share each 64x64 tile
     };
     int best = 0;
     double best_est = 0.0;
@@ -169,8 +181,12 @@ int default_entry(int64_t M, int64_t N, int64_t K) {
         const Pick& p = picks[i];
         // split-K as an estimate only from K = 2048 on (below it, it lost to
         // the tile the estimate picked otherwise at 1664^3, 1792^3 and
-        // 2560 x 2560 x 1024 by 1-2%)
-        if (p.wm * p.wn > 1 && p.bm == 32 && K < 2048) continue;
+        // 2560 x 2560 x 1024 by 1-2%); the 64x64 form only beyond 2560
+        // 32x32 tiles (below that it lost to the 32x32 forms at 1536^3 and
+        // 1664^3 by 11-16%)
+        const bool splitk = 32 * p.wm > p.bm || 32 * p.wn > p.bn;
+        if (splitk && K < 2048) continue;
+        if (splitk && p.bm == 64 && tiles32 <= 2560) continue;
         const int64_t per = per_cu(p.bm, p.bn);
         const double occ = std::min(1.0, (double)(per * p.wm * p.wn) / 4.0);
         const bool alone = (p.bm == 256 && p.bn == 256) || per == 1;
@@ -192,9 +208,10 @@ int default_entry(int64_t M, int64_t N, int64_t K) {
         // already and K is short (1024 x 2048 x 1024: 101.8 against 95.2
         // TFLOP/s).  Beyond 2560 tiles the estimate above decides between four
         // split-K waves (rate 0.79: 114-123 TFLOP/s from 2304^3 to 3584^3 and
-        // at 8192 deep, against 80-117 for the tiles picked before) and the
-        // other tiles.
-        const int64_t tiles = ((M + 31) / 32) * ((N + 31) / 32);
+        // at 8192 deep, against 80-117 for the tiles picked before; over a
+        // 64x64 tile, rate 0.85: 125-135 at 3072^3, 3584^3 and 3072^2 x 8192)
+        // and the other tiles.
+        const int64_t tiles = tiles32;
         const bool two_per_simd = tiles % 1024 == 0 && tiles >= 2048 && K < 4096;
         if (tiles <= 2560) {
             if (K >= 512 && !two_per_simd)

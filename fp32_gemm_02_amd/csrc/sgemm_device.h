@@ -94,4 +94,22 @@ template <int N>
 constexpr int kWaitVm = (N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8);
 static_assert(kWaitVm<0> == 0x70 && kWaitVm<4> == 0x74, "s_waitcnt encoding");
 
+// NB consecutive floats of B read with one LDS instruction, and element n of it.
+template <int NB> struct BVec;
+template <> struct BVec<1> {
+    using type = float;
+    static __device__ __forceinline__ float get(float v, int) { return v; }
+    static __device__ __forceinline__ void set(float& v, int, float x) { v = x; }
+};
+template <> struct BVec<2> {
+    using type = f32x2;
+    static __device__ __forceinline__ float get(f32x2 v, int n) { return v[n]; }
+    static __device__ __forceinline__ void set(f32x2& v, int n, float x) { v[n] = x; }
+};
+template <> struct BVec<4> {
+    using type = f32x4;
+    static __device__ __forceinline__ float get(f32x4 v, int n) { return v[n]; }
+    static __device__ __forceinline__ void set(f32x4& v, int n, float x) { v[n] = x; }
+};
+
 }  // namespace phobos

@@ -37,6 +37,8 @@ struct KernelEntry {
 
 // The compiled configurations (count written to *count).
 const KernelEntry* kernel_table(int* count);
+// The split-K entries (sgemm_splitk.hip), listed after kernel_table's.
+const KernelEntry* splitk_kernel_table(int* count);
 
 // The compiled configurations of the matrix-core variant for input format
 // fmt (SGEMM_TC_F16 or SGEMM_TC_BF16); nullptr and *count = 0 otherwise.

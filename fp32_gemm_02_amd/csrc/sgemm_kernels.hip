@@ -65,27 +65,6 @@
 namespace phobos {
 
 
-// NB consecutive floats of B read with one LDS instruction, and element n of it.
-template <int NB> struct BVec;
-template <> struct BVec<1> {
-    using type = float;
-    static __device__ __forceinline__ float get(float v, int) { return v; }
-    static __device__ __forceinline__ void set(float& v, int, float x) { v = x; }
-};
-template <> struct BVec<2> {
-    using type = f32x2;
-    static __device__ __forceinline__ float get(f32x2 v, int n) { return v[n]; }
-    static __device__ __forceinline__ void set(f32x2& v, int n, float x) { v[n] = x; }
-};
-template <> struct BVec<4> {
-    using type = f32x4;
-    static __device__ __forceinline__ float get(f32x4 v, int n) { return v[n]; }
-    static __device__ __forceinline__ void set(f32x4& v, int n, float x) { v[n] = x; }
-};
-
-
-
-
 template <int BM, int BN, int BK, int WM, int WN>
 struct TileShape {
     static constexpr int NT = 64 * WM * WN;      // threads per workgroup
@@ -584,173 +563,6 @@ __global__ __launch_bounds__(64 * WM * WN) void sgemm_mfma_kernel(GemmArgs p) {
     }
 }
 
-// ---------------------------------------------------------------------------
-// Split-K within one workgroup, for products with few 32 x 32 tiles (a single
-// wave per tile leaves most SIMDs idle and waits out every chunk's load
-// latency alone): KS waves share one 32 x 32 tile of C.  Wave w takes the
-// chunks w, w + KS, w + 2KS, ... of BK k each and accumulates its own partial
-// tile with v_mfma_f32_32x32x2_f32 (operand layout as in sgemm_mfma_kernel
-// with one 32 x 32 block per wave), through two LDS stages of its own: each
-// wave loads and reads only its own stages, so the K loop has no barrier,
-// only the wave's own wait for its loads.  The partial tiles are then added
-// in wave order 0, 1, ..., KS-1 through LDS, each wave finishing 16/KS of the
-// 16 accumulator rows of every lane, and stored as alpha*sum + beta*C.  Any
-// order of the k terms is within the error bound, and this one is fixed, so
-// results repeat bit for bit.
-template <int BK, int KS, bool VEC>
-__global__ __launch_bounds__(64 * KS) void sgemm_splitk_kernel(GemmArgs p) {
-    constexpr int QA = BK / 4;                  // 16-byte pieces per A row
-    constexpr int A_FLOATS = 32 * BK;
-    constexpr int STAGE = 2 * 32 * BK;          // A (32 x BK) then B (BK x 32)
-    constexpr int REGION = 2 * STAGE;           // a wave's two stages
-    constexpr int LA = 32 * QA / 64;            // 16-byte pieces of A per lane per chunk
-    constexpr int LB = BK * 8 / 64;             // and of B
-    constexpr int RW = 16 / KS;                 // accumulator rows each wave finishes
-    static_assert(QA == 4 || QA == 8, "BK is 16 or 32");
-    static_assert(RW * KS == 16, "accumulator rows split evenly over the waves");
-    static_assert(REGION >= 16 * 64, "a wave's partial tile fits its region");
-    static_assert(KS * REGION * 4 <= 160 * 1024, "LDS of one CU");
-    __shared__ __attribute__((aligned(16))) float smem[KS * REGION];
-
-    int tm, tn;
-    tile_of(p, tm, tn);
-    const int m0 = tm * 32, n0 = tn * 32;
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int l32 = lane & 31, h = lane >> 5;
-    float* const mine = smem + wave * REGION;
-    const int nk = (p.K + BK - 1) / BK;
-    const int nmine = wave < nk ? (nk - 1 - wave) / KS + 1 : 0;   // this wave's chunks
-
-    // Direct loads (as in sgemm_mfma_kernel): A piece g of a chunk sits in
-    // slot g (row g / QA, stored piece g % QA = logical piece ^ swz(row)); a
-    // row past M reads row M-1, a B piece wholly past N the tile's first piece
-    // (both feed only unstored results).  A chunk that holds row K-1 of B on
-    // a tile at the N edge, or runs past K, comes through registers.
-    const bool n_inside = n0 + 32 <= p.N;
-    const bool narrow = ((int64_t)31 * p.lda + BK) * 4 <= (int64_t)UINT32_MAX &&
-                        ((int64_t)(BK - 1) * p.ldb + 32) * 4 <= (int64_t)UINT32_MAX;
-    uint32_t da_off[LA], db_off[LB];
-#pragma unroll
-    for (int j = 0; j < LA; ++j) {
-        const int g = j * 64 + lane, row = g / QA;
-        const int q = (g % QA) ^ swz<QA>(row);
-        da_off[j] = (uint32_t)(((int64_t)(min(m0 + row, p.M - 1) - m0) * p.lda + 4 * q) * 4);
-    }
-#pragma unroll
-    for (int j = 0; j < LB; ++j) {
-        const int g = j * 64 + lane, gn = n0 + 4 * (g % 8);
-        db_off[j] = (uint32_t)(((int64_t)(g / 8) * p.ldb + (gn < p.N ? gn - n0 : 0)) * 4);
-    }
-    auto direct_ok = [&](int k0) {
-        return VEC && narrow && (n_inside ? k0 + BK <= p.K : k0 + BK < p.K);
-    };
-    // Chunk c into stage s; true if it went direct (its loads still in flight).
-    auto load_chunk = [&](int c, int s) -> bool {
-        float* As = mine + s * STAGE;
-        float* Bs = As + A_FLOATS;
-        const int k0 = c * BK;
-        if (direct_ok(k0)) {
-            // every read of this stage (chunk c - 2) has returned
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-            for (int j = 0; j < LA; ++j) dma16s(p.A + (int64_t)m0 * p.lda + k0, da_off[j], As + j * 256);
-#pragma unroll
-            for (int j = 0; j < LB; ++j) dma16s(p.B + (int64_t)k0 * p.ldb + n0, db_off[j], Bs + j * 256);
-            return true;
-        }
-#pragma unroll
-        for (int j = 0; j < LA; ++j) {
-            const int g = j * 64 + lane, row = g / QA, sp = g % QA;
-            const int gk = k0 + 4 * (sp ^ swz<QA>(row)), grow = m0 + row;
-            const int nvalid = grow < p.M ? p.K - gk : 0;
-            const float* src = p.A + (int64_t)(grow < p.M ? grow : 0) * p.lda + gk;
-            *reinterpret_cast<f32x4*>(As + 4 * g) = load4<VEC>(src, nvalid);
-        }
-#pragma unroll
-        for (int j = 0; j < LB; ++j) {
-            const int g = j * 64 + lane, gk = k0 + g / 8, gn = n0 + 4 * (g % 8);
-            const int nvalid = gk < p.K ? p.N - gn : 0;
-            const float* src = p.B + (int64_t)(gk < p.K ? gk : 0) * p.ldb + gn;
-            *reinterpret_cast<f32x4*>(Bs + 4 * g) = load4<VEC>(src, nvalid);
-        }
-        return false;
-    };
-
-    f32x16 acc;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-    // Operand offsets inside a stage: lane half h takes k = h*BK/2 + kk of the
-    // chunk; one 16-byte read gives 4 consecutive k of its A row.
-    const int a_row = l32 * BK;
-    const int b_col = A_FLOATS + h * (BK / 2) * 32 + l32;
-    bool pend = nmine > 0 && load_chunk(wave, 0);
-    for (int i = 0; i < nmine; ++i) {
-        const float* As = mine + (i & 1) * STAGE;
-        bool next = false;
-        if (i + 1 < nmine) next = load_chunk(wave + (i + 1) * KS, (i + 1) & 1);
-        // chunk i has landed: only the next chunk's direct loads may remain
-        if (pend) {
-            if (next) {
-                if constexpr (LA + LB == 8)
-                    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-                else
-                    asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-            } else {
-                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            }
-        }
-        pend = next;
-#pragma unroll
-        for (int c = 0; c < QA / 2; ++c) {
-            const f32x4 a = *reinterpret_cast<const f32x4*>(
-                As + a_row + 4 * ((h * (QA / 2) + c) ^ swz<QA>(l32)));
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float b = As[b_col + (4 * c + e) * 32];
-                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], b, acc, 0, 0, 0);
-            }
-        }
-    }
-
-    // Partial tiles into LDS (each wave over its own region, whose reads have
-    // all returned), then rows r = wave*RW .. +RW-1 of every lane summed in
-    // wave order and stored.
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mine[r * 64 + lane] = acc[r];
-    __syncthreads();
-    const float alpha = p.alpha, beta = p.beta;
-    const int col = n0 + l32;
-#pragma unroll
-    for (int rr = 0; rr < RW; ++rr) {
-        const int r = wave * RW + rr;
-        float sum = smem[r * 64 + lane];
-#pragma unroll
-        for (int w = 1; w < KS; ++w) sum += smem[w * REGION + r * 64 + lane];
-        const int row = m0 + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (row < p.M && col < p.N) {
-            float* dst = p.C + (int64_t)row * p.ldc + col;
-            float v = alpha * sum;
-            if (beta != 0.0f) v += beta * *dst;
-            *dst = v;
-        }
-    }
-}
-
-template <int BK, int KS, bool VEC>
-hipError_t launch_splitk(const GemmArgs& p, hipStream_t stream) {
-    const dim3 grid((unsigned)(p.tiles_m * p.tiles_n));
-    hipLaunchKernelGGL((sgemm_splitk_kernel<BK, KS, VEC>), grid, dim3(64 * KS), 0, stream, p);
-    return hipGetLastError();
-}
-
-// A split-K entry is named by the 32 x 32 tile with wm x wn waves (wm * wn =
-// KS): more waves than the tile's one 32 x 32 block, which split K instead.
-#define PHOBOS_SPLITK_CFG(BK, WM, WN)                                                    \
-    KernelEntry{sgemm_config{32, 32, BK, WM, WN}, 64 * WM * WN,                          \
-                WM * WN * 4 * 32 * BK * 4,                                               \
-                &launch_splitk<BK, WM * WN, true>, &launch_splitk<BK, WM * WN, false>}
-
 template <int BM, int BN, int BK, int WM, int WN, bool VEC>
 hipError_t launch_gemm(const GemmArgs& p, hipStream_t stream) {
     const dim3 grid((unsigned)(p.tiles_m * p.tiles_n));
@@ -787,10 +599,6 @@ const KernelEntry* kernel_table(int* count) {
         PHOBOS_CFG(32, 32, 16, 1, 1),
         PHOBOS_CFG(64, 64, 32, 1, 1),
         PHOBOS_CFG(32, 32, 32, 1, 1),
-        PHOBOS_SPLITK_CFG(32, 2, 2),
-        PHOBOS_SPLITK_CFG(32, 4, 2),
-        PHOBOS_SPLITK_CFG(16, 2, 2),
-        PHOBOS_SPLITK_CFG(16, 4, 2),
     };
     *count = (int)(sizeof(table) / sizeof(table[0]));
     return table;

@@ -74,10 +74,12 @@ extern "C" {
  * wm x wn wavefronts of 64 lanes (workgroup = 64*wm*wn threads).  These are
  * the TILE_M / TILE_N / TILE_K of the pages' @autotune attribute ("Show HN:
  * Phobos", sections "Introducing the Phobos Language" and "Runtime").
- * A 32x32 tile with more than one wave (wm*wn = 4 or 8) is a split-K entry:
- * its waves share the one 32x32 block of C, each taking every (wm*wn)-th
- * chunk of bk of K, and their partial sums are added in wave order before
- * the store (a fixed order, so results repeat bit for bit).
+ * An entry whose wave grid is larger than its tile's 32x32 blocks
+ * (32*wm > bm or 32*wn > bn; 32x32 tiles with 4 or 8 waves, 64x64 with 4) is
+ * a split-K entry: its wm*wn waves each hold the whole bm x bn tile, each
+ * taking every (wm*wn)-th chunk of bk of K, and their partial sums are added
+ * in wave order before the store (a fixed order, so results repeat bit for
+ * bit).
  */
 typedef struct sgemm_config {
     int32_t bm, bn, bk, wm, wn;
@@ -153,8 +155,9 @@ int sgemm_init_leaf(int64_t M, int64_t N, float beta, float* C, int64_t ldc,
  * resident one would hide, so the estimate is ceil(T/256) * bm * bn *
  * (K + [alone] * 64) / (rate * min(1, ceil(T/256) * waves / 4)), `rate`
  * being the tile's measured rate (1.00, 0.98, 0.90, and 0.60 / 0.70 for
- * 32x32 at depth 32 / 16), and from K = 2048 on also the split-K entry
- * 32x32x16 on 2x2 waves (4 waves per tile, rate 0.79).  When the least is a
+ * 32x32 at depth 32 / 16), and from K = 2048 on also the split-K entries
+ * 32x32x16 on 2x2 waves (4 waves per tile, rate 0.79) and, for more than 2560
+ * 32x32 tiles, 64x64x16 on 4x1 waves (rate 0.85).  When the least is a
  * 32x32 tile, with T 32x32 tiles: for T <= 2560, K >= 512 (except T a
  * multiple of 1024 from 2048 on with K < 4096, where two single-wave tiles
  * per SIMD already run) the split-K entry 32x32x32 on 4x2 waves if T <= 512

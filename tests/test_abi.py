@@ -95,8 +95,9 @@ def test_config_table_and_forcing():
     cfgs = g.configs()
     assert len(cfgs) >= 4
     for c in cfgs:
-        if c.bm == 32 and c.bn == 32 and c.wm * c.wn > 1:
-            # a split-K entry: more waves than the tile's one 32x32 block
+        if 32 * c.wm > c.bm or 32 * c.wn > c.bn:
+            # a split-K entry: a wave grid larger than the tile's 32x32 blocks
+            assert c.bm == c.bn and c.bm in (32, 64)
             assert c.wm * c.wn in (4, 8) and c.bk in (16, 32)
             continue
         # each tile is whole 32x32 MFMA blocks per wave, B reads 1, 2 or 4 wide
@@ -152,10 +153,12 @@ def test_get_config_checks():
     ((200, 200, 16), (32, 32, 16, 1, 1)),
     ((1664, 1664, 1664), (32, 32, 16, 1, 1)),
     # beyond 2560 such tiles, from K = 2048 on, the estimate weighs split-K
-    # (four waves, rate 0.79) against the other tiles
+    # (four waves over a 32x32 tile, rate 0.79, or over a 64x64 one, 0.85)
+    # against the other tiles
     ((2304, 2304, 2304), (32, 32, 16, 2, 2)),
-    ((3072, 3072, 3072), (32, 32, 16, 2, 2)),
-    ((3584, 3584, 3584), (32, 32, 16, 2, 2)),
+    ((3072, 3072, 3072), (64, 64, 16, 4, 1)),
+    ((3584, 3584, 3584), (64, 64, 16, 4, 1)),
+    ((3072, 3072, 8192), (64, 64, 16, 4, 1)),
     ((2560, 2560, 2560), (32, 32, 16, 2, 2)),
     ((1792, 1792, 8192), (32, 32, 16, 2, 2)),
     # one 128x128 tile per CU beats 13 small ones per CU, and 576 tiles of

@@ -82,17 +82,17 @@ def test_brute_force_every_tile(cfg):
 
 
 def _splitk_cfgs():
-    return [c for c in _all_cfgs() if c.bm == 32 and c.bn == 32 and c.wm * c.wn > 1]
+    return [c for c in _all_cfgs() if 32 * c.wm > c.bm or 32 * c.wn > c.bn]
 
 
 @pytest.mark.parametrize("cfg", _splitk_cfgs(), ids=_cfg_id)
 def test_brute_force_split_k(cfg):
-    """The split-K entries (waves of one workgroup sharing a 32x32 tile, each
-    taking every KS-th chunk of K): K from one chunk to several chunks per
-    wave, with a K tail, on tiles inside and at the edges of C."""
-    bk, ks = cfg.bk, cfg.wm * cfg.wn
-    ms = [1, 31, 32, 33, 100]
-    ns = [1, 31, 32, 33, 100]
+    """The split-K entries (waves of one workgroup sharing a 32x32 or 64x64
+    tile, each taking every KS-th chunk of K): K from one chunk to several
+    chunks per wave, with a K tail, on tiles inside and at the edges of C."""
+    bk, ks, t = cfg.bk, cfg.wm * cfg.wn, cfg.bm
+    ms = [1, t - 1, t, t + 1, 100]
+    ns = [1, t - 1, t, t + 1, 100]
     kss = [1, bk, ks * bk - 1, ks * bk, 2 * ks * bk + 7, 1000]
     cases = [(M, N, K) for M in ms for N in ns for K in kss]
     print(f"brute force {_cfg_id(cfg)}: {len(cases)} shapes", flush=True)
