@@ -106,6 +106,16 @@ template <> struct BVec<2> {
     static __device__ __forceinline__ float get(f32x2 v, int n) { return v[n]; }
     static __device__ __forceinline__ void set(f32x2& v, int n, float x) { v[n] = x; }
 };
+// Three floats as a plain struct: an ext_vector_type of 3 is 16 bytes wide
+// and 16-byte aligned, so its loads and stores would touch a fourth float.
+struct f32x3s {
+    float v[3];
+};
+template <> struct BVec<3> {
+    using type = f32x3s;
+    static __device__ __forceinline__ float get(const f32x3s& v, int n) { return v.v[n]; }
+    static __device__ __forceinline__ void set(f32x3s& v, int n, float x) { v.v[n] = x; }
+};
 template <> struct BVec<4> {
     using type = f32x4;
     static __device__ __forceinline__ float get(f32x4 v, int n) { return v[n]; }

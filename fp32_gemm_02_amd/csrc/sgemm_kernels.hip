@@ -88,7 +88,7 @@ struct TileShape {
     static constexpr int DB = BK * QB / 64 / NW; // direct loads of B per wave per stage
     static_assert(BM % WM == 0 && BN % WN == 0, "wave grid must divide the tile");
     static_assert(TWM % 32 == 0 && TWN % 32 == 0, "wave tile is whole 32x32 blocks");
-    static_assert(NB == 1 || NB == 2 || NB == 4, "B reads are 1, 2 or 4 floats wide");
+    static_assert(NB >= 1 && NB <= 4, "B reads are 1 to 4 floats wide");
     static_assert(QA == 4 || QA == 8, "BK is 16 or 32");
     static_assert((BM * QA) % NT == 0 && (BK * QB) % NT == 0, "whole loads per thread");
     static_assert(DA * 64 * NW == BM * QA && DB * 64 * NW == BK * QB,
@@ -517,46 +517,54 @@ __global__ __launch_bounds__(64 * WM * WN) void sgemm_mfma_kernel(GemmArgs p) {
         }
         return;
     }
+    // Tile at an edge of C: rows past M and columns past N are neither read
+    // nor written.  As above, a lane reads the C values of several rows of a
+    // block before it writes any (all 16, or 4 at a time where the
+    // accumulators fill the register file), so the edge tiles, which finish
+    // last, wait for one to four memory round trips per block rather than one
+    // per row.
+    const bool wide = VEC && ncols >= T::NB;   // all NB columns of the lane inside C
+    constexpr int RB = T::MB * T::NB * 16 >= 256 ? 4 : 16;   // rows per batch
 #pragma unroll
     for (int i = 0; i < T::MB; ++i) {
+        const int row0 = m0 + wm * T::TWM + i * 32 + 4 * h;
+        auto row_of = [&](int r) { return row0 + 8 * (r >> 2) + (r & 3); };
+        auto row_ptr = [&](int r) { return p.C + (int64_t)row_of(r) * p.ldc + col; };
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int row = m0 + wm * T::TWM + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-            if (row >= p.M || ncols <= 0) continue;
-            float* dst = p.C + (int64_t)row * p.ldc + col;
-            float v[T::NB];
+        for (int rb = 0; rb < 16; rb += RB) {
+            CV cv[RB];
+            if (beta != 0.0f) {
 #pragma unroll
-            for (int n = 0; n < T::NB; ++n) v[n] = alpha * acc[i][n][r];
-            if (VEC && ncols >= T::NB) {
-                if (beta != 0.0f) {
-                    if constexpr (T::NB == 4) {
-                        const f32x4 c = *reinterpret_cast<const f32x4*>(dst);
-                        v[0] += beta * c[0]; v[1] += beta * c[1];
-                        v[2] += beta * c[2]; v[3] += beta * c[3];
-                    } else if constexpr (T::NB == 2) {
-                        const f32x2 c = *reinterpret_cast<const f32x2*>(dst);
-                        v[0] += beta * c[0]; v[1] += beta * c[1];
+                for (int e = 0; e < RB; ++e) {
+                    if (row_of(rb + e) >= p.M || ncols <= 0) continue;
+                    const float* src = row_ptr(rb + e);
+                    if (wide) {
+                        cv[e] = *reinterpret_cast<const CV*>(src);
                     } else {
-                        v[0] += beta * dst[0];
+#pragma unroll
+                        for (int n = 0; n < T::NB; ++n)
+                            BVec<T::NB>::set(cv[e], n, n < ncols ? src[n] : 0.0f);
                     }
                 }
-                if constexpr (T::NB == 4) {
-                    f32x4 o = {v[0], v[1], v[2], v[3]};
-                    *reinterpret_cast<f32x4*>(dst) = o;
-                } else if constexpr (T::NB == 2) {
-                    f32x2 o = {v[0], v[1]};
-                    *reinterpret_cast<f32x2*>(dst) = o;
-                } else {
-                    dst[0] = v[0];
-                }
-            } else {
+            }
+#pragma unroll
+            for (int e = 0; e < RB; ++e) {
+                const int r = rb + e;
+                if (row_of(r) >= p.M || ncols <= 0) continue;
+                float* dst = row_ptr(r);
+                CV o;
 #pragma unroll
                 for (int n = 0; n < T::NB; ++n) {
-                    if (n < ncols) {
-                        float o = v[n];
-                        if (beta != 0.0f) o += beta * dst[n];
-                        dst[n] = o;
-                    }
+                    float v = alpha * acc[i][n][r];
+                    if (beta != 0.0f) v += beta * BVec<T::NB>::get(cv[e], n);
+                    BVec<T::NB>::set(o, n, v);
+                }
+                if (wide) {
+                    *reinterpret_cast<CV*>(dst) = o;
+                } else {
+#pragma unroll
+                    for (int n = 0; n < T::NB; ++n)
+                        if (n < ncols) dst[n] = BVec<T::NB>::get(o, n);
                 }
             }
         }
@@ -588,6 +596,7 @@ const KernelEntry* kernel_table(int* count) {
         PHOBOS_CFG(256, 256, 16, 2, 2),
         PHOBOS_CFG(256, 256, 32, 2, 2),
         PHOBOS_CFG(256, 128, 16, 4, 2),
+        PHOBOS_CFG(320, 192, 16, 2, 2),
         PHOBOS_CFG(256, 128, 16, 2, 2),
         PHOBOS_CFG(128, 256, 16, 2, 4),
         PHOBOS_CFG(128, 256, 16, 2, 2),

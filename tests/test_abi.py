@@ -100,9 +100,9 @@ def test_config_table_and_forcing():
             assert c.bm == c.bn and c.bm in (32, 64)
             assert c.wm * c.wn in (4, 8) and c.bk in (16, 32)
             continue
-        # each tile is whole 32x32 MFMA blocks per wave, B reads 1, 2 or 4 wide
+        # each tile is whole 32x32 MFMA blocks per wave, B reads 1 to 4 wide
         assert c.bm % (32 * c.wm) == 0 and c.bn % (32 * c.wn) == 0
-        assert (c.bn // c.wn // 32) in (1, 2, 4)
+        assert (c.bn // c.wn // 32) in (1, 2, 3, 4)
         assert c.bk % 8 == 0
     lib = g.lib()
     assert lib.sgemm_config_at(-1, ctypes.byref(g.sgemm_config())) == -1
