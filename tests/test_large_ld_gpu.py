@@ -62,6 +62,51 @@ def test_sgemm_row_span_past_4_gib(which):
     torch.cuda.empty_cache()
 
 
+# One entry of each kernel family: the 8-wave 256x256 tile, the 320x192 tile,
+# a single-wave 32x32 tile and the two split-K tile sizes.
+_FAMILIES = [(256, 256, 32, 4, 2), (320, 192, 16, 2, 2), (32, 32, 32, 1, 1),
+             (32, 32, 16, 2, 2), (64, 64, 16, 4, 1)]
+
+
+def _round4(x):
+    return (x + 3) // 4 * 4
+
+
+@pytest.mark.parametrize("which", ["lda", "ldb"])
+@pytest.mark.parametrize("cfg", _FAMILIES, ids=lambda c: "%dx%dx%d_w%dx%d" % c)
+def test_sgemm_row_span_past_4_gib_each_kernel(cfg, which):
+    """For each kernel family, forced: the BM rows of A, or the BK rows of B,
+    of one chunk span more than 4 GiB (leading dimensions that are multiples
+    of 4, so only the span rules out the direct loads).  One whole tile and a
+    ragged one in M, two whole chunks and a tail in K."""
+    bm, bn, bk = cfg[:3]
+    M, N, K = bm + 3, bn + 5, 2 * bk + 8
+    lda, ldb = K, N
+    if which == "lda":
+        lda = _round4(_2_32 // (4 * (bm - 1)) + 64)
+        assert ((bm - 1) * lda + bk) * 4 > _2_32
+    else:
+        ldb = _round4(_2_32 // (4 * (bk - 1)) + 64)
+        assert ((bk - 1) * ldb + bn) * 4 > _2_32
+    rng = np.random.default_rng(14)
+    A = rng.uniform(-1, 1, (M, K)).astype(np.float32)
+    B = rng.uniform(-1, 1, (K, N)).astype(np.float32)
+    C = rng.uniform(-1, 1, (M, N)).astype(np.float32)
+    print(f"sgemm cfg {cfg} {which} M={M} N={N} K={K} lda={lda} ldb={ldb}", flush=True)
+    dA, dB = _strided(A, lda), _strided(B, ldb)
+    dC = torch.from_numpy(C.copy()).to(gu.device())
+    g.sgemm_set_config(cfg)
+    try:
+        g.sgemm(M, N, K, -0.75, dA, lda, dB, ldb, 1.5, dC, N)
+        torch.cuda.synchronize()
+    finally:
+        g.sgemm_set_config(None)
+    ref, bnd = oracle.sgemm(M, N, K, -0.75, A, B, 1.5, C)
+    _check(dC.cpu().numpy(), ref, bnd, f"sgemm {cfg} {which}")
+    del dA, dB
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("fmt", [g.SGEMM_TC_F16, g.SGEMM_TC_BF16], ids=["f16", "bf16"])
 def test_tc_staged_k_past_4_gib(fmt):
     """A K so long that the staged form's 16-bit rows span more than 4 GiB per
