@@ -146,8 +146,9 @@ __attribute__((format(printf, 1, 2))) void log_line(const char* fmt, ...) {
 // with `rate` the tile's measured rate per CU against the 256x256 tile
 // (a sweep of every candidate over 20 square and skinny shapes from 1152^3
 // to 8192^3: the choice is within 2% of the fastest tile on every one, 0.2%
-// on average; 5003 x 3001 x 2047 takes 256x128, 478 us against 503 for
-// 256x256 on the same box).  The single-wave 32x32 tile, the only one
+// on average; 5003 x 3001 x 2047 takes 256x128: 472.6 us against 478.6
+// for 256x256 and 482.8 for the 320x192 tile of exactly 256 workgroups,
+// which only the tuner tries, in one run).  The single-wave 32x32 tile, the only one
 // that fills the SIMDs of small products (1024^3: 26 us against 71 us for
 // a 64x64 tile), steps through K 32 deep while its CU holds at most 9 of
 // them and 16 deep beyond that, where more of them fit the LDS at once

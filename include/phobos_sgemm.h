@@ -163,7 +163,10 @@ int sgemm_init_leaf(int64_t M, int64_t N, float beta, float* C, int64_t ldc,
  * per SIMD already run) the split-K entry 32x32x32 on 4x2 waves if T <= 512
  * or K >= 16384, else 32x32x16 on 2x2 waves, and for 64 <= K < 512 with
  * T <= 576 the 32x32x16 2x2 entry; for T > 2560 the split-K entry when the
- * estimate picked it; otherwise one wave per tile.
+ * estimate picked it; otherwise one wave per tile.  The other compiled
+ * configurations (among them 320x192x16 on 2x2 waves, whose 16 x 16 tiles
+ * cover 5120 x 3072 in exactly 256 workgroups) are there for the tuner and
+ * for forcing.
  */
 int sgemm_config_count(void);
 int sgemm_config_at(int32_t index, sgemm_config* out);
