@@ -3,6 +3,7 @@ and checks its arguments before any HIP call (no GPU work is started here)."""
 import ctypes
 import os
 import re
+import threading
 
 import pytest
 
@@ -331,3 +332,40 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
 def test_tc_noalloc_argument_checks(args, want):
     assert g.sgemm_tc_noalloc_raw(*args, stream=0) == want
     assert "static scratch" in g.status_string(g.SGEMM_ERR_SCRATCH)
+
+
+def test_host_entry_points_from_many_threads():
+    """The host-only entry points called from eight threads at once (ctypes
+    drops the GIL for the call): the built-in tile choice, the tuned table's
+    reset, the planner and the status strings give each thread what one
+    thread alone gets, and nothing crashes."""
+    shapes = [((37 * i) % 9000 + 1, (91 * i) % 7000 + 1, (53 * i) % 20000 + 1) for i in range(300)]
+    want = [g.sgemm_get_config(M, N, K, K, N, N).as_tuple() for M, N, K in shapes]
+    plan_want = g.sgemm_plan_supertiles(4096, 4096, 4096, 1.0, 256 << 20)
+    plan_key = (plan_want.TM, plan_want.TN, plan_want.TK, plan_want.walk)
+    errors = []
+
+    def work(t):
+        try:
+            for j in range(len(shapes)):
+                i = (t * 41 + j) % len(shapes)
+                M, N, K = shapes[i]
+                got = g.sgemm_get_config(M, N, K, K, N, N).as_tuple()
+                if got != want[i]:
+                    errors.append(("config", t, shapes[i], got, want[i]))
+                if j % 60 == 0:
+                    g.sgemm_tune_forget()
+                    p = g.sgemm_plan_supertiles(4096, 4096, 4096, 1.0, 256 << 20)
+                    if (p.TM, p.TN, p.TK, p.walk) != plan_key:
+                        errors.append(("plan", t))
+                if g.status_string(-(j % 12 + 1)) != "argument %d is invalid" % (j % 12 + 1):
+                    errors.append(("status", t, j))
+        except Exception as e:   # reported below, with the thread's number
+            errors.append(("exception", t, repr(e)))
+
+    threads = [threading.Thread(target=work, args=(t,)) for t in range(8)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not errors, errors[:5]

@@ -296,6 +296,60 @@ def test_concurrent_calls_on_two_streams():
         gu.check_full(w, x, dC3.cpu().numpy(), steps=steps, relaxed=True)
 
 
+def test_calls_from_four_host_threads():
+    """Four host threads, each enqueuing its own products on its own stream at
+    the same time (the library's calls run without the GIL): each thread's
+    results equal the same calls made one at a time, bit for bit, and the
+    first call of each agrees with the oracle."""
+    import threading
+
+    ws = [wl.custom(640, 600, 520, 1.0, -1.0, seed=81, lda=524, ldb=604, ldc=608),
+          wl.custom(300, 300, 2100, 0.5, 1.0, seed=82),
+          wl.custom(512, 768, 384, -1.0, 0.5, seed=83, entry="sgemm_supertiled", TM=256,
+                    TN=256, TK=128),
+          wl.custom(96, 1000, 4000, 2.0, 0.0, seed=84)]
+    xs = [wl.make_inputs(w) for w in ws]
+    devs = [(gu.to_dev(x.A), gu.to_dev(x.B), gu.to_dev(x.C)) for x in xs]
+    streams = [torch.cuda.Stream() for _ in ws]
+    torch.cuda.synchronize()
+
+    def call(w, dA, dB, dC, s=None):
+        if w.entry == "sgemm":
+            g.sgemm(w.M, w.N, w.K, w.alpha, dA, w.lda, dB, w.ldb, w.beta, dC, w.ldc, stream=s)
+        else:
+            g.sgemm_supertiled(w.M, w.N, w.K, w.alpha, dA, w.lda, dB, w.ldb, w.beta, dC,
+                               w.ldc, w.TM, w.TN, w.TK, stream=s)
+
+    errors = []
+
+    def work(t):
+        try:
+            for _ in range(5):
+                call(ws[t], *devs[t], s=streams[t])
+        except Exception as e:   # reported below, with the thread's number
+            errors.append((t, repr(e)))
+
+    threads = [threading.Thread(target=work, args=(t,)) for t in range(len(ws))]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for w, x, (dA, dB, dC) in zip(ws, xs, devs):
+        print(f"threads: {w.entry} {w.M}x{w.N}x{w.K}", flush=True)
+        dC2 = gu.to_dev(x.C)
+        for _ in range(5):
+            call(w, dA, dB, dC2)
+        torch.cuda.synchronize()
+        assert torch.equal(dC.view(torch.int32), dC2.view(torch.int32))
+        dC3 = gu.to_dev(x.C)
+        call(w, dA, dB, dC3)
+        torch.cuda.synchronize()
+        steps = 1 if w.entry == "sgemm" else -(-w.K // w.TK)
+        gu.check_full(w, x, dC3.cpu().numpy(), steps=steps, relaxed=True)
+
+
 @pytest.mark.parametrize("cfg", [None, (64, 64, 16, 1, 1)], ids=["default", "64x64"])
 @pytest.mark.parametrize("a_val,b_val", [(2.0 ** -140, 1.0), (2.0 ** -70, 2.0 ** -70)],
                          ids=["subnormal_input", "subnormal_product"])
