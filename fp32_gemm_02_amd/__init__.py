@@ -187,27 +187,32 @@ def _dev_shape(x, rows, cols, ld, name, where):
                              f"matrix with leading dimension {ld} spans {need}")
 
 
-def _dev_addr(x, name, where):
+def _dev_addr(x, name, where, cur):
     """Address of a device operand: an integer (or None) as it is; a tensor
-    only if it lives on the current GPU (ValueError otherwise)."""
+    only if it lives on GPU `cur`, the current one (ValueError otherwise)."""
     if x is None or not hasattr(x, "data_ptr"):
         return _ptr(x)
-    import torch
-    if not x.is_cuda:
+    dev = x.get_device()          # -1 for a tensor in host memory
+    if dev < 0:
         raise ValueError(f"{where}: {name} is on {x.device}, not on a GPU")
-    if x.device.index != torch.cuda.current_device():
+    if dev != cur:
         raise ValueError(f"{where}: {name} is on {x.device}, the current device is "
-                         f"cuda:{torch.cuda.current_device()}")
+                         f"cuda:{cur}")
     return x.data_ptr()
 
 
 def _dev_ptrs(where, *ops):
     """Checked addresses of device operands given as (x, rows, cols, ld, name):
     every operand's dtype and extent first, then where each lives, so that
-    nothing reaches the library unless all of them pass."""
+    nothing reaches the library unless all of them pass.  The current device
+    is read once per call."""
+    cur = None
     for x, rows, cols, ld, name in ops:
         _dev_shape(x, rows, cols, ld, name, where)
-    return tuple(_dev_addr(x, name, where) for x, _, _, _, name in ops)
+        if cur is None and hasattr(x, "data_ptr") and x.is_cuda:
+            import torch
+            cur = torch.cuda.current_device()
+    return tuple(_dev_addr(x, name, where, cur) for x, _, _, _, name in ops)
 
 
 def _dev(x, rows, cols, ld, name, where):
