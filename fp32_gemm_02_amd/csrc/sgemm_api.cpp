@@ -147,8 +147,11 @@ __attribute__((format(printf, 1, 2))) void log_line(const char* fmt, ...) {
 // (a sweep of every candidate over 20 square and skinny shapes from 1152^3
 // to 8192^3: the choice is within 2% of the fastest tile on every one, 0.2%
 // on average; 5003 x 3001 x 2047 takes 256x128: 472.6 us against 478.6
-// for 256x256 and 482.8 for the 320x192 tile of exactly 256 workgroups,
-// which only the tuner tries, in one run).  The single-wave 32x32 tile, the only one
+// for 256x256 and 482.8 for the 320x192 tile in one run).  The 320x192 tile
+// on 2x2 waves (one workgroup per CU, like 256x256) makes exactly 256
+// workgroups of 5120 x 3072; its rate, 0.965, is fitted on products whose K
+// is whole chunks (5120 x 3072 x 4096: 146.5 against 141.3 TFLOP/s for
+// 256x256; 2500 x 6000^2, 4800 x 2900 x 8000 and 7680^3: +2.6 to +3.5%).  The single-wave 32x32 tile, the only one
 // that fills the SIMDs of small products (1024^3: 26 us against 71 us for
 // a 64x64 tile), steps through K 32 deep while its CU holds at most 9 of
 // them and 16 deep beyond that, where more of them fit the LDS at once
@@ -159,7 +162,7 @@ __attribute__((format(printf, 1, 2))) void log_line(const char* fmt, ...) {
 // A split-K entry: a wave grid larger than the tile's 32 x 32 blocks.
 bool is_splitk(const sgemm_config& c) { return 32 * c.wm > c.bm || 32 * c.wn > c.bn; }
 
-int default_entry(int64_t M, int64_t N, int64_t K) {
+int default_entry(int64_t M, int64_t N, int64_t K, bool direct) {
     struct Pick { int bm, bn, bk, wm, wn; double rate; };
     constexpr int64_t kCUs = 256;
     auto per_cu = [&](int bm, int bn) {
@@ -175,6 +178,7 @@ int default_entry(int64_t M, int64_t N, int64_t K) {
         small_per_cu <= 9 ? Pick{32, 32, 32, 1, 1, 0.60} : Pick{32, 32, 16, 1, 1, 0.70},
         {32, 32, 16, 2, 2, 0.79},   // split-K: four waves share each 32x32 tile
         {64, 64, 16, 4, 1, 0.85},   // split-K: four waves share each 64x64 tile
+        {320, 192, 16, 2, 2, 0.965},
     };
     int best = 0;
     double best_est = 0.0;
@@ -188,9 +192,16 @@ int default_entry(int64_t M, int64_t N, int64_t K) {
         const bool splitk = 32 * p.wm > p.bm || 32 * p.wn > p.bn;
         if (splitk && K < 2048) continue;
         if (splitk && p.bm == 64 && tiles32 <= 2560) continue;
+        // the 320x192 tile only where its chunks load directly: K whole
+        // 16-deep chunks and operand rows 16-byte aligned.  Otherwise chunks
+        // come through registers, which its one workgroup per CU on one wave
+        // per SIMD cannot hide (5003 x 3001 x 2047: 482.8 us against 472.6
+        // for 256x128; 4095^3 with unaligned rows: 62 against 126 TFLOP/s
+        // for 256x256)
+        if (p.bm == 320 && (K % 16 != 0 || !direct)) continue;
         const int64_t per = per_cu(p.bm, p.bn);
         const double occ = std::min(1.0, (double)(per * p.wm * p.wn) / 4.0);
-        const bool alone = (p.bm == 256 && p.bn == 256) || per == 1;
+        const bool alone = (p.bm == 256 && p.bn == 256) || p.bm == 320 || per == 1;
         const double est =
             (double)per * p.bm * p.bn * (double)(K + (alone ? 64 : 0)) / (p.rate * occ);
         if (i == 0 || est < best_est) {
@@ -364,8 +375,10 @@ const char* source_name(ChoiceSource s) {
     }
 }
 
+// `ptrs16`: the operands' base addresses are 16-byte aligned (assumed when
+// only the shape is known).
 int choose_entry(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
-                 ChoiceSource* src = nullptr) {
+                 ChoiceSource* src = nullptr, bool ptrs16 = true) {
     load_env_cache_once();
     ChoiceSource dummy;
     ChoiceSource& from = src ? *src : dummy;
@@ -390,7 +403,7 @@ int choose_entry(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int6
         }
     }
     from = kDefault;
-    return default_entry(M, N, K);
+    return default_entry(M, N, K, ptrs16 && lda % 4 == 0 && ldb % 4 == 0 && ldc % 4 == 0);
 }
 
 // Record a trace event pair around a launch when tracing is on.
@@ -760,7 +773,8 @@ int host_launch_gemm(int64_t M, int64_t N, int64_t K, float alpha, const float* 
                      int64_t lda, const float* B, int64_t ldb, float beta, float* C,
                      int64_t ldc, hipStream_t stream) {
     ChoiceSource src;
-    const int entry = choose_entry(M, N, K, lda, ldb, ldc, &src);
+    const int entry = choose_entry(M, N, K, lda, ldb, ldc, &src,
+                                   aligned16(A) && aligned16(B) && aligned16(C));
     if (entry < 0) return SGEMM_ERR_NO_CONFIG;
     return launch_gemm(entry, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, src);
 }
@@ -788,7 +802,8 @@ int sgemm(int64_t M, int64_t N, int64_t K, float alpha, const float* A, int64_t 
         return launch_init(M, N, beta, C, ldc, s);
     }
     ChoiceSource src;
-    const int entry = choose_entry(M, N, K, lda, ldb, ldc, &src);
+    const int entry = choose_entry(M, N, K, lda, ldb, ldc, &src,
+                                   aligned16(A) && aligned16(B) && aligned16(C));
     if (entry < 0) return SGEMM_ERR_NO_CONFIG;
     return launch_gemm(entry, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s, src);
 }
@@ -832,7 +847,8 @@ int sgemm_supertiled(int64_t M, int64_t N, int64_t K, float alpha, const float* 
                 const float* As = A + r0 * lda + k0;
                 const float* Bs = B + k0 * ldb + c0;
                 ChoiceSource src;
-                const int entry = choose_entry(rows, cols, depth, lda, ldb, ldc, &src);
+                const int entry = choose_entry(rows, cols, depth, lda, ldb, ldc, &src,
+                                               aligned16(As) && aligned16(Bs) && aligned16(Cs));
                 if (entry < 0) return SGEMM_ERR_NO_CONFIG;
                 st = launch_gemm(entry, rows, cols, depth, alpha, As, lda, Bs, ldb, 1.0f, Cs,
                                  ldc, s, src);
@@ -1102,7 +1118,7 @@ int sgemm_tune(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_
     // warm-up the first candidates are timed slow.  About 100 ms of the
     // built-in choice first; its time also sizes the short timings below, so
     // that each covers about 1 ms rather than one launch-dominated call.
-    const int dflt = default_entry(M, N, K);
+    const int dflt = default_entry(M, N, K, lda % 4 == 0 && ldb % 4 == 0 && ldc % 4 == 0);
     float t_dflt = 0.0f;
     if (st == SGEMM_OK) st = time_one(dflt, 1, &t_dflt);
     const float t_est = std::max(t_dflt, 1e-3f);

@@ -34,13 +34,22 @@ __device__ __forceinline__ void tile_of(const Args& p, int& tm, int& tn) {
     tn = r / gsz;
 }
 
+// Four floats at 4-byte alignment: one 16-byte global load all the same
+// (gfx9 global memory instructions take dword-aligned addresses for wider
+// accesses), where the compiler would otherwise issue four dword loads.
+typedef float f32x4u __attribute__((ext_vector_type(4), aligned(4)));
+
 // Load 4 consecutive floats src[0..3] whose positions are valid while
-// e < nvalid (nvalid <= 0: all zero).  VEC: src is 16-byte aligned.
+// e < nvalid (nvalid <= 0: all zero).  VEC: src is 16-byte aligned;
+// otherwise 4-byte aligned, and a piece wholly inside is still read with
+// one 16-byte load.
 template <bool VEC>
 __device__ __forceinline__ f32x4 load4(const float* src, int nvalid) {
     f32x4 v;
     if (VEC && nvalid >= 4) {
         v = *reinterpret_cast<const f32x4*>(src);
+    } else if (nvalid >= 4) {
+        v = *reinterpret_cast<const f32x4u*>(src);
     } else {
         v[0] = nvalid > 0 ? src[0] : 0.0f;
         v[1] = nvalid > 1 ? src[1] : 0.0f;

@@ -150,23 +150,27 @@ int sgemm_init_leaf(int64_t M, int64_t N, float beta, float* C, int64_t ldc,
  * else 16 deep; 16 deep whenever K <= 16), the one with the least estimated
  * time on 256 CUs of 4 SIMDs: with T tiles the busiest CU holds
  * ceil(T/256) of them and runs its matrix cores at full rate only with at
- * least 4 waves, and a workgroup alone on its CU (a 256x256 one, or any
- * when ceil(T/256) == 1) pays about 64 k-steps of fixed cost that a second
+ * least 4 waves, and a workgroup alone on its CU (a 256x256 or 320x192
+ * one, or any when ceil(T/256) == 1) pays about 64 k-steps of fixed cost
+ * that a second
  * resident one would hide, so the estimate is ceil(T/256) * bm * bn *
  * (K + [alone] * 64) / (rate * min(1, ceil(T/256) * waves / 4)), `rate`
  * being the tile's measured rate (1.00, 0.98, 0.90, and 0.60 / 0.70 for
  * 32x32 at depth 32 / 16), and from K = 2048 on also the split-K entries
  * 32x32x16 on 2x2 waves (4 waves per tile, rate 0.79) and, for more than 2560
- * 32x32 tiles, 64x64x16 on 4x1 waves (rate 0.85).  When the least is a
+ * 32x32 tiles, 64x64x16 on 4x1 waves (rate 0.85), and where its chunks load
+ * straight into LDS (K a multiple of 16, leading dimensions multiples of 4,
+ * 16-byte aligned operands; sgemm_get_config, which sees no addresses,
+ * assumes aligned ones) the 320x192x16 tile on 2x2 waves (rate 0.965, alone
+ * on its CU like 256x256; 16 x 16 of them cover 5120 x 3072).  When the least
+ * is a
  * 32x32 tile, with T 32x32 tiles: for T <= 2560, K >= 512 (except T a
  * multiple of 1024 from 2048 on with K < 4096, where two single-wave tiles
  * per SIMD already run) the split-K entry 32x32x32 on 4x2 waves if T <= 512
  * or K >= 16384, else 32x32x16 on 2x2 waves, and for 64 <= K < 512 with
  * T <= 576 the 32x32x16 2x2 entry; for T > 2560 the split-K entry when the
  * estimate picked it; otherwise one wave per tile.  The other compiled
- * configurations (among them 320x192x16 on 2x2 waves, whose 16 x 16 tiles
- * cover 5120 x 3072 in exactly 256 workgroups) are there for the tuner and
- * for forcing.
+ * configurations are there for the tuner and for forcing.
  */
 int sgemm_config_count(void);
 int sgemm_config_at(int32_t index, sgemm_config* out);

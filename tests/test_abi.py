@@ -172,6 +172,12 @@ def test_get_config_checks():
     # two resident 256x128 tiles per CU hide each other's fixed cost
     ((2560, 2560, 1024), (256, 128, 16, 4, 2)),
     ((8192, 8192, 1024), (256, 128, 16, 4, 2)),
+    # 16 x 16 tiles of 320x192 (exactly 256 workgroups) where K is whole
+    # 16-deep chunks, and not otherwise (the same product with K = 4095)
+    ((5120, 3072, 4096), (320, 192, 16, 2, 2)),
+    ((2500, 6000, 6000), (320, 192, 16, 2, 2)),
+    ((7680, 7680, 7680), (320, 192, 16, 2, 2)),
+    ((5120, 3072, 4095), (256, 256, 32, 4, 2)),
     # the five workloads' shapes and the super-tiled step leaf
     ((4096, 4096, 4096), (256, 256, 32, 4, 2)),
     ((65536, 512, 4096), (256, 256, 32, 4, 2)),
@@ -182,6 +188,14 @@ def test_default_config_picks(shape, want):
     """The built-in choice at the boundaries of its rule, fixed on the CPU."""
     M, N, K = shape
     assert g.sgemm_get_config(M, N, K, K, N, N).as_tuple() == want
+
+
+def test_default_config_needs_direct_loads_for_the_320x192_tile():
+    """With leading dimensions that are not multiples of 4 every chunk comes
+    through registers, and the 320x192 tile is not taken."""
+    assert g.sgemm_get_config(5120, 3072, 4096, 4096, 3072, 3072).as_tuple() == (320, 192, 16, 2, 2)
+    for lds in [(4097, 3072, 3072), (4096, 3073, 3072), (4096, 3072, 3075)]:
+        assert g.sgemm_get_config(5120, 3072, 4096, *lds).as_tuple() == (256, 256, 32, 4, 2)
 
 
 def test_default_config_fits_the_shape():

@@ -382,6 +382,7 @@ def test_subnormals_are_kept(cfg, a_val, b_val):
     (768, 1280, 1536, (32, 32, 16, 2, 2)),
     (2048, 2048, 2048, (128, 128, 32, 2, 2)),
     (4096, 4096, 4096, (256, 256, 32, 4, 2)),  # 256x256 tiles with the C prefetch
+    (5120, 3072, 2048, (320, 192, 16, 2, 2)),  # exactly 256 tiles of 320x192
 ])
 def test_results_repeat_bit_for_bit(M, N, K, want):
     """The split-K entries add their waves' partial sums in a fixed order and
