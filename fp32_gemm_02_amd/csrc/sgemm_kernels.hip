@@ -522,8 +522,10 @@ __global__ __launch_bounds__(64 * WM * WN) void sgemm_mfma_kernel(GemmArgs p) {
     // block before it writes any (all 16, or 4 at a time where the
     // accumulators fill the register file), so the edge tiles, which finish
     // last, wait for one to four memory round trips per block rather than one
-    // per row.
-    const bool wide = VEC && ncols >= T::NB;   // all NB columns of the lane inside C
+    // per row.  A lane whose NB columns all lie inside C reads and writes
+    // them with one access (at 4-byte alignment when the rows are not
+    // 16-byte aligned).
+    const bool wide = ncols >= T::NB;   // all NB columns of the lane inside C
     constexpr int RB = T::MB * T::NB * 16 >= 256 ? 4 : 16;   // rows per batch
 #pragma unroll
     for (int i = 0; i < T::MB; ++i) {
@@ -538,8 +540,10 @@ __global__ __launch_bounds__(64 * WM * WN) void sgemm_mfma_kernel(GemmArgs p) {
                 for (int e = 0; e < RB; ++e) {
                     if (row_of(rb + e) >= p.M || ncols <= 0) continue;
                     const float* src = row_ptr(rb + e);
-                    if (wide) {
+                    if (wide && VEC) {
                         cv[e] = *reinterpret_cast<const CV*>(src);
+                    } else if (wide) {
+                        __builtin_memcpy(&cv[e], src, T::NB * sizeof(float));
                     } else {
 #pragma unroll
                         for (int n = 0; n < T::NB; ++n)
@@ -559,8 +563,10 @@ __global__ __launch_bounds__(64 * WM * WN) void sgemm_mfma_kernel(GemmArgs p) {
                     if (beta != 0.0f) v += beta * BVec<T::NB>::get(cv[e], n);
                     BVec<T::NB>::set(o, n, v);
                 }
-                if (wide) {
+                if (wide && VEC) {
                     *reinterpret_cast<CV*>(dst) = o;
+                } else if (wide) {
+                    __builtin_memcpy(dst, &o, T::NB * sizeof(float));
                 } else {
 #pragma unroll
                     for (int n = 0; n < T::NB; ++n)
