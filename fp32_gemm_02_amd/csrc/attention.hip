@@ -209,20 +209,29 @@ __global__ __launch_bounds__(256 * KSPLIT) void attention_kernel(AttnArgs p) {
         const char* ks = kring + buf * TILE + half * (KW * kRowB);
 #pragma unroll
         for (int kb = 0; kb < NSB; ++kb) s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {
-            f32x4 a[NSB];
+        // K fragments read two k-chunks ahead of the MFMAs that use them, so
+        // their LDS latency hides behind MFMAs instead of stalling the wave
+        f32x4 a[3][NSB];
+        auto read_k = [&](int cc, f32x4* dst) {
 #pragma unroll
             for (int kb = 0; kb < NSB; ++kb) {
                 const int krow = 16 * kb + q;             // A' row of this lane
                 // the swizzle of row KW*half + krow is that of krow (KW = 0 mod 16)
-                a[kb] = *reinterpret_cast<const f32x4*>(ks + krow * kRowB + 16 * kswz(krow, 4 * g + cc));
+                dst[kb] = *reinterpret_cast<const f32x4*>(ks + krow * kRowB + 16 * kswz(krow, 4 * g + cc));
             }
+        };
+        read_k(0, a[0]);
+        read_k(1, a[1]);
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+            if (cc + 2 < 4) read_k(cc + 2, a[(cc + 2) % 3]);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int e = 0; e < 4; ++e)
 #pragma unroll
                 for (int kb = 0; kb < NSB; ++kb)
-                    s[kb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[kb][e], qv[4 * cc + e], s[kb], 0, 0, 0);
+                    s[kb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[cc % 3][kb][e], qv[4 * cc + e], s[kb], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
@@ -234,6 +243,16 @@ __global__ __launch_bounds__(256 * KSPLIT) void attention_kernel(AttnArgs p) {
 
     // softmax of one step's scores s (in place) and the output products
     auto consume = [&](int it, f32x4* s, int vstage) {
+        // the first two V fragments are read before the softmax, the others
+        // two groups of MFMAs ahead of their use
+        const char* vs = vring + vstage * TILE + half * (KW * kRowB);
+        auto read_v = [&](int ts) {
+            const int vrow = 16 * (ts >> 2) + 4 * g + (ts & 3);
+            return *reinterpret_cast<const f32x4*>(vs + vrow * kRowB + 16 * q);
+        };
+        f32x4 va[3];
+        va[0] = read_v(0);
+        va[1] = read_v(1);
         // online softmax in base 2; keys past Nk weigh nothing (only the
         // last step can hold any)
         float bm = -INFINITY;
@@ -269,15 +288,15 @@ __global__ __launch_bounds__(256 * KSPLIT) void attention_kernel(AttnArgs p) {
         for (int db = 0; db < 4; ++db) o[db] *= alpha;
 
         // O^T += V^T P^T: step ts uses keys 16(ts/4) + 4g + ts%4 (lane group g)
-        const char* vs = vring + vstage * TILE + half * (KW * kRowB);
 #pragma unroll
         for (int ts = 0; ts < 4 * NSB; ++ts) {
-            const int vrow = 16 * (ts >> 2) + 4 * g + (ts & 3);
-            const f32x4 a = *reinterpret_cast<const f32x4*>(vs + vrow * kRowB + 16 * q);
+            if (ts + 2 < 4 * NSB) va[(ts + 2) % 3] = read_v(ts + 2);
+            __builtin_amdgcn_sched_barrier(0);
             const float w = s[ts >> 2][ts & 3];
 #pragma unroll
             for (int db = 0; db < 4; ++db)
-                o[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[db], w, o[db], 0, 0, 0);
+                o[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(va[ts % 3][db], w, o[db], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
