@@ -270,10 +270,20 @@ __global__ __launch_bounds__(256 * KSPLIT) void attention_kernel(AttnArgs p) {
             for (int r = 0; r < 4; ++r) bm = fmaxf(bm, s[kb][r]);
         bm = quad_max(bm);
         const float mn = fmaxf(m, bm);
+        const bool grew = mn > m;
         // a key half that has met no key yet keeps weight 0 (not exp2(-inf + inf))
         const float base = (mn == -INFINITY) ? 0.0f : mn;
         const float alpha = __builtin_amdgcn_exp2f(m - base);   // 0 until a key is met
         m = mn;
+        // The running output and weight sum are rescaled first, so that the
+        // output products need not wait for the multiplies, and only when the
+        // maximum of some lane of the wave grew: otherwise alpha is exactly 1
+        // (or o and l are still 0) and they would change nothing.
+        if (__builtin_amdgcn_ballot_w64(grew) != 0) {
+            l *= alpha;
+#pragma unroll
+            for (int db = 0; db < 4; ++db) o[db] *= alpha;
+        }
         float bl = 0.0f;
 #pragma unroll
         for (int kb = 0; kb < NSB; ++kb)
@@ -283,9 +293,7 @@ __global__ __launch_bounds__(256 * KSPLIT) void attention_kernel(AttnArgs p) {
                 s[kb][r] = w;
                 bl += w;
             }
-        l = l * alpha + bl;
-#pragma unroll
-        for (int db = 0; db < 4; ++db) o[db] *= alpha;
+        l += bl;
 
         // O^T += V^T P^T: step ts uses keys 16(ts/4) + 4g + ts%4 (lane group g)
 #pragma unroll
