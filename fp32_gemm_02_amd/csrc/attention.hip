@@ -284,15 +284,17 @@ __global__ __launch_bounds__(256 * KSPLIT) void attention_kernel(AttnArgs p) {
 #pragma unroll
             for (int db = 0; db < 4; ++db) o[db] *= alpha;
         }
-        float bl = 0.0f;
 #pragma unroll
         for (int kb = 0; kb < NSB; ++kb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float w = __builtin_amdgcn_exp2f(s[kb][r] - base);
-                s[kb][r] = w;
-                bl += w;
-            }
+            for (int r = 0; r < 4; ++r) s[kb][r] = __builtin_amdgcn_exp2f(s[kb][r] - base);
+        // the step's weights summed pairwise (short dependency chains)
+        float part[NSB];
+#pragma unroll
+        for (int kb = 0; kb < NSB; ++kb) part[kb] = (s[kb][0] + s[kb][1]) + (s[kb][2] + s[kb][3]);
+        float bl = part[0];
+#pragma unroll
+        for (int kb = 1; kb < NSB; ++kb) bl += part[kb];
         l += bl;
 
         // O^T += V^T P^T: step ts uses keys 16(ts/4) + 4g + ts%4 (lane group g)
