@@ -77,6 +77,26 @@ def test_attention_large_scores():
     check_attn(w, x, run_attn(w, x))
 
 
+@pytest.mark.parametrize("order", ["rising", "falling"])
+def test_attention_running_maximum_paths(order):
+    """Scores that rise along the keys move every query's running maximum at
+    every step (the kernel rescales its running sums each step); scores that
+    fall leave it where the first step put it (the rescale is skipped from
+    then on).  Both against the oracle, over several steps and a ragged last
+    one."""
+    w = wl.AttnWorkload("max_" + order, 200, 2000, 64, 0.125, seed=8)
+    x = wl.make_attn_inputs(w)
+    rng = np.random.default_rng(9)
+    q, k = x.logical("Q"), x.logical("K")
+    q[:] = rng.uniform(0.5, 1.0, q.shape).astype(np.float32)
+    base = rng.uniform(0.5, 1.0, (1, w.D)).astype(np.float32)
+    ramp = np.arange(w.Nk, dtype=np.float32)[:, None] / w.Nk
+    if order == "falling":
+        ramp = ramp[::-1]
+    k[:] = (base * (1.0 + 4.0 * ramp)).astype(np.float32)
+    check_attn(w, x, run_attn(w, x))
+
+
 @pytest.mark.parametrize("BR", [64, 100, 1000, 5000])
 def test_supertiled_equals_monolithic(BR):
     """Super-tiles of BR query rows (a grouped launch; BR not a multiple of 64
