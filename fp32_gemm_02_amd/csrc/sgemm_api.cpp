@@ -192,13 +192,14 @@ int default_entry(int64_t M, int64_t N, int64_t K, bool direct) {
         const bool splitk = 32 * p.wm > p.bm || 32 * p.wn > p.bn;
         if (splitk && K < 2048) continue;
         if (splitk && p.bm == 64 && tiles32 <= 2560) continue;
-        // the 320x192 tile only where its chunks load directly: K whole
-        // 16-deep chunks and operand rows 16-byte aligned.  Otherwise chunks
-        // come through registers, which its one workgroup per CU on one wave
-        // per SIMD cannot hide (5003 x 3001 x 2047: 482.8 us against 472.6
-        // for 256x128; 4095^3 with unaligned rows: 62 against 126 TFLOP/s
-        // for 256x256)
-        if (p.bm == 320 && (K % 16 != 0 || !direct)) continue;
+        // the 320x192 tile only where its chunks load directly (operand rows
+        // 16-byte aligned).  Otherwise every chunk comes through registers,
+        // which its one workgroup per CU on one wave per SIMD cannot hide
+        // (4095^3 with unaligned rows: 62 against 126 TFLOP/s for 256x256).
+        // A K that is not whole chunks costs it only its last chunk through
+        // registers (5120 x 3072 x 2047 and x 2048: 455.5 and 455.6 us;
+        // 5003 x 3001 x 2047: 465.1 us against 472.3 for 256x128)
+        if (p.bm == 320 && !direct) continue;
         const int64_t per = per_cu(p.bm, p.bn);
         const double occ = std::min(1.0, (double)(per * p.wm * p.wn) / 4.0);
         const bool alone = (p.bm == 256 && p.bn == 256) || p.bm == 320 || per == 1;

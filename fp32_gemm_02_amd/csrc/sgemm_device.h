@@ -38,6 +38,7 @@ __device__ __forceinline__ void tile_of(const Args& p, int& tm, int& tn) {
 // (gfx9 global memory instructions take dword-aligned addresses for wider
 // accesses), where the compiler would otherwise issue four dword loads.
 typedef float f32x4u __attribute__((ext_vector_type(4), aligned(4)));
+typedef float f32x2u __attribute__((ext_vector_type(2), aligned(4)));
 
 // Load 4 consecutive floats src[0..3] whose positions are valid while
 // e < nvalid (nvalid <= 0: all zero).  VEC: src is 16-byte aligned;
@@ -103,15 +104,19 @@ template <int N>
 constexpr int kWaitVm = (N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8);
 static_assert(kWaitVm<0> == 0x70 && kWaitVm<4> == 0x74, "s_waitcnt encoding");
 
-// NB consecutive floats of B read with one LDS instruction, and element n of it.
+// NB consecutive floats of B read with one LDS instruction, and element n of
+// it; utype is the same NB floats at 4-byte alignment, for global accesses at
+// any float position.
 template <int NB> struct BVec;
 template <> struct BVec<1> {
     using type = float;
+    using utype = float;
     static __device__ __forceinline__ float get(float v, int) { return v; }
     static __device__ __forceinline__ void set(float& v, int, float x) { v = x; }
 };
 template <> struct BVec<2> {
     using type = f32x2;
+    using utype = f32x2u;
     static __device__ __forceinline__ float get(f32x2 v, int n) { return v[n]; }
     static __device__ __forceinline__ void set(f32x2& v, int n, float x) { v[n] = x; }
 };
@@ -122,11 +127,13 @@ struct f32x3s {
 };
 template <> struct BVec<3> {
     using type = f32x3s;
+    using utype = f32x3s;
     static __device__ __forceinline__ float get(const f32x3s& v, int n) { return v.v[n]; }
     static __device__ __forceinline__ void set(f32x3s& v, int n, float x) { v.v[n] = x; }
 };
 template <> struct BVec<4> {
     using type = f32x4;
+    using utype = f32x4u;
     static __device__ __forceinline__ float get(f32x4 v, int n) { return v[n]; }
     static __device__ __forceinline__ void set(f32x4& v, int n, float x) { v[n] = x; }
 };

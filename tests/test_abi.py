@@ -172,22 +172,32 @@ def test_get_config_checks():
     # two resident 256x128 tiles per CU hide each other's fixed cost
     ((2560, 2560, 1024), (256, 128, 16, 4, 2)),
     ((8192, 8192, 1024), (256, 128, 16, 4, 2)),
-    # 16 x 16 tiles of 320x192 (exactly 256 workgroups) where K is whole
-    # 16-deep chunks, and not otherwise (the same product with K = 4095)
+    # 16 x 16 tiles of 320x192 (exactly 256 workgroups) where the leading
+    # dimensions are multiples of 4, K whole 16-deep chunks or not ...
     ((5120, 3072, 4096), (320, 192, 16, 2, 2)),
     ((2500, 6000, 6000), (320, 192, 16, 2, 2)),
     ((7680, 7680, 7680), (320, 192, 16, 2, 2)),
+    ((5120, 3072, 4095, 4096, 3072, 3072), (320, 192, 16, 2, 2)),
+    # ... and not where they are not (every chunk through registers)
     ((5120, 3072, 4095), (256, 256, 32, 4, 2)),
-    # the five workloads' shapes and the super-tiled step leaf
+    # 286 of them (two rounds of 256 CUs) lose to 256 of 256x256
+    ((4095, 4095, 4095, 4096, 4096, 4096), (256, 256, 32, 4, 2)),
+    # the five workloads' shapes (with their leading dimensions) and the
+    # super-tiled step leaf
     ((4096, 4096, 4096), (256, 256, 32, 4, 2)),
     ((65536, 512, 4096), (256, 256, 32, 4, 2)),
-    ((5003, 3001, 2047), (256, 128, 16, 4, 2)),
+    ((5003, 3001, 2047, 2048, 3008, 3008), (320, 192, 16, 2, 2)),
+    ((4096, 4096, 4096, 16384, 16384, 16384), (256, 256, 32, 4, 2)),
     ((16384, 16384, 16384), (256, 256, 32, 4, 2)),
+    # the unaligned shape with unpadded rows
+    ((5003, 3001, 2047), (256, 128, 16, 4, 2)),
 ])
 def test_default_config_picks(shape, want):
-    """The built-in choice at the boundaries of its rule, fixed on the CPU."""
-    M, N, K = shape
-    assert g.sgemm_get_config(M, N, K, K, N, N).as_tuple() == want
+    """The built-in choice at the boundaries of its rule, fixed on the CPU
+    (leading dimensions K, N, N unless given)."""
+    M, N, K = shape[:3]
+    lds = shape[3:] if len(shape) > 3 else (K, N, N)
+    assert g.sgemm_get_config(M, N, K, *lds).as_tuple() == want
 
 
 def test_default_config_needs_direct_loads_for_the_320x192_tile():
