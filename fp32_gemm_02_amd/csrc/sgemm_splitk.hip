@@ -175,37 +175,53 @@ __global__ __launch_bounds__(64 * KS) void sgemm_splitk_kernel(GemmArgs p) {
     const int col = n0 + NB * l32;
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
+        auto row_of = [&](int rr) {
+            const int r = wave * RW + rr;
+            return m0 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        };
+        float v[RW][NB];
 #pragma unroll
         for (int rr = 0; rr < RW; ++rr) {
             const int r = wave * RW + rr;
-            const int row = m0 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-            float v[NB];
 #pragma unroll
             for (int n = 0; n < NB; ++n) {
                 const int q = ((i * NB + n) * 16 + r) * 64 + lane;
                 float sum = smem[q];
 #pragma unroll
                 for (int w = 1; w < KS; ++w) sum += smem[w * REGION + q];
-                v[n] = alpha * sum;
+                v[rr][n] = alpha * sum;
             }
+        }
+        if (beta != 0.0f) {
+            // The C values of all the wave's rows, read with no branch (a row
+            // past M reads row M-1, a column past N column N-1: every read
+            // lies inside C and feeds only elements that are stored), then
+            // one wait: a read under a per-lane bounds check made the
+            // compiler wait for it before the next row.
+            float c[RW][NB];
+#pragma unroll
+            for (int rr = 0; rr < RW; ++rr) {
+                const float* src = p.C + (int64_t)min(row_of(rr), p.M - 1) * p.ldc;
+#pragma unroll
+                for (int n = 0; n < NB; ++n) c[rr][n] = src[min(col + n, p.N - 1)];
+            }
+            __builtin_amdgcn_s_waitcnt(kWaitVm<0>);
+#pragma unroll
+            for (int rr = 0; rr < RW; ++rr)
+#pragma unroll
+                for (int n = 0; n < NB; ++n) v[rr][n] += beta * c[rr][n];
+        }
+#pragma unroll
+        for (int rr = 0; rr < RW; ++rr) {
+            const int row = row_of(rr);
             if (row >= p.M) continue;
             float* dst = p.C + (int64_t)row * p.ldc + col;
             if (VEC && NB == 2 && col + 1 < p.N) {
-                if (beta != 0.0f) {
-                    const f32x2 c2 = *reinterpret_cast<const f32x2*>(dst);
-                    v[0] += beta * c2[0];
-                    v[NB - 1] += beta * c2[1];
-                }
-                *reinterpret_cast<f32x2*>(dst) = f32x2{v[0], v[NB - 1]};
+                *reinterpret_cast<f32x2*>(dst) = f32x2{v[rr][0], v[rr][NB - 1]};
             } else {
 #pragma unroll
-                for (int n = 0; n < NB; ++n) {
-                    if (col + n < p.N) {
-                        float o = v[n];
-                        if (beta != 0.0f) o += beta * dst[n];
-                        dst[n] = o;
-                    }
-                }
+                for (int n = 0; n < NB; ++n)
+                    if (col + n < p.N) dst[n] = v[rr][n];
             }
         }
     }
