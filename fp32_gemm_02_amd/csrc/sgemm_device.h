@@ -138,4 +138,95 @@ template <> struct BVec<4> {
     static __device__ __forceinline__ void set(f32x4& v, int n, float x) { v[n] = x; }
 };
 
+// Epilogue of one lane's share of a 32-row block of C that may reach past
+// an edge of the matrix: for r = 0..15, row = row0 + 8*(r/4) + r%4, and
+// n = 0..NB-1, C[row][col+n] <- alpha*acc(n, r) + beta*C[row][col+n] where
+// row < M and col+n < N (beta == 0: C not read); nothing past M or N is
+// written.  RB rows form a batch: their C values are read before any of them
+// is written.  The reads take no branch: a row past M reads row M-1, and a
+// lane whose NB columns pass N reads the NB columns that end at column N-1
+// and moves the ones it needs into place, so every read lies inside C and
+// feeds only elements that are stored.  Reads under per-lane bounds checks
+// made the compiler wait for every outstanding access before each row, one
+// memory round trip per row.  After the batch's one wait its results are all
+// formed, then its guarded stores issue back to back.  A lane whose NB
+// columns lie inside C writes them with one access.  Needs M >= 1.
+template <int NB, int RB, typename Acc>
+__device__ __forceinline__ void edge_block_epilogue(float* C, int64_t ldc, int M, int N, int row0,
+                                                    int col, float alpha, float beta, Acc acc) {
+    static_assert(16 % RB == 0, "whole batches of rows");
+    using CV = typename BVec<NB>::type;
+    using UV = typename BVec<NB>::utype;
+    const int ncols = N - col;
+    auto row_of = [&](int r) { return row0 + 8 * (r >> 2) + (r & 3); };
+    if (N < NB) {
+        // C narrower than one lane's NB columns: element by element.
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            if (row_of(r) >= M) continue;
+            float* dst = C + (int64_t)row_of(r) * ldc + col;
+#pragma unroll
+            for (int n = 0; n < NB; ++n) {
+                if (n >= ncols) continue;
+                float v = alpha * acc(n, r);
+                if (beta != 0.0f) v += beta * dst[n];
+                dst[n] = v;
+            }
+        }
+        return;
+    }
+    const bool wide = ncols >= NB;   // all NB columns of the lane inside C
+    // First column read by the lane and how far its wanted columns sit past
+    // it (0 for a wide lane, 1..NB-1 for one that straddles N, more for a
+    // lane wholly past N, whose values go unused).
+    const int cs = min(col, N - NB);
+    const int sh = col - cs;
+#pragma unroll
+    for (int rb = 0; rb < 16; rb += RB) {
+        CV cv[RB];
+        if (beta != 0.0f) {
+#pragma unroll
+            for (int e = 0; e < RB; ++e)
+                cv[e] = *reinterpret_cast<const UV*>(C + (int64_t)min(row_of(rb + e), M - 1) * ldc + cs);
+            __builtin_amdgcn_s_waitcnt(kWaitVm<0>);
+            if constexpr (NB > 1) {
+#pragma unroll
+                for (int e = 0; e < RB; ++e) {
+                    const CV x = cv[e];
+#pragma unroll
+                    for (int n = 0; n < NB; ++n) {
+                        float v = BVec<NB>::get(x, n);
+#pragma unroll
+                        for (int s = 1; n + s < NB; ++s) v = sh == s ? BVec<NB>::get(x, n + s) : v;
+                        BVec<NB>::set(cv[e], n, v);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < RB; ++e) {
+#pragma unroll
+            for (int n = 0; n < NB; ++n) {
+                float v = alpha * acc(n, rb + e);
+                if (beta != 0.0f) v += beta * BVec<NB>::get(cv[e], n);
+                BVec<NB>::set(cv[e], n, v);
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < RB; ++e) {
+            const int row = row_of(rb + e);
+            if (row >= M || ncols <= 0) continue;
+            float* dst = C + (int64_t)row * ldc + col;
+            if (wide) {
+                *reinterpret_cast<UV*>(dst) = cv[e];
+            } else {
+#pragma unroll
+                for (int n = 0; n < NB; ++n)
+                    if (n < ncols) dst[n] = BVec<NB>::get(cv[e], n);
+            }
+        }
+    }
+}
+
 }  // namespace phobos
+

@@ -477,7 +477,6 @@ __global__ __launch_bounds__(64 * WM * WN) void sgemm_mfma_kernel(GemmArgs p) {
     // ---- epilogue: C <- alpha*acc + beta*C (beta == 0: C not read) ----
     const float alpha = p.alpha, beta = p.beta;
     const int col = n0 + wn * T::TWN + T::NB * l32;
-    const int ncols = p.N - col;
     using CV = typename BVec<T::NB>::type;
     if (whole) {
         // Whole tile inside C: the 16 rows of a 32-row block are read before
@@ -517,106 +516,15 @@ __global__ __launch_bounds__(64 * WM * WN) void sgemm_mfma_kernel(GemmArgs p) {
         }
         return;
     }
-    // Tile at an edge of C: rows past M and columns past N are never written.
-    // As above, a lane reads the C values of several rows of a block before
-    // it writes any (all 16, or 4 at a time where the accumulators fill the
-    // register file).  The reads take no branch: a row past M reads row M-1,
-    // and a lane whose NB columns pass N reads the NB columns that end at
-    // column N-1 and moves the ones it needs into place, so every read lies
-    // inside C and feeds only elements that are stored.  Reads guarded by
-    // per-lane branches made the compiler wait for every outstanding access
-    // before each row, so each row of the edge tiles, which finish last, cost
-    // a memory round trip.  A lane whose NB columns all lie inside C writes
-    // them with one access (at 4-byte alignment when the rows are not 16-byte
-    // aligned).
-    const bool wide = ncols >= T::NB;   // all NB columns of the lane inside C
-    constexpr int RB = T::MB * T::NB * 16 >= 256 ? 4 : 16;   // rows per batch
-    if (p.N < T::NB) {
-        // C narrower than one lane's NB columns: element by element.
+    // Tile at an edge of C: as above, a lane reads the C values of several
+    // rows of a block before it writes any (all 16, or 2 at a time where the
+    // accumulators fill the register file), with unguarded reads clamped
+    // into C (edge_block_epilogue).
+    constexpr int RB = T::MB * T::NB * 16 >= 256 ? 2 : 16;   // rows per batch
 #pragma unroll
-        for (int i = 0; i < T::MB; ++i) {
-            const int row0 = m0 + wm * T::TWM + i * 32 + 4 * h;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = row0 + 8 * (r >> 2) + (r & 3);
-                if (row >= p.M) continue;
-                float* dst = p.C + (int64_t)row * p.ldc + col;
-#pragma unroll
-                for (int n = 0; n < T::NB; ++n) {
-                    if (n >= ncols) continue;
-                    float v = alpha * acc[i][n][r];
-                    if (beta != 0.0f) v += beta * dst[n];
-                    dst[n] = v;
-                }
-            }
-        }
-        return;
-    }
-    // First column read by the lane and how far its wanted columns sit past
-    // it (0 for a wide lane, 1..NB-1 for one that straddles N, more for a
-    // lane wholly past N, whose values go unused).
-    using UV = typename BVec<T::NB>::utype;
-    const int cs = min(col, p.N - T::NB);
-    const int sh = col - cs;
-    auto shift = [&](CV x) -> CV {
-        CV y = x;
-#pragma unroll
-        for (int n = 0; n < T::NB; ++n) {
-            float v = BVec<T::NB>::get(x, n);
-#pragma unroll
-            for (int s = 1; n + s < T::NB; ++s) v = sh == s ? BVec<T::NB>::get(x, n + s) : v;
-            BVec<T::NB>::set(y, n, v);
-        }
-        return y;
-    };
-#pragma unroll
-    for (int i = 0; i < T::MB; ++i) {
-        const int row0 = m0 + wm * T::TWM + i * 32 + 4 * h;
-        auto row_of = [&](int r) { return row0 + 8 * (r >> 2) + (r & 3); };
-        auto row_ptr = [&](int r) { return p.C + (int64_t)row_of(r) * p.ldc + col; };
-#pragma unroll
-        for (int rb = 0; rb < 16; rb += RB) {
-            CV cv[RB];
-            if (beta != 0.0f) {
-#pragma unroll
-                for (int e = 0; e < RB; ++e)
-                    cv[e] = *reinterpret_cast<const UV*>(
-                        p.C + (int64_t)min(row_of(rb + e), p.M - 1) * p.ldc + cs);
-                __builtin_amdgcn_s_waitcnt(kWaitVm<0>);
-                if (T::NB > 1) {
-#pragma unroll
-                    for (int e = 0; e < RB; ++e) cv[e] = shift(cv[e]);
-                }
-            }
-            // All results of the batch first, in place of the C values, so
-            // that the stores below issue back to back.
-#pragma unroll
-            for (int e = 0; e < RB; ++e) {
-#pragma unroll
-                for (int n = 0; n < T::NB; ++n) {
-                    float v = alpha * acc[i][n][rb + e];
-                    if (beta != 0.0f) v += beta * BVec<T::NB>::get(cv[e], n);
-                    BVec<T::NB>::set(cv[e], n, v);
-                }
-            }
-#pragma unroll
-            for (int e = 0; e < RB; ++e) {
-                const int r = rb + e;
-                if (row_of(r) >= p.M || ncols <= 0) continue;
-                float* dst = row_ptr(r);
-                const CV o = cv[e];
-                if (wide && VEC) {
-                    *reinterpret_cast<CV*>(dst) = o;
-                } else if (wide) {
-                    *reinterpret_cast<UV*>(dst) = o;
-                } else {
-#pragma unroll
-                    for (int n = 0; n < T::NB; ++n)
-                        if (n < ncols) dst[n] = BVec<T::NB>::get(o, n);
-                }
-            }
-        }
-    }
+    for (int i = 0; i < T::MB; ++i)
+        edge_block_epilogue<T::NB, RB>(p.C, p.ldc, p.M, p.N, m0 + wm * T::TWM + i * 32 + 4 * h, col,
+                                       alpha, beta, [&](int n, int r) { return acc[i][n][r]; });
 }
 
 template <int BM, int BN, int BK, int WM, int WN, bool VEC>

@@ -292,49 +292,15 @@ __global__ __launch_bounds__(64 * WM * WN) void sgemm_tc_kernel(GemmArgs p) {
     }
 
     // ---- epilogue: C <- alpha*acc + beta*C (beta == 0: C not read) ----
+    // Every tile through edge_block_epilogue: several rows of C per block
+    // read before any is written, with unguarded reads clamped into C.
     const float alpha = p.alpha, beta = p.beta;
     const int col = n0 + wn * TWN + NB * l32;
-    const int ncols = p.N - col;
+    constexpr int RB = MB * NB * 16 >= 256 ? 4 : 16;   // rows per batch
 #pragma unroll
-    for (int i = 0; i < MB; ++i) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int row = m0 + wm * TWM + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-            if (row >= p.M || ncols <= 0) continue;
-            float* dst = p.C + (int64_t)row * p.ldc + col;
-            float v[NB];
-#pragma unroll
-            for (int n = 0; n < NB; ++n) v[n] = alpha * acc[i][n][r];
-            if (VEC && ncols >= NB) {
-                if constexpr (NB == 4) {
-                    if (beta != 0.0f) {
-                        const f32x4 cv = *reinterpret_cast<const f32x4*>(dst);
-                        v[0] += beta * cv[0]; v[1] += beta * cv[1];
-                        v[2] += beta * cv[2]; v[3] += beta * cv[3];
-                    }
-                    *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
-                } else if constexpr (NB == 2) {
-                    if (beta != 0.0f) {
-                        const f32x2 cv = *reinterpret_cast<const f32x2*>(dst);
-                        v[0] += beta * cv[0]; v[1] += beta * cv[1];
-                    }
-                    *reinterpret_cast<f32x2*>(dst) = f32x2{v[0], v[1]};
-                } else {
-                    if (beta != 0.0f) v[0] += beta * dst[0];
-                    dst[0] = v[0];
-                }
-            } else {
-#pragma unroll
-                for (int n = 0; n < NB; ++n) {
-                    if (n < ncols) {
-                        float o = v[n];
-                        if (beta != 0.0f) o += beta * dst[n];
-                        dst[n] = o;
-                    }
-                }
-            }
-        }
-    }
+    for (int i = 0; i < MB; ++i)
+        edge_block_epilogue<NB, RB>(p.C, p.ldc, p.M, p.N, m0 + wm * TWM + i * 32 + 4 * h, col, alpha,
+                                    beta, [&](int n, int r) { return acc[i][n][r]; });
 }
 
 template <int FMT, int BM, int BN, int BK, int WM, int WN, int PF, bool VEC>
@@ -743,7 +709,6 @@ __global__ __launch_bounds__(64 * WM * WN) void tc16_kernel(Tc16Args p) {
     // ---- epilogue: C <- alpha*acc + beta*C (beta == 0: C not read) ----
     const float alpha = p.alpha, beta = p.beta;
     const int col = n0 + wn * TWN + NB * l32;
-    const int ncols = p.N - col;
     if constexpr (NB == 4) {
         if (p.vec_c && m0 + BM <= p.M && n0 + BN <= p.N) {
             // Whole tile inside C: the 16 rows of C of a 32-row block are read
@@ -773,35 +738,14 @@ __global__ __launch_bounds__(64 * WM * WN) void tc16_kernel(Tc16Args p) {
             return;
         }
     }
+    // A tile at an edge of C (or C rows not 16-byte aligned): several rows
+    // per block read before any is written, with unguarded reads clamped
+    // into C (edge_block_epilogue).
+    constexpr int RB = MB * NB * 16 >= 256 ? 4 : 16;   // rows per batch
 #pragma unroll
-    for (int i = 0; i < MB; ++i) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int row = m0 + wm * TWM + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-            if (row >= p.M || ncols <= 0) continue;
-            float* dst = p.C + (int64_t)row * p.ldc + col;
-            float v[NB];
-#pragma unroll
-            for (int n = 0; n < NB; ++n) v[n] = alpha * acc[i][n][r];
-            if (p.vec_c && ncols >= NB && NB == 4) {
-                if (beta != 0.0f) {
-                    const f32x4 cv = *reinterpret_cast<const f32x4*>(dst);
-                    v[0] += beta * cv[0]; v[1] += beta * cv[1];
-                    v[2] += beta * cv[2]; v[3] += beta * cv[3];
-                }
-                *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
-            } else {
-#pragma unroll
-                for (int n = 0; n < NB; ++n) {
-                    if (n < ncols) {
-                        float o = v[n];
-                        if (beta != 0.0f) o += beta * dst[n];
-                        dst[n] = o;
-                    }
-                }
-            }
-        }
-    }
+    for (int i = 0; i < MB; ++i)
+        edge_block_epilogue<NB, RB>(p.C, p.ldc, p.M, p.N, m0 + wm * TWM + i * 32 + 4 * h, col, alpha,
+                                    beta, [&](int n, int r) { return acc[i][n][r]; });
 }
 
 template <int FMT, int BM, int BN, int BK, int NS, int WM, int WN>
