@@ -540,17 +540,33 @@ int tc_find(int32_t fmt, const sgemm_tc_config& c) {
     return -1;
 }
 
-// Forced, else: the staged form for products large enough that the cast pass
-// (one read of A and B, a write of half their size) is small against the
-// GEMM, else the fused form with the largest tile that still gives every CU
-// work (the fp32 rule), else small fused tiles.
+// Forced, else, with T256 and T128 the tiles of 256x256 and of 128x128 that
+// cover C (a sweep of every compiled entry over 19 shapes from 768^3 to
+// 4096 x 4096 x 1024, fp16; each rule below picked the fastest entry or one
+// within 1% of it):
+//   - K >= 1024 and T256 >= 144: the staged form on 256x256x64 tiles (at
+//     least 144 of them keep the chip busy, and the cast pass is small
+//     against the GEMM);
+//   - K > 2048, T256 < 144 and T128 >= 16: the staged form on 128x128x64
+//     tiles (a long K pays for the cast pass: 2048 x 2048 x 4096 433 against
+//     420 TFLOP/s fused, 2560^3 491 against 415);
+//   - T256 < 144 and T128 >= 64: the fused form on 128x128x64 tiles
+//     (2048 x 2048 x 1024: 282 against 236 staged on 128x128 and 205 on
+//     256x256);
+//   - else the fused form with the largest tile that still gives every CU
+//     work (the fp32 rule), else small fused tiles.
 int tc_choose(int32_t fmt, int64_t M, int64_t N, int64_t K) {
     {
         std::lock_guard<std::mutex> lk(g_mu);
         if (g_tc_forced[fmt] >= 0) return g_tc_forced[fmt];
     }
-    if (M >= 2048 && N >= 2048 && K >= 1024)
-        return tc_find(fmt, sgemm_tc_config{256, 256, 64, 4, 2, 1});
+    const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
+    const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
+    if (K >= 1024 && t256 >= 144) return tc_find(fmt, sgemm_tc_config{256, 256, 64, 4, 2, 1});
+    if (t256 < 144) {
+        if (K > 2048 && t128 >= 16) return tc_find(fmt, sgemm_tc_config{128, 128, 64, 2, 2, 1});
+        if (t128 >= 64) return tc_find(fmt, sgemm_tc_config{128, 128, 64, 2, 2, 0});
+    }
     static const int order[][4] = {{256, 256, 2, 2}, {256, 128, 2, 2}, {128, 128, 2, 2},
                                    {128, 64, 2, 1}};
     for (const auto& o : order) {

@@ -277,6 +277,31 @@ def test_tc_argument_checks(args, want):
     assert g.sgemm_tc_raw(*args, stream=0) == want
 
 
+@pytest.mark.parametrize("shape,want", [
+    # at least 144 tiles of 256x256 and K >= 1024: staged on 256x256x64
+    ((3072, 3072, 1024), (256, 256, 64, 4, 2, 1)),
+    ((16384, 16384, 16384), (256, 256, 64, 4, 2, 1)),
+    ((5003, 3001, 2047), (256, 256, 64, 4, 2, 1)),
+    # fewer, K > 2048 and at least 16 tiles of 128x128: staged on 128x128x64
+    ((2560, 2560, 2560), (128, 128, 64, 2, 2, 1)),
+    ((2048, 2048, 4096), (128, 128, 64, 2, 2, 1)),
+    ((512, 512, 4096), (128, 128, 64, 2, 2, 1)),
+    # fewer, K <= 2048 and at least 64 tiles of 128x128: fused on 128x128x64
+    ((2048, 2048, 2048), (128, 128, 64, 2, 2, 0)),
+    ((2048, 2048, 1024), (128, 128, 64, 2, 2, 0)),
+    ((1024, 1024, 1024), (128, 128, 64, 2, 2, 0)),
+    # otherwise the fused order of before
+    ((768, 768, 768), (64, 64, 32, 1, 1, 0)),
+    ((4096, 4096, 512), (256, 256, 32, 2, 2, 0)),
+    ((256, 256, 65536), (64, 64, 32, 1, 1, 0)),
+])
+def test_tc_default_config_picks(shape, want):
+    """The matrix-core variant's built-in choice at the boundaries of its
+    rule, both formats, fixed on the CPU."""
+    for fmt in (g.SGEMM_TC_F16, g.SGEMM_TC_BF16):
+        assert g.sgemm_tc_get_config(fmt, *shape).as_tuple() == want
+
+
 def test_tc_configs():
     for fmt in (g.SGEMM_TC_F16, g.SGEMM_TC_BF16):
         cfgs = g.tc_configs(fmt)

@@ -102,7 +102,7 @@ def test_attention_graph_replays_equal_eager(BR):
 
 @pytest.mark.parametrize("fmt", [g.SGEMM_TC_F16, g.SGEMM_TC_BF16], ids=["f16", "bf16"])
 def test_tc_staged_graph_replays_equal_eager(fmt):
-    M = N = K = 2048                      # large enough for the staged form
+    M, N, K = 2048, 2048, 4096            # long enough K for the staged form
     assert g.sgemm_tc_get_config(fmt, M, N, K).staged == 1
     w = wl.custom(M, N, K, 1.0, 0.5, seed=73)
     x = wl.make_inputs(w)
