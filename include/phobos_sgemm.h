@@ -20,6 +20,9 @@
  *   read and then feed only columns of the tile that are not stored.  Rows
  *   of a tile past M read row M-1 of A instead, and are not stored either.
  *   Rows past the last one are never read.  No other kernel reads a pad.
+ *   C is read (beta != 0) only inside the logical matrix: a tile at an edge
+ *   of C reads row M-1 and columns up to N-1 in place of those past the
+ *   edges, and those values feed only elements that are not stored.
  * Memory.  A, B and C are device pointers (hipMalloc'ed or equivalent) owned
  *   by the caller.  The library neither frees nor retains them.  They must
  *   stay valid until the work enqueued on `stream` has finished.  C must not
