@@ -162,7 +162,7 @@ __attribute__((format(printf, 1, 2))) void log_line(const char* fmt, ...) {
 // A split-K entry: a wave grid larger than the tile's 32 x 32 blocks.
 bool is_splitk(const sgemm_config& c) { return 32 * c.wm > c.bm || 32 * c.wn > c.bn; }
 
-int default_entry(int64_t M, int64_t N, int64_t K, bool direct) {
+int default_entry(int64_t M, int64_t N, int64_t K, bool direct, bool a_rows64) {
     struct Pick { int bm, bn, bk, wm, wn; double rate; };
     constexpr int64_t kCUs = 256;
     auto per_cu = [&](int bm, int bn) {
@@ -198,8 +198,12 @@ int default_entry(int64_t M, int64_t N, int64_t K, bool direct) {
         // (4095^3 with unaligned rows: 62 against 126 TFLOP/s for 256x256).
         // A K that is not whole chunks costs it only its last chunk through
         // registers (5120 x 3072 x 2047 and x 2048: 455.5 and 455.6 us;
-        // 5003 x 3001 x 2047: 465.1 us against 472.3 for 256x128)
-        if (p.bm == 320 && !direct) continue;
+        // 5003 x 3001 x 2047: 465.1 us against 472.3 for 256x128).  Its
+        // 64-byte rows of an A chunk also need 64-byte aligned rows of A (lda
+        // a multiple of 16): otherwise they straddle cache lines and it loses
+        // 5-6% (7680^3: 138.3 TFLOP/s at lda 7680, 129.7 at lda 7684, where
+        // 128x128x32 runs 135.9; 4800 x 2900 x 8000: 129.8 against 122.7)
+        if (p.bm == 320 && (!direct || !a_rows64)) continue;
         const int64_t per = per_cu(p.bm, p.bn);
         const double occ = std::min(1.0, (double)(per * p.wm * p.wn) / 4.0);
         const bool alone = (p.bm == 256 && p.bn == 256) || p.bm == 320 || per == 1;
@@ -379,7 +383,7 @@ const char* source_name(ChoiceSource s) {
 // `ptrs16`: the operands' base addresses are 16-byte aligned (assumed when
 // only the shape is known).
 int choose_entry(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
-                 ChoiceSource* src = nullptr, bool ptrs16 = true) {
+                 ChoiceSource* src = nullptr, bool ptrs16 = true, bool a64 = true) {
     load_env_cache_once();
     ChoiceSource dummy;
     ChoiceSource& from = src ? *src : dummy;
@@ -404,7 +408,8 @@ int choose_entry(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int6
         }
     }
     from = kDefault;
-    return default_entry(M, N, K, ptrs16 && lda % 4 == 0 && ldb % 4 == 0 && ldc % 4 == 0);
+    return default_entry(M, N, K, ptrs16 && lda % 4 == 0 && ldb % 4 == 0 && ldc % 4 == 0,
+                         a64 && lda % 16 == 0);
 }
 
 // Record a trace event pair around a launch when tracing is on.
@@ -443,6 +448,7 @@ struct TraceScope {
 };
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned64(const void* p) { return ((uintptr_t)p & 63u) == 0; }
 
 const char* kind_name(int32_t kind) {
     switch (kind) {
@@ -791,7 +797,7 @@ int host_launch_gemm(int64_t M, int64_t N, int64_t K, float alpha, const float* 
                      int64_t ldc, hipStream_t stream) {
     ChoiceSource src;
     const int entry = choose_entry(M, N, K, lda, ldb, ldc, &src,
-                                   aligned16(A) && aligned16(B) && aligned16(C));
+                                   aligned16(A) && aligned16(B) && aligned16(C), aligned64(A));
     if (entry < 0) return SGEMM_ERR_NO_CONFIG;
     return launch_gemm(entry, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, src);
 }
@@ -820,7 +826,7 @@ int sgemm(int64_t M, int64_t N, int64_t K, float alpha, const float* A, int64_t 
     }
     ChoiceSource src;
     const int entry = choose_entry(M, N, K, lda, ldb, ldc, &src,
-                                   aligned16(A) && aligned16(B) && aligned16(C));
+                                   aligned16(A) && aligned16(B) && aligned16(C), aligned64(A));
     if (entry < 0) return SGEMM_ERR_NO_CONFIG;
     return launch_gemm(entry, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s, src);
 }
@@ -865,7 +871,8 @@ int sgemm_supertiled(int64_t M, int64_t N, int64_t K, float alpha, const float* 
                 const float* Bs = B + k0 * ldb + c0;
                 ChoiceSource src;
                 const int entry = choose_entry(rows, cols, depth, lda, ldb, ldc, &src,
-                                               aligned16(As) && aligned16(Bs) && aligned16(Cs));
+                                               aligned16(As) && aligned16(Bs) && aligned16(Cs),
+                                               aligned64(As));
                 if (entry < 0) return SGEMM_ERR_NO_CONFIG;
                 st = launch_gemm(entry, rows, cols, depth, alpha, As, lda, Bs, ldb, 1.0f, Cs,
                                  ldc, s, src);
@@ -1135,7 +1142,8 @@ int sgemm_tune(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_
     // warm-up the first candidates are timed slow.  About 100 ms of the
     // built-in choice first; its time also sizes the short timings below, so
     // that each covers about 1 ms rather than one launch-dominated call.
-    const int dflt = default_entry(M, N, K, lda % 4 == 0 && ldb % 4 == 0 && ldc % 4 == 0);
+    const int dflt = default_entry(M, N, K, lda % 4 == 0 && ldb % 4 == 0 && ldc % 4 == 0,
+                                   lda % 16 == 0);
     float t_dflt = 0.0f;
     if (st == SGEMM_OK) st = time_one(dflt, 1, &t_dflt);
     const float t_est = std::max(t_dflt, 1e-3f);

@@ -163,8 +163,9 @@ int sgemm_init_leaf(int64_t M, int64_t N, float beta, float* C, int64_t ldc,
  * 32x32x16 on 2x2 waves (4 waves per tile, rate 0.79) and, for more than 2560
  * 32x32 tiles, 64x64x16 on 4x1 waves (rate 0.85), and where its chunks load
  * straight into LDS (leading dimensions multiples of 4 and 16-byte aligned
- * operands; sgemm_get_config, which sees no addresses, assumes aligned ones)
- * the 320x192x16 tile on 2x2 waves (rate 0.965, alone on its CU like
+ * operands) and the rows of A are 64-byte aligned (lda a multiple of 16, A
+ * 64-byte aligned; sgemm_get_config, which sees no addresses, assumes aligned
+ * ones) the 320x192x16 tile on 2x2 waves (rate 0.965, alone on its CU like
  * 256x256; 16 x 16 of them cover 5120 x 3072).  When the least is a 32x32
  * tile, with T 32x32 tiles: for T <= 2560, K >= 512 (except T a
  * multiple of 1024 from 2048 on with K < 4096, where two single-wave tiles

@@ -178,8 +178,12 @@ def test_get_config_checks():
     ((2500, 6000, 6000), (320, 192, 16, 2, 2)),
     ((7680, 7680, 7680), (320, 192, 16, 2, 2)),
     ((5120, 3072, 4095, 4096, 3072, 3072), (320, 192, 16, 2, 2)),
-    # ... and not where they are not (every chunk through registers)
+    # ... and not where they are not (every chunk through registers), nor
+    # where the rows of A are not 64-byte aligned (lda not a multiple of 16)
     ((5120, 3072, 4095), (256, 256, 32, 4, 2)),
+    ((7680, 7680, 7681, 7696, 7680, 7680), (320, 192, 16, 2, 2)),
+    ((7680, 7680, 7681, 7684, 7680, 7680), (256, 256, 32, 4, 2)),
+    ((4800, 2900, 8000, 8004, 2900, 2900), (256, 256, 32, 4, 2)),
     # 286 of them (two rounds of 256 CUs) lose to 256 of 256x256
     ((4095, 4095, 4095, 4096, 4096, 4096), (256, 256, 32, 4, 2)),
     # the five workloads' shapes (with their leading dimensions) and the
