@@ -218,7 +218,7 @@ int default_entry(int64_t M, int64_t N, int64_t K, bool direct, bool a_rows64) {
     if (p.bm == 32) {
         // Split-K inside the workgroup where single-wave 32x32 tiles leave
         // SIMDs idle or wait out their loads alone (a sweep of 40 shapes up to
-        // 3072^3 on one box: with it the built-in choice is within 3.3% of the
+        // 3072^3 on one MI355X: with it the built-in choice is within 3.3% of the
         // fastest entry on every shape, 0.5% on average): eight waves per tile
         // for at most 512 tiles or K of 16384 and more, else four waves of
         // 16-deep chunks.  Not where exactly two single-wave tiles per SIMD run
