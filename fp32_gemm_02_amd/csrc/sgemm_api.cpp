@@ -173,8 +173,16 @@ int default_entry(int64_t M, int64_t N, int64_t K, bool direct, bool a_rows64) {
     const int64_t tiles32 = ((M + 31) / 32) * ((N + 31) / 32);
     const Pick picks[] = {
         {256, 256, 32, 4, 2, 1.00},
-        {256, 128, 16, 4, 2, 0.98},
-        {128, 128, 32, 2, 2, 0.90},
+        // From K = 2048 on, 256x128 at 0.94 and 128x128 at 0.93, their rates
+        // at whole rounds of tiles (8192^3: 147.4 TFLOP/s at 8 256x128 tiles
+        // per CU; 6144^3 and 13312 x 4096 x 4096: 146.1 and 147.5 at 9 and 13
+        // 128x128 tiles per CU).  With 0.98 and 0.90 the estimate gave 7168^3,
+        // 9216^2 x 4096, 10240^2 x 4096 and 13312 x 4096 x 4096 to 256x128,
+        // which ran them 3-6% slower than 128x128.  Where K is short, 0.98
+        // and 0.90 (two resident 256x128 workgroups hide each other's first
+        // loads and epilogue: 2560^2 x 1024, 8192^2 x 1024)
+        {256, 128, 16, 4, 2, K >= 2048 ? 0.94 : 0.98},
+        {128, 128, 32, 2, 2, K >= 2048 ? 0.93 : 0.90},
         small_per_cu <= 9 ? Pick{32, 32, 32, 1, 1, 0.60} : Pick{32, 32, 16, 1, 1, 0.70},
         {32, 32, 16, 2, 2, 0.79},   // split-K: four waves share each 32x32 tile
         {64, 64, 16, 4, 1, 0.85},   // split-K: four waves share each 64x64 tile

@@ -158,8 +158,9 @@ int sgemm_init_leaf(int64_t M, int64_t N, float beta, float* C, int64_t ldc,
  * that a second
  * resident one would hide, so the estimate is ceil(T/256) * bm * bn *
  * (K + [alone] * 64) / (rate * min(1, ceil(T/256) * waves / 4)), `rate`
- * being the tile's measured rate (1.00, 0.98, 0.90, and 0.60 / 0.70 for
- * 32x32 at depth 32 / 16), and from K = 2048 on also the split-K entries
+ * being the tile's measured rate (1.00, 0.98, 0.90, from K = 2048 on 1.00,
+ * 0.94, 0.93, and 0.60 / 0.70 for 32x32 at depth 32 / 16), and from
+ * K = 2048 on also the split-K entries
  * 32x32x16 on 2x2 waves (4 waves per tile, rate 0.79) and, for more than 2560
  * 32x32 tiles, 64x64x16 on 4x1 waves (rate 0.85), and where its chunks load
  * straight into LDS (leading dimensions multiples of 4 and 16-byte aligned

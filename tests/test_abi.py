@@ -164,6 +164,9 @@ def test_get_config_checks():
     ((1792, 1792, 8192), (32, 32, 16, 2, 2)),
     # one 128x128 tile per CU beats 13 small ones per CU, and 576 tiles of
     # 256x256 (2.25 rounds of 256 CUs) lose to 2304 of 128x128 (9 rounds)
+    ((7168, 7168, 7168), (128, 128, 32, 2, 2)),
+    ((13312, 4096, 4096), (128, 128, 32, 2, 2)),
+    ((10240, 10240, 4096), (128, 128, 32, 2, 2)),
     ((1792, 1792, 1792), (128, 128, 32, 2, 2)),
     ((2048, 2048, 2048), (128, 128, 32, 2, 2)),
     ((6144, 6144, 6144), (128, 128, 32, 2, 2)),
@@ -182,7 +185,7 @@ def test_get_config_checks():
     # where the rows of A are not 64-byte aligned (lda not a multiple of 16)
     ((5120, 3072, 4095), (256, 256, 32, 4, 2)),
     ((7680, 7680, 7681, 7696, 7680, 7680), (320, 192, 16, 2, 2)),
-    ((7680, 7680, 7681, 7684, 7680, 7680), (256, 256, 32, 4, 2)),
+    ((7680, 7680, 7681, 7684, 7680, 7680), (128, 128, 32, 2, 2)),
     ((4800, 2900, 8000, 8004, 2900, 2900), (256, 256, 32, 4, 2)),
     # 286 of them (two rounds of 256 CUs) lose to 256 of 256x256
     ((4095, 4095, 4095, 4096, 4096, 4096), (256, 256, 32, 4, 2)),
